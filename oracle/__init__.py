@@ -1,0 +1,24 @@
+"""CPU float64 oracle for exact scaled-dot-product attention (TEST INFRASTRUCTURE).
+
+Only the test suite, the smoke check and the benchmark's CPU-baseline leg may
+import this package. The product path (the HIP library and its Python
+binding) never calls it, shares no code with it, and fails loudly when its
+native library is missing instead of falling back to anything here.
+
+Contents:
+  attention.py  plain definition: explicit S, mask, row softmax, P.V, LSE, and
+                the analytic backward (NumPy, float64).
+  brute.py      pure-Python triple loops with math.exp / math.fsum for tiny
+                shapes (an independent second statement of the forward).
+  online.py     the blocked online-softmax recurrence, step by step, used only
+                to show that the recurrence the fused kernel runs is exact.
+
+Every function cites the passage of the pages it follows. Parity pins (closed
+forms, invariants, brute force, library special cases, finite differences)
+live in tests/test_oracle.py.
+"""
+from .attention import attn_fwd, attn_fwd_rows, attn_bwd, softmax_rows
+from .brute import brute_fwd
+from .online import online_fwd
+
+__all__ = ["attn_fwd", "attn_fwd_rows", "attn_bwd", "softmax_rows", "brute_fwd", "online_fwd"]

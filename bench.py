@@ -1,0 +1,245 @@
+#!/usr/bin/env python3
+"""Attention throughput on one MI355X: TFLOPS (fwd, fwd+bwd) and % of the dense bf16 MFMA peak.
+
+One step is one pass of the whole hot path over one batch of resident synthetic input: the fused
+forward (O, LSE) followed by the three backward stages (delta, dK/dV, dQ) of the causal bf16
+workload B=4 H=16 N=2048 d=64. FLOPs follow the workload definition: 4*B*H*N^2*d for the
+forward, halved for the causal mask, and 2.5x that for the backward (five N x N x d products).
+
+Prints ONE JSON line. Besides the headline it carries:
+  roofline      for the kernel with the largest measured time: algorithmic flops per launch /
+                its average duration (HIP events on the launch stream, inside the timed region),
+                against 2516.6 TFLOP/s dense bf16; traffic = HBM bytes per launch from the
+                committed rocprofv3 counter summary, or null if that kernel's source changed since
+  cpu_baseline  the float64 CPU oracle timed on the host cores over a bounded sample of heads
+  workloads     forward-only TFLOPS of the other bf16 workloads and the fp32 workload's latency
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # 256 CUs x 2.4 GHz x 4096 flop/clk/CU (dense)
+PEAK_FP32_TFLOPS = 157.3
+HEADLINE = "fwdbwd_bf16_b4h16n2048d64_causal"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = {
+    "fwd": "fa_fwd_bf16.hip",
+    "bwd_delta": "fa_bwd_bf16.hip",
+    "bwd_dkdv": "fa_bwd_bf16.hip",
+    "bwd_dq": "fa_bwd_bf16.hip",
+}
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="bound on the CPU-oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-workloads", action="store_true", help="skip the forward-only workloads")
+    return ap.parse_args()
+
+
+def source_digest(fname: str) -> str:
+    h = hashlib.sha256()
+    for f in (fname, "fa_device.h", "fa_launch.h"):
+        with open(os.path.join(ROOT, "io_aware_flashattention_flash_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(kernel: str):
+    """HBM bytes per launch from the committed counter summary, if it matches the current source."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f).get(kernel)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("source_digest") != source_digest(KERNEL_SOURCES[kernel]):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this library runs on one GPU; --gpus must be 1 (no multi-GPU path exists)"}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from io_aware_flashattention_flash_amd import (flash_attn_bwd_delta, flash_attn_bwd_dkdv, flash_attn_bwd_dq,
+                                                   flash_attn_fwd, inputs, load_library)
+
+    load_library()  # raises if the HIP library is not built
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    props = torch.cuda.get_device_properties(dev)
+
+    def to_dev(a, dt):
+        return torch.from_numpy(a).to(dev).to(dt)
+
+    # ------------------------------------------------------------------ headline: fwd + bwd
+    w = inputs.WORKLOADS[HEADLINE]
+    x = inputs.make_inputs(w)
+    q, k, v, do = (to_dev(x[n], torch.bfloat16) for n in ("q", "k", "v", "do"))
+    o = torch.empty_like(q)
+    lse = torch.empty(w.B, w.H, w.N, device=dev)
+    delta = torch.empty_like(lse)
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+
+    def step(evs=None):
+        if evs is not None:
+            evs[0].record()
+        flash_attn_fwd(q, k, v, w.scale, True, out=o, lse=lse)
+        if evs is not None:
+            evs[1].record()
+        flash_attn_bwd_delta(o, do, delta)
+        if evs is not None:
+            evs[2].record()
+        flash_attn_bwd_dkdv(q, k, v, lse, do, delta, w.scale, True, dk=dk, dv=dv)
+        if evs is not None:
+            evs[3].record()
+        flash_attn_bwd_dq(q, k, v, lse, do, delta, w.scale, True, dq=dq)
+        if evs is not None:
+            evs[4].record()
+
+    names = ["fwd", "bwd_delta", "bwd_dkdv", "bwd_dq"]
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for i in range(args.steps):
+        step(ev[i])
+    t1.record()
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    ms_step = total_ms / args.steps
+    kern_ms = {n: sum(e[j].elapsed_time(e[j + 1]) for e in ev) / args.steps for j, n in enumerate(names)}
+    if not (torch.isfinite(o.float()).all() and torch.isfinite(dq.float()).all()):
+        raise RuntimeError("non-finite output in the benchmark step")
+
+    f_fwd, f_bwd = w.fwd_flops(), w.bwd_flops()
+    value = (f_fwd + f_bwd) / (ms_step * 1e-3) / 1e12
+    kflops = {"fwd": f_fwd, "bwd_delta": 0.0, "bwd_dkdv": 2.0 * f_fwd, "bwd_dq": 0.5 * f_fwd}
+    kbytes = {  # algorithmic HBM bytes per launch (each tensor moved once)
+        "fwd": w.B * w.H * (4 * w.N * w.d * 2 + 4 * w.N),
+        "bwd_delta": w.B * w.H * (2 * w.N * w.d * 2 + 4 * w.N),
+        "bwd_dkdv": w.B * w.H * (6 * w.N * w.d * 2 + 8 * w.N),
+        "bwd_dq": w.B * w.H * (5 * w.N * w.d * 2 + 8 * w.N),
+    }
+    dom = max(kern_ms, key=kern_ms.get)
+    bound = "hbm" if kflops[dom] == 0 else "mfma"
+    if bound == "mfma":
+        achieved, peak, unit = kflops[dom] / (kern_ms[dom] * 1e-3) / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"
+    else:
+        achieved, peak, unit = kbytes[dom] / (kern_ms[dom] * 1e-3) / 1e9, 8000.0, "GB/s"
+    roofline = {"kernel": dom, "bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+                "frac": round(achieved / peak, 4), "traffic": traffic_for(dom),
+                "algorithmic_flops_per_launch": kflops[dom], "algorithmic_bytes_per_launch": kbytes[dom],
+                "avg_launch_us": round(kern_ms[dom] * 1e3, 2)}
+    kernels = {n: {"avg_us": round(kern_ms[n] * 1e3, 2),
+                   "tflops": round(kflops[n] / (kern_ms[n] * 1e-3) / 1e12, 1) if kflops[n] else None,
+                   "gbps_algorithmic": round(kbytes[n] / (kern_ms[n] * 1e-3) / 1e9, 1)} for n in names}
+    bwd_ms = kern_ms["bwd_delta"] + kern_ms["bwd_dkdv"] + kern_ms["bwd_dq"]
+
+    # ------------------------------------------------------------------ forward-only workloads
+    workloads = {}
+    if not args.no_workloads:
+        for name, wl in inputs.WORKLOADS.items():
+            if wl.backward:
+                continue
+            xi = inputs.make_inputs(wl)
+            dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+            qi, ki, vi = (to_dev(xi[n], dt) for n in ("q", "k", "v"))
+            oi = torch.empty_like(qi)
+            li = torch.empty(wl.B, wl.H, wl.N, device=dev)
+            reps = 20
+            for _ in range(5):
+                flash_attn_fwd(qi, ki, vi, wl.scale, wl.causal, out=oi, lse=li)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            a.record()
+            for _ in range(reps):
+                flash_attn_fwd(qi, ki, vi, wl.scale, wl.causal, out=oi, lse=li)
+            b.record()
+            torch.cuda.synchronize()
+            us = a.elapsed_time(b) / reps * 1e3
+            tf = wl.fwd_flops() / (us * 1e-6) / 1e12
+            peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_FP32_TFLOPS
+            workloads[name] = {"pass": "fwd", "us": round(us, 2), "tflops": round(tf, 1),
+                               "pct_of_peak": round(100 * tf / peak, 2),
+                               "gbps_algorithmic": round(wl.B * wl.H * (4 * wl.N * wl.d * (2 if dt == torch.bfloat16
+                                                                                            else 4) + 4 * wl.N)
+                                                         / (us * 1e-6) / 1e9, 1)}
+            del qi, ki, vi, oi, li
+        torch.cuda.empty_cache()
+
+    # ------------------------------------------------------------------ CPU oracle baseline
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import attn_bwd, attn_fwd
+        try:
+            from threadpoolctl import threadpool_info
+            cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+        except Exception:
+            cores = len(os.sched_getaffinity(0))
+        heads = [(b, h) for b in range(w.B) for h in range(w.H)]
+        done = 0
+        c0 = time.perf_counter()
+        for b, h in heads:
+            sl = (slice(b, b + 1), slice(h, h + 1))
+            attn_fwd(x["q"][sl], x["k"][sl], x["v"][sl], w.scale, True)
+            attn_bwd(x["q"][sl], x["k"][sl], x["v"][sl], x["do"][sl], w.scale, True)
+            done += 1
+            if time.perf_counter() - c0 >= args.cpu_seconds:
+                break
+        secs = time.perf_counter() - c0
+        per_head = (f_fwd + f_bwd) / len(heads)
+        cpu = {"value": round(per_head * done / secs / 1e12, 6), "unit": "TFLOPS", "cores": cores, "kind": "oracle",
+               "sample": f"float64 oracle forward+backward on {done} of {len(heads)} (batch, head) slices of "
+                         f"{HEADLINE}, {secs:.1f} s; value scaled by the workload's flop count per head"}
+
+    out = {
+        "metric": "attention TFLOPS (fwd, fwd+bwd) and % of MI355X dense bf16 MFMA peak",
+        "value": round(value, 2),
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded N(0,1) Q, K, V, dO rounded to bf16 (numpy default_rng(0))",
+        "config": {"workload": HEADLINE, "pass": "fwd+bwd", "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+                   "causal": True, "scale": w.scale},
+        "pct_of_peak": round(100 * value / PEAK_BF16_TFLOPS, 2),
+        "fwd_tflops": round(f_fwd / (kern_ms["fwd"] * 1e-3) / 1e12, 1),
+        "bwd_tflops": round(f_bwd / (bwd_ms * 1e-3) / 1e12, 1),
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernels": kernels,
+        "workloads": workloads,
+        "device": {"name": props.name, "arch": getattr(props, "gcnArchName", ""), "cus": props.multi_processor_count},
+    }
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,146 @@
+/*
+ * flash_attn.h - C ABI of the MI355X (gfx950) exact-attention library.
+ *
+ * The library computes exact scaled-dot-product attention the IO-aware way:
+ * one fused forward kernel streams K/V tiles past a resident Q tile, keeps the
+ * softmax statistics online, and writes back only O and the per-row
+ * log-sum-exp; the backward recomputes the probabilities from those saved
+ * statistics instead of reading an N x N matrix.
+ *
+ * Passages defining the operations (page title, section):
+ *   - codechina.net CUDA/FlashAttention article, section 3: Q, K, V are N x d,
+ *     S = Q K^T, P = softmax(S), O = P V.
+ *   - 52jiny.com FlashAttention explainer, "why standard attention is
+ *     IO-bound": scaling and a mask sit between Q K^T and the softmax.
+ *   - 52jiny.com, "key ideas" parts 1-3: tile Q, K, V into on-chip memory,
+ *     online softmax (running max and sum, rescale on update), fused kernel
+ *     that writes back only the output and a few normalisation statistics.
+ *   - 52jiny.com, "key ideas" part 4: the backward saves the output and the
+ *     softmax statistics and recomputes intermediates block by block.
+ *
+ * Conventions shared by every entry point
+ *   Layout     Q, K, V, O, dO, dQ, dK, dV: contiguous row-major [B, H, N, d],
+ *              d fastest. LSE: contiguous [B, H, N] float32. Q, K and V share
+ *              one N (square self-attention).
+ *   Pointers   DEVICE pointers on the current HIP device, 16-byte aligned.
+ *              The caller owns all memory; the library allocates and frees
+ *              nothing and keeps no state between calls.
+ *   Scale      Multiplies Q K^T in float32 before the mask and softmax; must be
+ *              finite (any sign).
+ *   Causal     causal != 0 masks key j for query i when j > i.
+ *   LSE        Natural-log log-sum-exp of row i of the scaled, masked scores:
+ *              ln(sum_j exp(scale * q_i . k_j)).
+ *   Streams    Every call is asynchronous on `stream` (a hipStream_t; NULL is
+ *              the null stream) and never synchronises. All arguments are
+ *              validated before anything is launched; a call that returns an
+ *              error status has launched nothing and written nothing.
+ *   Errors     The library never aborts and never prints. Launch failures are
+ *              reported as FA_ERR_HIP.
+ *   Support    bf16: d in {64, 128}, forward and backward.
+ *              fp32: d in {64, 128}, forward only.
+ *              B, H, N >= 1 and B*H*N*d < 2^31 elements per tensor.
+ */
+#ifndef FLASH_ATTN_H_
+#define FLASH_ATTN_H_
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_NULL_POINTER = 1, /* a required pointer is NULL */
+  FA_ERR_BAD_SHAPE = 2,    /* B, H, N or d < 1, or a tensor exceeds 2^31 elements */
+  FA_ERR_UNSUPPORTED = 3,  /* (dtype, d, pass) outside the support matrix */
+  FA_ERR_BAD_SCALE = 4,    /* scale is NaN or infinite */
+  FA_ERR_MISALIGNED = 5,   /* a pointer is not 16-byte aligned */
+  FA_ERR_WORKSPACE = 6,    /* workspace NULL or smaller than flash_attn_bwd_workspace_size() */
+  FA_ERR_HIP = 7           /* the HIP runtime reported an error at launch */
+} fa_status_t;
+
+typedef enum { FA_DTYPE_FP32 = 0, FA_DTYPE_BF16 = 1 } fa_dtype_t;
+
+/*
+ * Forward: O = softmax(scale * Q K^T [+ causal mask]) V and LSE.
+ *   q, k, v  [B,H,N,d] of `dtype`, read only.
+ *   o        [B,H,N,d] of `dtype`, written (rounded to nearest even for bf16).
+ *   lse      [B,H,N] float32, written; may be NULL when not wanted.
+ * Arithmetic: products on the matrix cores with float32 accumulation,
+ * softmax in float32. Deterministic: the same inputs give bitwise-identical
+ * outputs.
+ */
+fa_status_t flash_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+                           int B, int H, int N, int d, float scale, int causal,
+                           int dtype, void* stream);
+
+/*
+ * Bytes of device workspace flash_attn_bwd needs for this shape (the per-row
+ * term D = rowsum(dO * O), float32 [B,H,N]). Returns 0 for an invalid shape.
+ */
+size_t flash_attn_bwd_workspace_size(int B, int H, int N, int d, int dtype);
+
+/*
+ * Backward with recomputation, for the loss sum(O * dO):
+ *   D  = rowsum(dO * O)                     (into the workspace)
+ *   P  = exp(scale * Q K^T - LSE)           (recomputed tile by tile)
+ *   dV = P^T dO,  dP = dO V^T,  dS = P * (dP - D),
+ *   dQ = scale * dS K,  dK = scale * dS^T Q.
+ *   q, k, v, o, dout   [B,H,N,d] of `dtype`, read only; o and lse are the
+ *                      forward's outputs for the same q, k, v, scale, causal.
+ *   lse                [B,H,N] float32, read only (must not be NULL).
+ *   dq, dk, dv         [B,H,N,d] of `dtype`, written.
+ *   workspace          device scratch of at least workspace_bytes >=
+ *                      flash_attn_bwd_workspace_size(); its contents on entry
+ *                      are ignored; on return it holds delta (float32 [B,H,N]).
+ * Runs flash_attn_bwd_delta, flash_attn_bwd_dkdv and flash_attn_bwd_dq (below)
+ * in that order on `stream`. Deterministic (no atomics). bf16 only.
+ */
+fa_status_t flash_attn_bwd(const void* q, const void* k, const void* v, const void* o,
+                           const float* lse, const void* dout,
+                           void* dq, void* dk, void* dv,
+                           void* workspace, size_t workspace_bytes,
+                           int B, int H, int N, int d, float scale, int causal,
+                           int dtype, void* stream);
+
+/*
+ * The three stages flash_attn_bwd runs, in this order, exposed so a caller can
+ * run (or time) them separately. Same conventions and validation as
+ * flash_attn_bwd; bf16 only; deterministic.
+ *
+ * Stage 1: delta[b,h,i] = sum_c dout[b,h,i,c] * o[b,h,i,c] (float32 [B,H,N],
+ *          written). This is the row term that the softmax Jacobian subtracts:
+ *          it equals sum_j P_ij dP_ij.
+ */
+fa_status_t flash_attn_bwd_delta(const void* o, const void* dout, float* delta,
+                                 int B, int H, int N, int d, int dtype, void* stream);
+
+/*
+ * Stage 2 (key-outer): for every key tile, recompute P = exp(scale*Q K^T - LSE)
+ * and dP = dO V^T over all query tiles, and accumulate
+ *   dV = P^T dO,   dK = scale * (P * (dP - delta))^T Q.
+ * lse and delta are read only; dk and dv are written.
+ */
+fa_status_t flash_attn_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse,
+                                const void* dout, const float* delta, void* dk, void* dv,
+                                int B, int H, int N, int d, float scale, int causal,
+                                int dtype, void* stream);
+
+/*
+ * Stage 3 (query-outer): for every query tile, recompute P and dP over the key
+ * tiles and accumulate dQ = scale * (P * (dP - delta)) K. dq is written.
+ */
+fa_status_t flash_attn_bwd_dq(const void* q, const void* k, const void* v, const float* lse,
+                              const void* dout, const float* delta, void* dq,
+                              int B, int H, int N, int d, float scale, int causal,
+                              int dtype, void* stream);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+const char* flash_attn_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLASH_ATTN_H_ */

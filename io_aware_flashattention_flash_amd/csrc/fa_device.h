@@ -1,0 +1,110 @@
+// Device-side building blocks for the gfx950 (CDNA4, wave64) attention kernels.
+//
+// Lane layouts below were measured on gfx950 with a probe kernel and are the
+// contract every kernel in this library relies on:
+//
+//   v_mfma_f32_32x32x16_bf16   C[32x32] += A[32x16] * B[16x32]
+//     A: lane l holds row  (l % 32), 8 consecutive k of group (l / 32)
+//     B: lane l holds col  (l % 32), 8 consecutive k of group (l / 32)
+//     C: lane l holds col  (l % 32); accumulator register r holds
+//        row (r / 4) * 8 + (l / 32) * 4 + (r % 4)
+//   v_mfma_f32_32x32x2_f32     same A/B/C roles with one k per lane (k = l / 32)
+//
+//   ds_read_b64_tr_b16: within every group of 16 lanes, treat the 16 lanes'
+//     8-byte reads as a 16 x 4 matrix M (row j = the 4 halfwords lane j
+//     addressed); lane i of the group receives M[4e + i/4][i % 4], e = 0..3.
+//
+//   v_permlane32_swap(x, x) returns {x[l % 32], x[l % 32 + 32]} in every lane.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ f32x16 mfma_bf16_32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16 mfma_f32_32x32x2(float a, float b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+// Max / sum of a lane value with the lane 32 apart (the other half of a 32-row block).
+__device__ __forceinline__ float half_swap_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_swap_min(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fminf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float half_swap_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// 16-byte global load / store helpers (addresses are 16-byte aligned by contract).
+__device__ __forceinline__ u32x4 ld_global16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ void st_global16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+
+// Row-major bf16 tile of ROWS x D in LDS, stored as 16-byte chunks with an XOR swizzle so that
+// (a) 16 consecutive rows read at the same logical chunk, and (b) 4 consecutive rows times 4
+// consecutive chunks (the transpose-read pattern), both land on distinct 16-byte bank groups.
+template <int D>
+struct SwizzledTile {
+  static constexpr int kChunks = D / 8;                       // 16-byte chunks per row
+  static constexpr int kRowsPerLine = kChunks >= 16 ? 1 : 16 / kChunks;  // rows per 256-byte bank line
+  static constexpr int kQuarter = kChunks / 4;
+  static_assert(kChunks == 8 || kChunks == 16, "D must be 64 or 128");
+  __device__ __forceinline__ static int swz(int row) {
+    int m = row / kRowsPerLine;
+    return 4 * (m % kQuarter) + (m / kQuarter) % 4;
+  }
+  // Byte offset of logical (row, chunk).
+  __device__ __forceinline__ static int chunk_off(int row, int chunk) {
+    return (row * kChunks + (chunk ^ swz(row))) * 16;
+  }
+  // Byte offset of element (row, col); col % 4 == 0 keeps an 8-byte read aligned.
+  __device__ __forceinline__ static int elem_off(int row, int col) {
+    return chunk_off(row, col >> 3) + (col & 7) * 2;
+  }
+};
+
+__device__ __forceinline__ bf16x8 lds_read16(const char* base, int off) {
+  return *reinterpret_cast<const bf16x8*>(base + off);
+}
+__device__ __forceinline__ void lds_write16(char* base, int off, u32x4 v) {
+  *reinterpret_cast<u32x4*>(base + off) = v;
+}
+__device__ __forceinline__ bf16x4 lds_read_tr16(const char* base, int off) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(base + off));
+}
+
+__device__ __forceinline__ bf16x8 cat4(bf16x4 a, bf16x4 b) {
+  return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
+// Sum of the two bf16 values of a packed pair, accumulated in fp32.
+__device__ __forceinline__ float dot2_ones(bf16x2 p, float acc) {
+  const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(p, ones, acc, false);
+}
+
+}  // namespace fa

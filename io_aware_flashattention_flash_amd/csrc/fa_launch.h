@@ -1,0 +1,47 @@
+// Internal host-side launch functions shared by the C-ABI entry points (not exported).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace fa {
+
+// Forward, bf16 storage. BH = B*H. d in {64, 128}. c = scale * log2(e).
+hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
+                           int BH, int N, int d, float scale, bool causal, hipStream_t stream);
+
+// Forward, fp32 storage. d in {64, 128}.
+hipError_t launch_fwd_fp32(const void* q, const void* k, const void* v, void* o, float* lse,
+                           int BH, int N, int d, float scale, bool causal, hipStream_t stream);
+
+// Backward stages, bf16 storage, d in {64, 128}. delta: float32 [BH, N].
+hipError_t launch_bwd_delta(const void* o, const void* dout, float* delta, int BH, int N, int d,
+                            hipStream_t stream);
+hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse,
+                           const void* dout, const float* delta, void* dk, void* dv, int BH, int N,
+                           int d, float scale, bool causal, hipStream_t stream);
+hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const float* lse,
+                         const void* dout, const float* delta, void* dq, int BH, int N, int d,
+                         float scale, bool causal, hipStream_t stream);
+
+// Work decomposition shared by the kernels: workgroup id -> (head, tile).
+// The hardware hands consecutive workgroup ids to the 8 XCDs round-robin, each with its
+// own L2. When the head count is a multiple of 8, heads are dealt to XCDs so that all tiles
+// of one head run on one XCD (K/V of that head stay in that L2); within an XCD the heads
+// are taken one after another. With `heavy_first` the tiles of a head are issued from the
+// one with the most work (the last, for a causal mask) to the least.
+__device__ __forceinline__ void map_workgroup(int wg, int n_tiles, int nh, bool heavy_first,
+                                              int& head, int& tile) {
+  int rank;
+  if ((nh & 7) == 0) {
+    const int xcd = wg & 7, pos = wg >> 3;
+    const int t = pos / n_tiles;
+    rank = pos - t * n_tiles;
+    head = xcd + 8 * t;
+  } else {
+    head = wg / n_tiles;
+    rank = wg - head * n_tiles;
+  }
+  tile = heavy_first ? n_tiles - 1 - rank : rank;
+}
+
+}  // namespace fa

@@ -1,0 +1,132 @@
+// C-ABI entry points: argument validation, then dispatch to the kernels' launchers.
+// Every check runs before anything is launched, so a call that returns an error status
+// has launched nothing and written nothing. The library allocates nothing.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/flash_attn.h"
+#include "fa_launch.h"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+fa_status_t check_shape(int B, int H, int N, int d) {
+  if (B < 1 || H < 1 || N < 1 || d < 1) return FA_ERR_BAD_SHAPE;
+  const int64_t elems = (int64_t)B * H * N * d;
+  if (elems >= ((int64_t)1 << 31)) return FA_ERR_BAD_SHAPE;
+  return FA_OK;
+}
+
+bool supported_d(int d) { return d == 64 || d == 128; }
+
+}  // namespace
+
+extern "C" {
+
+fa_status_t flash_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
+                           int d, float scale, int causal, int dtype, void* stream) {
+  if (!q || !k || !v || !o) return FA_ERR_NULL_POINTER;
+  fa_status_t st = check_shape(B, H, N, d);
+  if (st != FA_OK) return st;
+  if ((dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_FP32) || !supported_d(d)) return FA_ERR_UNSUPPORTED;
+  if (!isfinite(scale)) return FA_ERR_BAD_SCALE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || (lse && !aligned4(lse)))
+    return FA_ERR_MISALIGNED;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = dtype == FA_DTYPE_BF16 ? fa::launch_fwd_bf16(q, k, v, o, lse, B * H, N, d, scale, causal != 0, s)
+                                        : fa::launch_fwd_fp32(q, k, v, o, lse, B * H, N, d, scale, causal != 0, s);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+size_t flash_attn_bwd_workspace_size(int B, int H, int N, int d, int dtype) {
+  (void)dtype;
+  if (check_shape(B, H, N, d) != FA_OK) return 0;
+  const size_t bytes = (size_t)B * H * N * sizeof(float);
+  return (bytes + 255) & ~(size_t)255;
+}
+
+namespace {
+// Checks shared by the backward entry points (bf16 only).
+fa_status_t check_bwd_common(int B, int H, int N, int d, float scale, int dtype) {
+  fa_status_t st = check_shape(B, H, N, d);
+  if (st != FA_OK) return st;
+  if (dtype != FA_DTYPE_BF16 || !supported_d(d)) return FA_ERR_UNSUPPORTED;
+  if (!isfinite(scale)) return FA_ERR_BAD_SCALE;
+  return FA_OK;
+}
+}  // namespace
+
+fa_status_t flash_attn_bwd_delta(const void* o, const void* dout, float* delta, int B, int H, int N, int d,
+                                 int dtype, void* stream) {
+  if (!o || !dout || !delta) return FA_ERR_NULL_POINTER;
+  fa_status_t st = check_bwd_common(B, H, N, d, 1.0f, dtype);
+  if (st != FA_OK) return st;
+  if (!aligned16(o) || !aligned16(dout) || !aligned4(delta)) return FA_ERR_MISALIGNED;
+  hipError_t e = fa::launch_bwd_delta(o, dout, delta, B * H, N, d, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+fa_status_t flash_attn_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse, const void* dout,
+                                const float* delta, void* dk, void* dv, int B, int H, int N, int d, float scale,
+                                int causal, int dtype, void* stream) {
+  if (!q || !k || !v || !lse || !dout || !delta || !dk || !dv) return FA_ERR_NULL_POINTER;
+  fa_status_t st = check_bwd_common(B, H, N, d, scale, dtype);
+  if (st != FA_OK) return st;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dout) || !aligned16(dk) || !aligned16(dv) ||
+      !aligned4(lse) || !aligned4(delta))
+    return FA_ERR_MISALIGNED;
+  hipError_t e = fa::launch_bwd_dkdv(q, k, v, lse, dout, delta, dk, dv, B * H, N, d, scale, causal != 0,
+                                     static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+fa_status_t flash_attn_bwd_dq(const void* q, const void* k, const void* v, const float* lse, const void* dout,
+                              const float* delta, void* dq, int B, int H, int N, int d, float scale, int causal,
+                              int dtype, void* stream) {
+  if (!q || !k || !v || !lse || !dout || !delta || !dq) return FA_ERR_NULL_POINTER;
+  fa_status_t st = check_bwd_common(B, H, N, d, scale, dtype);
+  if (st != FA_OK) return st;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dout) || !aligned16(dq) || !aligned4(lse) ||
+      !aligned4(delta))
+    return FA_ERR_MISALIGNED;
+  hipError_t e = fa::launch_bwd_dq(q, k, v, lse, dout, delta, dq, B * H, N, d, scale, causal != 0,
+                                   static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+fa_status_t flash_attn_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                           const void* dout, void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                           int B, int H, int N, int d, float scale, int causal, int dtype, void* stream) {
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FA_ERR_NULL_POINTER;
+  fa_status_t st = check_bwd_common(B, H, N, d, scale, dtype);
+  if (st != FA_OK) return st;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) || !aligned16(dq) ||
+      !aligned16(dk) || !aligned16(dv) || !aligned4(lse))
+    return FA_ERR_MISALIGNED;
+  if (!workspace || workspace_bytes < flash_attn_bwd_workspace_size(B, H, N, d, dtype)) return FA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return FA_ERR_MISALIGNED;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* delta = static_cast<float*>(workspace);
+  hipError_t e = fa::launch_bwd_delta(o, dout, delta, B * H, N, d, s);
+  if (e == hipSuccess) e = fa::launch_bwd_dkdv(q, k, v, lse, dout, delta, dk, dv, B * H, N, d, scale, causal != 0, s);
+  if (e == hipSuccess) e = fa::launch_bwd_dq(q, k, v, lse, dout, delta, dq, B * H, N, d, scale, causal != 0, s);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+const char* flash_attn_status_string(int status) {
+  switch (status) {
+    case FA_OK: return "FA_OK: success";
+    case FA_ERR_NULL_POINTER: return "FA_ERR_NULL_POINTER: a required pointer is NULL";
+    case FA_ERR_BAD_SHAPE: return "FA_ERR_BAD_SHAPE: B, H, N, d must be >= 1 and each tensor < 2^31 elements";
+    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: (dtype, head dim, pass) not supported";
+    case FA_ERR_BAD_SCALE: return "FA_ERR_BAD_SCALE: scale must be finite";
+    case FA_ERR_MISALIGNED: return "FA_ERR_MISALIGNED: pointers must be 16-byte aligned (lse 4-byte)";
+    case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace missing or smaller than flash_attn_bwd_workspace_size()";
+    case FA_ERR_HIP: return "FA_ERR_HIP: the HIP runtime reported a launch error";
+    default: return "unknown flash_attn status";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,228 @@
+"""Python binding of libflashattn.so (argument marshalling only).
+
+The functions carry the C ABI's names. They check what only Python can see
+(device, dtype, contiguity, matching shapes), allocate outputs and the
+backward workspace with torch (PyTorch supplies device memory and the current
+stream), pass raw device pointers to the library and raise RuntimeError with
+the library's status string on any error. Every step of the attention runs in
+the library's HIP kernels; there is no fallback path. If the shared library
+has not been built, the first call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libflashattn.so")
+
+FA_DTYPE_FP32 = 0
+FA_DTYPE_BF16 = 1
+_DTYPES = {torch.float32: FA_DTYPE_FP32, torch.bfloat16: FA_DTYPE_BF16}
+
+# Names and C signatures of every exported entry point (mirrors include/flash_attn.h).
+_vp, _int, _float, _size = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+SIGNATURES = {
+    "flash_attn_fwd": (_int, [_vp, _vp, _vp, _vp, _vp, _int, _int, _int, _int, _float, _int, _int, _vp]),
+    "flash_attn_bwd_workspace_size": (_size, [_int, _int, _int, _int, _int]),
+    "flash_attn_bwd": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _size,
+                              _int, _int, _int, _int, _float, _int, _int, _vp]),
+    "flash_attn_bwd_delta": (_int, [_vp, _vp, _vp, _int, _int, _int, _int, _int, _vp]),
+    "flash_attn_bwd_dkdv": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                   _int, _int, _int, _int, _float, _int, _int, _vp]),
+    "flash_attn_bwd_dq": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                 _int, _int, _int, _int, _float, _int, _int, _vp]),
+    "flash_attn_status_string": (ctypes.c_char_p, [_int]),
+}
+
+_lib_handle = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the HIP library once and declare its signatures. Raises if it is not built."""
+    global _lib_handle
+    if _lib_handle is None:
+        if not os.path.exists(path):
+            raise RuntimeError(f"HIP library {path} is not built; run __graft_entry__.build() "
+                               "or python -m io_aware_flashattention_flash_amd.build")
+        lib = ctypes.CDLL(path)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib_handle = lib
+    return _lib_handle
+
+
+def flash_attn_status_string(status: int) -> str:
+    return load_library().flash_attn_status_string(int(status)).decode()
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise RuntimeError(flash_attn_status_string(status))
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _check_tensor(name: str, t: torch.Tensor, like: Optional[torch.Tensor] = None) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous [B, H, N, d]")
+    if t.dim() != 4:
+        raise ValueError(f"{name} must be 4-D [B, H, N, d], got {tuple(t.shape)}")
+    if t.dtype not in _DTYPES:
+        raise ValueError(f"{name} must be bfloat16 or float32, got {t.dtype}")
+    if like is not None and (t.shape != like.shape or t.dtype != like.dtype or t.device != like.device):
+        raise ValueError(f"{name} must match q in shape, dtype and device")
+
+
+def _stream_handle(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def flash_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: Optional[float] = None,
+                   causal: bool = False, out: Optional[torch.Tensor] = None,
+                   lse: Optional[torch.Tensor] = None, want_lse: bool = True
+                   ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """O = softmax(scale * Q K^T [causal]) V and the natural-log LSE, on the current stream."""
+    _check_tensor("q", q)
+    _check_tensor("k", k, q)
+    _check_tensor("v", v, q)
+    B, H, N, d = q.shape
+    scale = float(d) ** -0.5 if scale is None else float(scale)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check_tensor("out", out, q)
+    if lse is None and want_lse:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N) or not lse.is_contiguous()
+                            or lse.device != q.device):
+        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor on q's device")
+    st = load_library().flash_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, d, scale,
+                                       int(bool(causal)), _DTYPES[q.dtype], _stream_handle(q))
+    _check(st)
+    return out, lse
+
+
+def flash_attn_bwd_workspace_size(B: int, H: int, N: int, d: int, dtype: int = FA_DTYPE_BF16) -> int:
+    return int(load_library().flash_attn_bwd_workspace_size(B, H, N, d, dtype))
+
+
+def flash_attn_bwd(dout: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
+                   lse: torch.Tensor, scale: Optional[float] = None, causal: bool = False,
+                   dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
+                   dv: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None
+                   ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """dQ, dK, dV of sum(O * dout), recomputing P from the forward's O and LSE."""
+    _check_tensor("q", q)
+    for name, t in (("k", k), ("v", v), ("o", o), ("dout", dout)):
+        _check_tensor(name, t, q)
+    B, H, N, d = q.shape
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, N) or not lse.is_contiguous() \
+            or lse.device != q.device:
+        raise ValueError("lse must be a contiguous float32 [B, H, N] tensor on q's device")
+    scale = float(d) ** -0.5 if scale is None else float(scale)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _check_tensor(name, t, q)
+    dt = _DTYPES[q.dtype]
+    need = flash_attn_bwd_workspace_size(B, H, N, d, dt)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    if workspace.device != q.device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on q's device")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = load_library().flash_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
+                                       _ptr(dk), _ptr(dv), _ptr(workspace), ws_bytes, B, H, N, d, scale,
+                                       int(bool(causal)), dt, _stream_handle(q))
+    _check(st)
+    return dq, dk, dv
+
+
+def _check_rows(name: str, t: torch.Tensor, q: torch.Tensor) -> None:
+    B, H, N, _ = q.shape
+    if t.dtype != torch.float32 or tuple(t.shape) != (B, H, N) or not t.is_contiguous() or t.device != q.device:
+        raise ValueError(f"{name} must be a contiguous float32 [B, H, N] tensor on q's device")
+
+
+def flash_attn_bwd_delta(o: torch.Tensor, dout: torch.Tensor, delta: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Backward stage 1: delta = rowsum(dout * o), float32 [B, H, N]."""
+    _check_tensor("o", o)
+    _check_tensor("dout", dout, o)
+    B, H, N, d = o.shape
+    if delta is None:
+        delta = torch.empty((B, H, N), dtype=torch.float32, device=o.device)
+    _check_rows("delta", delta, o)
+    _check(load_library().flash_attn_bwd_delta(_ptr(o), _ptr(dout), _ptr(delta), B, H, N, d, _DTYPES[o.dtype],
+                                               _stream_handle(o)))
+    return delta
+
+
+def flash_attn_bwd_dkdv(q, k, v, lse, dout, delta, scale=None, causal=False, dk=None, dv=None):
+    """Backward stage 2 (key-outer recompute): dK and dV."""
+    _check_tensor("q", q)
+    for name, t in (("k", k), ("v", v), ("dout", dout)):
+        _check_tensor(name, t, q)
+    _check_rows("lse", lse, q)
+    _check_rows("delta", delta, q)
+    B, H, N, d = q.shape
+    scale = float(d) ** -0.5 if scale is None else float(scale)
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    _check_tensor("dk", dk, q)
+    _check_tensor("dv", dv, q)
+    _check(load_library().flash_attn_bwd_dkdv(_ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(dout), _ptr(delta),
+                                              _ptr(dk), _ptr(dv), B, H, N, d, scale, int(bool(causal)),
+                                              _DTYPES[q.dtype], _stream_handle(q)))
+    return dk, dv
+
+
+def flash_attn_bwd_dq(q, k, v, lse, dout, delta, scale=None, causal=False, dq=None):
+    """Backward stage 3 (query-outer recompute): dQ."""
+    _check_tensor("q", q)
+    for name, t in (("k", k), ("v", v), ("dout", dout)):
+        _check_tensor(name, t, q)
+    _check_rows("lse", lse, q)
+    _check_rows("delta", delta, q)
+    B, H, N, d = q.shape
+    scale = float(d) ** -0.5 if scale is None else float(scale)
+    dq = torch.empty_like(q) if dq is None else dq
+    _check_tensor("dq", dq, q)
+    _check(load_library().flash_attn_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(dout), _ptr(delta),
+                                            _ptr(dq), B, H, N, d, scale, int(bool(causal)), _DTYPES[q.dtype],
+                                            _stream_handle(q)))
+    return dq
+
+
+class FlashAttnFunction(torch.autograd.Function):
+    """autograd wrapper: forward saves (q, k, v, o, lse); backward calls flash_attn_bwd."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, scale=None, causal=False):
+        o, lse = flash_attn_fwd(q, k, v, scale, causal)
+        ctx.save_for_backward(q, k, v, o, lse)
+        ctx.scale = scale
+        ctx.causal = causal
+        return o
+
+    @staticmethod
+    def backward(ctx, do):
+        q, k, v, o, lse = ctx.saved_tensors
+        dq, dk, dv = flash_attn_bwd(do.contiguous(), q, k, v, o, lse, ctx.scale, ctx.causal)
+        return dq, dk, dv, None, None
+
+
+def flash_attention(q, k, v, scale=None, causal=False):
+    return FlashAttnFunction.apply(q, k, v, scale, causal)

@@ -1,0 +1,182 @@
+"""CPU-side tests of the C ABI: the library loads, exports every symbol the header declares,
+and rejects each invalid argument with its status before anything is launched.
+
+Every call here fails validation (NULL or fake host addresses are never dereferenced: the
+library returns before any HIP call), so these tests need no GPU."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+from io_aware_flashattention_flash_amd import flash_attn as fa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "flash_attn.h")
+
+OK, NULLP, SHAPE, UNSUP, SCALE, ALIGN, WS, HIP = range(8)
+A = 0x10000  # a 16-byte-aligned fake address; never dereferenced (validation fails first)
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(fa.LIB_PATH):
+        pytest.skip("libflashattn.so not built (run __graft_entry__.build())")
+    return fa.load_library()
+
+
+def _header_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:fa_status_t|size_t|const char\*)\s+(flash_attn_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_every_bound_entry_point():
+    assert _header_functions() == sorted(fa.SIGNATURES)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _header_functions():
+        assert hasattr(lib, name), name
+
+
+def test_exports_have_c_linkage():
+    """The shared object's dynamic symbol table carries the plain C names (no C++ mangling)."""
+    import subprocess
+    if not os.path.exists(fa.LIB_PATH):
+        pytest.skip("not built")
+    out = subprocess.run(["nm", "-D", "--defined-only", fa.LIB_PATH], capture_output=True, text=True).stdout
+    names = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for name in _header_functions():
+        assert name in names, name
+
+
+def test_status_strings(lib):
+    for s in range(8):
+        txt = fa.flash_attn_status_string(s)
+        assert txt.startswith("FA_"), txt
+    assert "unknown" in fa.flash_attn_status_string(99)
+
+
+def _fwd(lib, q=A, k=A, v=A, o=A, lse=A, B=1, H=1, N=8, d=64, scale=0.125, causal=0, dtype=1):
+    return lib.flash_attn_fwd(q, k, v, o, lse, B, H, N, d, scale, causal, dtype, None)
+
+
+def _bwd(lib, ptrs=None, ws=A, ws_bytes=1 << 20, B=1, H=1, N=8, d=64, scale=0.125, causal=0, dtype=1):
+    p = dict(q=A, k=A, v=A, o=A, lse=A, do=A, dq=A, dk=A, dv=A)
+    p.update(ptrs or {})
+    return lib.flash_attn_bwd(p["q"], p["k"], p["v"], p["o"], p["lse"], p["do"], p["dq"], p["dk"], p["dv"],
+                              ws, ws_bytes, B, H, N, d, scale, causal, dtype, None)
+
+
+@pytest.mark.parametrize("which", ["q", "k", "v", "o"])
+def test_fwd_null_pointer(lib, which):
+    assert _fwd(lib, **{which: None}) == NULLP
+
+
+@pytest.mark.parametrize("shape", [(0, 1, 8, 64), (1, 0, 8, 64), (1, 1, 0, 64), (1, 1, 8, 0), (-1, 1, 8, 64),
+                                   (1 << 10, 1 << 10, 1 << 10, 64)])
+def test_fwd_bad_shape(lib, shape):
+    B, H, N, d = shape
+    assert _fwd(lib, B=B, H=H, N=N, d=d) == SHAPE
+
+
+@pytest.mark.parametrize("d,dtype", [(32, 1), (96, 1), (256, 1), (80, 0), (64, 2), (64, -1)])
+def test_fwd_unsupported(lib, d, dtype):
+    assert _fwd(lib, d=d, dtype=dtype) == UNSUP
+
+
+@pytest.mark.parametrize("scale", [math.nan, math.inf, -math.inf])
+def test_fwd_bad_scale(lib, scale):
+    assert _fwd(lib, scale=scale) == SCALE
+
+
+@pytest.mark.parametrize("which,addr", [("q", A + 8), ("k", A + 4), ("v", A + 2), ("o", A + 1), ("lse", A + 2)])
+def test_fwd_misaligned(lib, which, addr):
+    assert _fwd(lib, **{which: addr}) == ALIGN
+
+
+@pytest.mark.parametrize("which", ["q", "k", "v", "o", "lse", "do", "dq", "dk", "dv"])
+def test_bwd_null_pointer(lib, which):
+    assert _bwd(lib, {which: None}) == NULLP
+
+
+def test_bwd_unsupported_fp32_and_head_dim(lib):
+    assert _bwd(lib, dtype=0) == UNSUP
+    assert _bwd(lib, d=96) == UNSUP
+
+
+def test_bwd_bad_scale_and_shape(lib):
+    assert _bwd(lib, scale=math.nan) == SCALE
+    assert _bwd(lib, N=0) == SHAPE
+
+
+def test_bwd_workspace(lib):
+    need = lib.flash_attn_bwd_workspace_size(2, 3, 100, 64, 1)
+    assert need >= 2 * 3 * 100 * 4 and need % 256 == 0
+    assert need < 2 * 3 * 100 * 100 * 4  # linear in N: no N x N scratch
+    assert _bwd(lib, ws=None, B=2, H=3, N=100) == WS
+    assert _bwd(lib, ws_bytes=need - 1, B=2, H=3, N=100) == WS
+    assert _bwd(lib, ws=A + 4, ws_bytes=need, B=2, H=3, N=100) == ALIGN
+
+
+def test_workspace_size_invalid_shape_is_zero(lib):
+    assert lib.flash_attn_bwd_workspace_size(0, 1, 1, 64, 1) == 0
+
+
+@pytest.mark.parametrize("which", ["q", "o", "do", "dq", "dk", "dv"])
+def test_bwd_misaligned(lib, which):
+    assert _bwd(lib, {which: A + 8}) == ALIGN
+
+
+def test_python_binding_rejects_cpu_tensors():
+    import torch
+    x = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fa.flash_attn_fwd(x, x, x)
+
+
+def test_signature_table_matches_header_parameter_counts():
+    text = open(HEADER).read()
+    for name, (_, args) in fa.SIGNATURES.items():
+        m = re.search(r"^\s*(?:fa_status_t|size_t|const char\*)\s+" + name + r"\s*\(([^)]*)\)", text, re.M)
+        assert m, name
+        nparams = len([p for p in m.group(1).split(",") if p.strip()])
+        assert nparams == len(args), (name, nparams, len(args))
+
+
+def _stage_args(**kw):
+    a = dict(q=A, k=A, v=A, lse=A, do=A, delta=A, dk=A, dv=A, dq=A, B=1, H=1, N=8, d=64, scale=0.125, causal=0,
+             dtype=1)
+    a.update(kw)
+    return a
+
+
+def _dkdv(lib, **kw):
+    a = _stage_args(**kw)
+    return lib.flash_attn_bwd_dkdv(a["q"], a["k"], a["v"], a["lse"], a["do"], a["delta"], a["dk"], a["dv"], a["B"],
+                                   a["H"], a["N"], a["d"], a["scale"], a["causal"], a["dtype"], None)
+
+
+def _dq(lib, **kw):
+    a = _stage_args(**kw)
+    return lib.flash_attn_bwd_dq(a["q"], a["k"], a["v"], a["lse"], a["do"], a["delta"], a["dq"], a["B"], a["H"],
+                                 a["N"], a["d"], a["scale"], a["causal"], a["dtype"], None)
+
+
+def test_bwd_stage_validation(lib):
+    assert lib.flash_attn_bwd_delta(None, A, A, 1, 1, 8, 64, 1, None) == NULLP
+    assert lib.flash_attn_bwd_delta(A, A, A + 2, 1, 1, 8, 64, 1, None) == ALIGN
+    assert lib.flash_attn_bwd_delta(A, A, A, 1, 1, 8, 96, 1, None) == UNSUP
+    assert lib.flash_attn_bwd_delta(A, A, A, 1, 1, 0, 64, 1, None) == SHAPE
+    for fn in (_dkdv, _dq):
+        assert fn(lib, q=None) == NULLP
+        assert fn(lib, delta=None) == NULLP
+        assert fn(lib, dtype=0) == UNSUP
+        assert fn(lib, d=32) == UNSUP
+        assert fn(lib, scale=math.inf) == SCALE
+        assert fn(lib, N=0) == SHAPE
+        assert fn(lib, k=A + 8) == ALIGN
+        assert fn(lib, lse=A + 1) == ALIGN
+    assert _dkdv(lib, dv=None) == NULLP
+    assert _dq(lib, dq=A + 8) == ALIGN

@@ -46,6 +46,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="bound on the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-workloads", action="store_true", help="skip the forward-only workloads")
+    ap.add_argument("--workload", default=None,
+                    help="time only this workload (any name in inputs.WORKLOADS) and print its own JSON line; "
+                         "used to profile one kernel at a time")
     return ap.parse_args()
 
 
@@ -69,6 +72,35 @@ def traffic_for(kernel: str):
     return rec.get("bytes_per_launch")
 
 
+def time_forward(name, reps, warmup, dev, to_dev):
+    """Forward-only timing of one workload (HIP events around `reps` back-to-back launches)."""
+    import torch
+
+    from io_aware_flashattention_flash_amd import flash_attn_fwd, inputs
+
+    wl = inputs.WORKLOADS[name]
+    xi = inputs.make_inputs(wl)
+    dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    qi, ki, vi = (to_dev(xi[n], dt) for n in ("q", "k", "v"))
+    oi = torch.empty_like(qi)
+    li = torch.empty(wl.B, wl.H, wl.N, device=dev)
+    for _ in range(warmup):
+        flash_attn_fwd(qi, ki, vi, wl.scale, wl.causal, out=oi, lse=li)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(reps):
+        flash_attn_fwd(qi, ki, vi, wl.scale, wl.causal, out=oi, lse=li)
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) / reps * 1e3
+    tf = wl.fwd_flops() / (us * 1e-6) / 1e12
+    peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_FP32_TFLOPS
+    nbytes = wl.B * wl.H * (4 * wl.N * wl.d * (2 if dt == torch.bfloat16 else 4) + 4 * wl.N)
+    return {"workload": name, "pass": "fwd", "us": round(us, 2), "tflops": round(tf, 1),
+            "pct_of_peak": round(100 * tf / peak, 2), "gbps_algorithmic": round(nbytes / (us * 1e-6) / 1e9, 1)}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -88,6 +120,10 @@ def main():
 
     def to_dev(a, dt):
         return torch.from_numpy(a).to(dev).to(dt)
+
+    if args.workload is not None and args.workload != HEADLINE:
+        print(json.dumps(time_forward(args.workload, args.steps, args.warmup, dev, to_dev)))
+        return
 
     # ------------------------------------------------------------------ headline: fwd + bwd
     w = inputs.WORKLOADS[HEADLINE]
@@ -161,32 +197,8 @@ def main():
     workloads = {}
     if not args.no_workloads:
         for name, wl in inputs.WORKLOADS.items():
-            if wl.backward:
-                continue
-            xi = inputs.make_inputs(wl)
-            dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
-            qi, ki, vi = (to_dev(xi[n], dt) for n in ("q", "k", "v"))
-            oi = torch.empty_like(qi)
-            li = torch.empty(wl.B, wl.H, wl.N, device=dev)
-            reps = 20
-            for _ in range(5):
-                flash_attn_fwd(qi, ki, vi, wl.scale, wl.causal, out=oi, lse=li)
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            torch.cuda.synchronize()
-            a.record()
-            for _ in range(reps):
-                flash_attn_fwd(qi, ki, vi, wl.scale, wl.causal, out=oi, lse=li)
-            b.record()
-            torch.cuda.synchronize()
-            us = a.elapsed_time(b) / reps * 1e3
-            tf = wl.fwd_flops() / (us * 1e-6) / 1e12
-            peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_FP32_TFLOPS
-            workloads[name] = {"pass": "fwd", "us": round(us, 2), "tflops": round(tf, 1),
-                               "pct_of_peak": round(100 * tf / peak, 2),
-                               "gbps_algorithmic": round(wl.B * wl.H * (4 * wl.N * wl.d * (2 if dt == torch.bfloat16
-                                                                                            else 4) + 4 * wl.N)
-                                                         / (us * 1e-6) / 1e9, 1)}
-            del qi, ki, vi, oi, li
+            if not wl.backward:
+                workloads[name] = time_forward(name, 20, 5, dev, to_dev)
         torch.cuda.empty_cache()
 
     # ------------------------------------------------------------------ CPU oracle baseline

@@ -38,7 +38,8 @@
  *              reported as FA_ERR_HIP.
  *   Support    bf16: d in {64, 128}, forward and backward.
  *              fp32: d in {64, 128}, forward only.
- *              B, H, N >= 1 and B*H*N*d < 2^31 elements per tensor.
+ *              B, H, N >= 1, B*H*N*d < 2^31 elements per tensor and
+ *              N*d < 2^29 (one head is addressed with 32-bit byte offsets).
  */
 #ifndef FLASH_ATTN_H_
 #define FLASH_ATTN_H_
@@ -52,7 +53,7 @@ extern "C" {
 typedef enum {
   FA_OK = 0,
   FA_ERR_NULL_POINTER = 1, /* a required pointer is NULL */
-  FA_ERR_BAD_SHAPE = 2,    /* B, H, N or d < 1, or a tensor exceeds 2^31 elements */
+  FA_ERR_BAD_SHAPE = 2,    /* B, H, N or d < 1, a tensor exceeds 2^31 elements, or N*d >= 2^29 */
   FA_ERR_UNSUPPORTED = 3,  /* (dtype, d, pass) outside the support matrix */
   FA_ERR_BAD_SCALE = 4,    /* scale is NaN or infinite */
   FA_ERR_MISALIGNED = 5,   /* a pointer is not 16-byte aligned */

@@ -44,10 +44,15 @@ __device__ __forceinline__ f32x16 mfma_f32_32x32x2(float a, float b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
 
+// NaN-propagating maximum (IEEE 754-2019 maximum): v_maximum3_f32 on gfx950, with no quieting
+// of the inputs, unlike fmaxf.
+__device__ __forceinline__ float vmax(float a, float b) { return __builtin_elementwise_maximum(a, b); }
+__device__ __forceinline__ float vmax3(float a, float b, float c) { return vmax(a, vmax(b, c)); }
+
 // Max / sum of a lane value with the lane 32 apart (the other half of a 32-row block).
 __device__ __forceinline__ float half_swap_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return vmax(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float half_swap_min(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -86,6 +91,32 @@ struct SwizzledTile {
     return chunk_off(row, col >> 3) + (col & 7) * 2;
   }
 };
+
+// Buffer resources (V#) for bounds-checked loads/stores: an access at byte offset >= num_bytes
+// reads zero / is dropped. Word 3 selects the raw 32-bit data format used for untyped access.
+constexpr int kBufferWord3 = 0x00020000;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int num_bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, num_bytes, kBufferWord3);
+}
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+__device__ __forceinline__ void buf_store8(__amdgpu_buffer_rsrc_t r, int off, u32x2 v) {
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, 0);
+}
+__device__ __forceinline__ void buf_store16(__amdgpu_buffer_rsrc_t r, int off, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
+}
+__device__ __forceinline__ void buf_store4(__amdgpu_buffer_rsrc_t r, int off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, 0);
+}
+// Global -> LDS without registers: lane l's 16 bytes at byte offset `off` land at lds_dst + 16*l
+// (lds_dst must be wave-uniform; it is placed in M0). Out-of-range lanes deposit zeros.
+__device__ __forceinline__ void buf_load16_to_lds(__amdgpu_buffer_rsrc_t r, char* lds_dst, int off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_dst, 16, off, 0, 0, 0);
+}
+// Wait until this wave's outstanding vector-memory operations (including LDS DMA) have completed.
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 __device__ __forceinline__ bf16x8 lds_read16(const char* base, int off) {
   return *reinterpret_cast<const bf16x8*>(base + off);

@@ -16,6 +16,8 @@ fa_status_t check_shape(int B, int H, int N, int d) {
   if (B < 1 || H < 1 || N < 1 || d < 1) return FA_ERR_BAD_SHAPE;
   const int64_t elems = (int64_t)B * H * N * d;
   if (elems >= ((int64_t)1 << 31)) return FA_ERR_BAD_SHAPE;
+  // One head is addressed with 32-bit byte offsets (buffer descriptors).
+  if ((int64_t)N * d >= ((int64_t)1 << 29)) return FA_ERR_BAD_SHAPE;
   return FA_OK;
 }
 

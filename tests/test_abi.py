@@ -75,7 +75,7 @@ def test_fwd_null_pointer(lib, which):
 
 
 @pytest.mark.parametrize("shape", [(0, 1, 8, 64), (1, 0, 8, 64), (1, 1, 0, 64), (1, 1, 8, 0), (-1, 1, 8, 64),
-                                   (1 << 10, 1 << 10, 1 << 10, 64)])
+                                   (1 << 10, 1 << 10, 1 << 10, 64), (1, 1, 1 << 23, 64)])
 def test_fwd_bad_shape(lib, shape):
     B, H, N, d = shape
     assert _fwd(lib, B=B, H=H, N=N, d=d) == SHAPE

@@ -41,8 +41,8 @@ KERNEL_SOURCES = {
 def parse():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--cpu-seconds", type=float, default=10.0, help="bound on the CPU-oracle sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-workloads", action="store_true", help="skip the forward-only workloads")
@@ -86,6 +86,13 @@ def time_forward(name, reps, warmup, dev, to_dev):
     li = torch.empty(wl.B, wl.H, wl.N, device=dev)
     for _ in range(warmup):
         flash_attn_fwd(qi, ki, vi, wl.scale, wl.causal, out=oi, lse=li)
+    if reps is None:  # about 0.3 s of back-to-back launches, so clocks settle
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        flash_attn_fwd(qi, ki, vi, wl.scale, wl.causal, out=oi, lse=li)
+        b.record()
+        torch.cuda.synchronize()
+        reps = int(min(2000, max(20, 300.0 / max(a.elapsed_time(b), 1e-3))))
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     a.record()
@@ -97,7 +104,7 @@ def time_forward(name, reps, warmup, dev, to_dev):
     tf = wl.fwd_flops() / (us * 1e-6) / 1e12
     peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_FP32_TFLOPS
     nbytes = wl.B * wl.H * (4 * wl.N * wl.d * (2 if dt == torch.bfloat16 else 4) + 4 * wl.N)
-    return {"workload": name, "pass": "fwd", "us": round(us, 2), "tflops": round(tf, 1),
+    return {"workload": name, "pass": "fwd", "reps": reps, "us": round(us, 2), "tflops": round(tf, 1),
             "pct_of_peak": round(100 * tf / peak, 2), "gbps_algorithmic": round(nbytes / (us * 1e-6) / 1e9, 1)}
 
 
@@ -198,7 +205,7 @@ def main():
     if not args.no_workloads:
         for name, wl in inputs.WORKLOADS.items():
             if not wl.backward:
-                workloads[name] = time_forward(name, 20, 5, dev, to_dev)
+                workloads[name] = time_forward(name, None, 10, dev, to_dev)
         torch.cuda.empty_cache()
 
     # ------------------------------------------------------------------ CPU oracle baseline

@@ -21,6 +21,8 @@
 //  3. dQ kernel (query-outer): the forward's layout (S^T = K Q^T, a lane holds
 //     one query); recomputes P and dP, forms dS^T and accumulates
 //     dQ^T += K^T dS^T with K^T from the LDS transpose read.
+#include <type_traits>
+
 #include "fa_device.h"
 #include "fa_launch.h"
 
@@ -74,38 +76,44 @@ template <int D, int NW, int BQ, bool CAUSAL>
 __global__ __launch_bounds__(NW * 64, (D > 64 ? 1 : 2)) void bwd_dkdv_kernel(BwdParams p) {
   constexpr int BKV = 32 * NW;
   constexpr int NCH = D / 8;
-  constexpr int NT = NW * 64;
   constexpr int TILE_BYTES = BQ * D * 2;
-  constexpr int KCH = BQ * NCH / NT;
-  static_assert(KCH * NT == BQ * NCH, "tile must split evenly over the workgroup");
-  static_assert(BQ <= NT, "one thread per row of LSE/delta");
+  constexpr int NLD = BQ * NCH / (64 * NW);  // LDS-DMA instructions per wave per tensor per tile
+  static_assert(NLD * 64 * NW == BQ * NCH, "tile must split evenly over the workgroup's waves");
+  static_assert(BQ == 64, "wave 0 stages one LSE / delta row per lane");
+  static_assert(BKV % BQ == 0, "key tiles start on query-tile boundaries");
   constexpr int NKK = D / 16, NDB = D / 32, NQB = BQ / 32;
-  constexpr int BUF_BYTES = 2 * TILE_BYTES + 2 * BQ * 4;  // Q, dO, lse2, delta
   using T = SwizzledTile<D>;
 
-  __shared__ __attribute__((aligned(16))) char smem[2 * BUF_BYTES];
+  __shared__ __attribute__((aligned(16))) char sq0[TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) char so0[TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) char sq1[TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) char so1[TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) float sr0[2 * BQ];  // [lse * log2(e) | delta] of the tile's rows
+  __shared__ __attribute__((aligned(16))) float sr1[2 * BQ];
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6, l = tid & 63, lq = l & 31, hf = l >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l = tid & 63, lq = l & 31, hf = l >> 5;
   const int N = p.N;
   int head, kt;
-  map_workgroup(blockIdx.x, p.n_tiles, p.nh, false, head, kt);  // causal: tile 0 has the most work
+  map_workgroup(blockIdx.x, p.n_tiles, p.nh, false, head, kt);  // causal: key tile 0 has the most work
   const size_t base = (size_t)head * N * D;
   const size_t rbase = (size_t)head * N;
+  const int head_bytes = N * D * 2;
   const int key_w0 = kt * BKV + 32 * w;
   const int key = key_w0 + lq;
 
-  // K^T and V^T operands (B side of S = Q K^T and dP = dO V^T): lane (key, hf).
+  // K^T and V^T operands (B side of S = Q K^T and dP = dO V^T): lane (key, hf); keys >= N read 0.
   bf16x8 kreg[NKK], vreg[NKK];
+  {
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k + base, head_bytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + base, head_bytes);
 #pragma unroll
-  for (int kk = 0; kk < NKK; ++kk) {
-    u32x4 a = {0, 0, 0, 0}, b = {0, 0, 0, 0};
-    if (key < N) {
-      a = ld_global16(p.k + base + (size_t)key * D + 16 * kk + 8 * hf);
-      b = ld_global16(p.v + base + (size_t)key * D + 16 * kk + 8 * hf);
+    for (int kk = 0; kk < NKK; ++kk) {
+      const int off = key * (D * 2) + (16 * kk + 8 * hf) * 2;
+      kreg[kk] = __builtin_bit_cast(bf16x8, buf_load16(rk, off));
+      vreg[kk] = __builtin_bit_cast(bf16x8, buf_load16(rv, off));
     }
-    kreg[kk] = __builtin_bit_cast(bf16x8, a);
-    vreg[kk] = __builtin_bit_cast(bf16x8, b);
   }
 
   f32x16 dk[NDB], dv[NDB];
@@ -118,62 +126,52 @@ __global__ __launch_bounds__(NW * 64, (D > 64 ? 1 : 2)) void bwd_dkdv_kernel(Bwd
   const int n_qt = (N + BQ - 1) / BQ;
   const int qt0 = CAUSAL ? (kt * BKV) / BQ : 0;
 
-  u32x4 stQ[KCH], stO[KCH];
-  float stL = 0.f, stD = 0.f;
-  auto gload = [&](int i) {
+  int goff[NLD];
 #pragma unroll
-    for (int t = 0; t < KCH; ++t) {
-      const int x = tid + t * NT, r = x / NCH, c = x % NCH, row = i * BQ + r;
-      stQ[t] = u32x4{0, 0, 0, 0};
-      stO[t] = u32x4{0, 0, 0, 0};
-      if (row < N) {
-        stQ[t] = ld_global16(p.q + base + (size_t)row * D + 8 * c);
-        stO[t] = ld_global16(p.dout + base + (size_t)row * D + 8 * c);
-      }
+  for (int i = 0; i < NLD; ++i) {
+    const int pos = (w + NW * i) * 64 + l;
+    const int row = pos / NCH, pc = pos % NCH;
+    goff[i] = row * (D * 2) + ((pc ^ T::swz(row)) * 16);
+  }
+  const __amdgpu_buffer_rsrc_t rlse = make_rsrc(p.lse + rbase, N * 4);
+  const __amdgpu_buffer_rsrc_t rdel = make_rsrc(p.delta + rbase, N * 4);
+  float st_l = 0.f, st_d = 0.f;  // wave 0: this tile's row statistics, staged in registers
+  auto dma = [&](int i, char* qb, char* ob) __attribute__((always_inline)) {
+    const int row0 = i * BQ;
+    const int bytes = min(BQ, N - row0) * (D * 2);
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + base + (size_t)row0 * D, bytes);
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(p.dout + base + (size_t)row0 * D, bytes);
+#pragma unroll
+    for (int t = 0; t < NLD; ++t) {
+      buf_load16_to_lds(rq, qb + (w + NW * t) * 1024, goff[t]);
+      buf_load16_to_lds(ro, ob + (w + NW * t) * 1024, goff[t]);
     }
-    if (tid < BQ) {
-      const int row = i * BQ + tid;
-      stL = row < N ? p.lse[rbase + row] * kLog2e : 0.f;
-      stD = row < N ? p.delta[rbase + row] : 0.f;
+    if (w == 0) {
+      st_l = buf_load4f(rlse, (row0 + l) * 4) * kLog2e;
+      st_d = buf_load4f(rdel, (row0 + l) * 4);
     }
   };
-  auto swrite = [&](int buf) {
-    char* qb = smem + buf * BUF_BYTES;
-    char* ob = qb + TILE_BYTES;
-    float* lb = reinterpret_cast<float*>(ob + TILE_BYTES);
-#pragma unroll
-    for (int t = 0; t < KCH; ++t) {
-      const int x = tid + t * NT, r = x / NCH, c = x % NCH;
-      const int off = T::chunk_off(r, c);
-      lds_write16(qb, off, stQ[t]);
-      lds_write16(ob, off, stO[t]);
-    }
-    if (tid < BQ) {
-      lb[tid] = stL;
-      lb[BQ + tid] = stD;
+  auto stage_rows = [&](float* sr) __attribute__((always_inline)) {
+    if (w == 0) {
+      sr[l] = st_l;
+      sr[BQ + l] = st_d;
     }
   };
 
   const int g16 = l >> 4, j16 = l & 15;
   const int tr_row_lane = 4 * hf + (j16 >> 2);
   const int tr_col_lane = 16 * (g16 & 1) + 4 * (j16 & 3);
+  const float c = p.c;
 
-  if (qt0 < n_qt) {
-    gload(qt0);
-    swrite(qt0 & 1);
-  }
-  __syncthreads();
-
-  for (int i = qt0; i < n_qt; ++i) {
-    if (i + 1 < n_qt) gload(i + 1);
-    const char* qbuf = smem + (i & 1) * BUF_BYTES;
-    const char* obuf = qbuf + TILE_BYTES;
-    const float* lbuf = reinterpret_cast<const float*>(obuf + TILE_BYTES);
+  // One query tile. DIAG (causal only): the tile meets this key tile's diagonal, so blocks
+  // entirely before a wave's keys are skipped and the rest are masked. Query rows >= N need no
+  // mask here: their Q and dO rows arrive as zeros, so they add nothing to dK or dV.
+  auto compute = [&](auto diag_tag, int i, const char* qbuf, const char* obuf, const float* sr) __attribute__((always_inline)) {
+    constexpr bool DIAG = decltype(diag_tag)::value;
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
       const int q0 = i * BQ + 32 * qb;
-      if (q0 >= N) continue;                          // ragged last tile
-      if (CAUSAL && q0 + 31 < key_w0) continue;       // every query precedes every key of this wave
+      if (DIAG && q0 + 31 < key_w0) continue;  // wave-uniform: every query precedes every key
       f32x16 s = f32x16{}, dp = f32x16{};
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
@@ -181,27 +179,24 @@ __global__ __launch_bounds__(NW * 64, (D > 64 ? 1 : 2)) void bwd_dkdv_kernel(Bwd
         s = mfma_bf16_32x32x16(lds_read16(qbuf, off), kreg[kk], s);
         dp = mfma_bf16_32x32x16(lds_read16(obuf, off), vreg[kk], dp);
       }
-      const bool need_mask = (q0 + 32 > N) || (CAUSAL && q0 < key_w0 + 31);
+      // Register r holds query q0 + 8*(r/4) + 4*hf + r%4 against this lane's key.
+      const int kmin = key - q0 - 4 * hf;  // (DIAG) query offsets below this are masked
       bf16x8 pb[2], dsb[2];
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const f32x4 lse4 = *reinterpret_cast<const f32x4*>(lbuf + 32 * qb + 8 * g + 4 * hf);
-        const f32x4 dl4 = *reinterpret_cast<const f32x4*>(lbuf + BQ + 32 * qb + 8 * g + 4 * hf);
+        const f32x4 lse4 = *reinterpret_cast<const f32x4*>(sr + 32 * qb + 8 * g + 4 * hf);
+        const f32x4 dl4 = *reinterpret_cast<const f32x4*>(sr + BQ + 32 * qb + 8 * g + 4 * hf);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * g + e;
-          float pr = fast_exp2(s[r] * p.c - lse4[e]);
-          if (need_mask) {
-            const int qr = q0 + 8 * g + 4 * hf + e;
-            if (qr >= N || (CAUSAL && key > qr)) pr = 0.f;
-          }
-          const float ds = pr * (dp[r] - dl4[e]);
+          float pr = fast_exp2(fmaf(s[r], c, -lse4[e]));
+          if constexpr (DIAG) pr = (8 * g + e < kmin) ? 0.f : pr;
           pb[r >> 3][r & 7] = (bf16)pr;
-          dsb[r >> 3][r & 7] = (bf16)ds;
+          dsb[r >> 3][r & 7] = (bf16)(pr * (dp[r] - dl4[e]));
         }
       }
       // dV^T += dO^T P and dK^T += Q^T dS; k-step ks covers queries
-      // 32qb + 16ks + {4hf..4hf+3, 8+4hf..8+4hf+3}.
+      // 32qb + 16ks + {4hf..4hf+3, 8+4hf..8+4hf+3} (registers 8ks..8ks+7).
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
         const int col = 32 * db + tr_col_lane;
@@ -214,26 +209,53 @@ __global__ __launch_bounds__(NW * 64, (D > 64 ? 1 : 2)) void bwd_dkdv_kernel(Bwd
         }
       }
     }
-    if (i + 1 < n_qt) swrite((i + 1) & 1);
+  };
+  // Ping-pong over two LDS buffers: query tile i+1 streams in while tile i is computed. A causal
+  // key tile's first BKV / BQ query tiles meet its diagonal; they run first, in their own loop, so
+  // the steady-state loop body holds only the unmasked path.
+  constexpr int NDIAG = CAUSAL ? BKV / BQ : 0;
+  static_assert(NDIAG % 2 == 0, "the diagonal section must keep the buffer parity");
+  auto pair = [&](auto diag_tag, int i) __attribute__((always_inline)) {
+    if (i + 1 < n_qt) dma(i + 1, sq1, so1);
+    compute(diag_tag, i, sq0, so0, sr0);
+    wait_vmem();
+    stage_rows(sr1);
     __syncthreads();
+    if (i + 1 < n_qt) {
+      if (i + 2 < n_qt) dma(i + 2, sq0, so0);
+      compute(diag_tag, i + 1, sq1, so1, sr1);
+      wait_vmem();
+      stage_rows(sr0);
+      __syncthreads();
+    }
+  };
+  if (qt0 < n_qt) {
+    dma(qt0, sq0, so0);
+    stage_rows(sr0);
+    wait_vmem();
+    __syncthreads();
+    int i = qt0;
+#pragma unroll 1
+    for (; i < qt0 + NDIAG && i < n_qt; i += 2) pair(std::true_type{}, i);
+#pragma unroll 1
+    for (; i < n_qt; i += 2) pair(std::false_type{}, i);
   }
 
-  if (key < N) {
-    bf16* dKr = p.dk + base + (size_t)key * D;
-    bf16* dVr = p.dv + base + (size_t)key * D;
+  const __amdgpu_buffer_rsrc_t rdk = make_rsrc(p.dk + base, head_bytes);
+  const __amdgpu_buffer_rsrc_t rdv = make_rsrc(p.dv + base, head_bytes);
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
+  for (int db = 0; db < NDB; ++db) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        bf16x4 a, b;
+    for (int g = 0; g < 4; ++g) {
+      bf16x4 a, b;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          a[e] = (bf16)(dk[db][4 * g + e] * p.scale);
-          b[e] = (bf16)dv[db][4 * g + e];
-        }
-        *reinterpret_cast<bf16x4*>(dKr + 32 * db + 8 * g + 4 * hf) = a;
-        *reinterpret_cast<bf16x4*>(dVr + 32 * db + 8 * g + 4 * hf) = b;
+      for (int e = 0; e < 4; ++e) {
+        a[e] = (bf16)(dk[db][4 * g + e] * p.scale);
+        b[e] = (bf16)dv[db][4 * g + e];
       }
+      const int off = key * (D * 2) + (32 * db + 8 * g + 4 * hf) * 2;
+      buf_store8(rdk, off, __builtin_bit_cast(u32x2, a));
+      buf_store8(rdv, off, __builtin_bit_cast(u32x2, b));
     }
   }
 }
@@ -245,37 +267,43 @@ template <int D, int BC, int NW, bool CAUSAL>
 __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdParams p) {
   constexpr int BR = 32 * NW;
   constexpr int NCH = D / 8;
-  constexpr int NT = NW * 64;
   constexpr int TILE_BYTES = BC * D * 2;
-  constexpr int KCH = BC * NCH / NT;
-  static_assert(KCH * NT == BC * NCH, "tile must split evenly over the workgroup");
+  constexpr int NLD = BC * NCH / (64 * NW);
+  static_assert(NLD * 64 * NW == BC * NCH, "tile must split evenly over the workgroup's waves");
   constexpr int NKB = BC / 32, NDB = D / 32, NKK = D / 16, NKS = BC / 16;
   using T = SwizzledTile<D>;
 
-  __shared__ __attribute__((aligned(16))) char smem[4 * TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) char sk0[TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) char sv0[TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) char sk1[TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) char sv1[TILE_BYTES];
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6, l = tid & 63, lq = l & 31, hf = l >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l = tid & 63, lq = l & 31, hf = l >> 5;
   const int N = p.N;
   int head, qt;
   map_workgroup(blockIdx.x, p.n_tiles, p.nh, CAUSAL, head, qt);
   const size_t base = (size_t)head * N * D;
+  const size_t rbase = (size_t)head * N;
+  const int head_bytes = N * D * 2;
   const int q_w0 = qt * BR + 32 * w;
   const int q = q_w0 + lq;
 
   bf16x8 qreg[NKK], oreg[NKK];
+  float lse2, dlt;
+  {
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + base, head_bytes);
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(p.dout + base, head_bytes);
 #pragma unroll
-  for (int kk = 0; kk < NKK; ++kk) {
-    u32x4 a = {0, 0, 0, 0}, b = {0, 0, 0, 0};
-    if (q < N) {
-      a = ld_global16(p.q + base + (size_t)q * D + 16 * kk + 8 * hf);
-      b = ld_global16(p.dout + base + (size_t)q * D + 16 * kk + 8 * hf);
+    for (int kk = 0; kk < NKK; ++kk) {
+      const int off = q * (D * 2) + (16 * kk + 8 * hf) * 2;
+      qreg[kk] = __builtin_bit_cast(bf16x8, buf_load16(rq, off));
+      oreg[kk] = __builtin_bit_cast(bf16x8, buf_load16(ro, off));
     }
-    qreg[kk] = __builtin_bit_cast(bf16x8, a);
-    oreg[kk] = __builtin_bit_cast(bf16x8, b);
+    lse2 = buf_load4f(make_rsrc(p.lse + rbase, N * 4), q * 4) * kLog2e;
+    dlt = buf_load4f(make_rsrc(p.delta + rbase, N * 4), q * 4);
   }
-  const float lse2 = q < N ? p.lse[(size_t)head * N + q] * kLog2e : 0.f;
-  const float dlt = q < N ? p.delta[(size_t)head * N + q] : 0.f;
 
   int n_kv = (N + BC - 1) / BC;
   if (CAUSAL) n_kv = min(n_kv, (min(N, (qt + 1) * BR) - 1) / BC + 1);
@@ -284,99 +312,109 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
   for (int db = 0; db < NDB; ++db) dq[db] = f32x16{};
 
-  u32x4 stK[KCH], stV[KCH];
-  auto gload = [&](int j) {
+  int goff[NLD];
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int x = tid + i * NT, r = x / NCH, c = x % NCH, key = j * BC + r;
-      stK[i] = u32x4{0, 0, 0, 0};
-      stV[i] = u32x4{0, 0, 0, 0};
-      if (key < N) {
-        stK[i] = ld_global16(p.k + base + (size_t)key * D + 8 * c);
-        stV[i] = ld_global16(p.v + base + (size_t)key * D + 8 * c);
-      }
-    }
-  };
-  auto swrite = [&](int buf) {
-    char* kb = smem + buf * 2 * TILE_BYTES;
-    char* vb = kb + TILE_BYTES;
+  for (int i = 0; i < NLD; ++i) {
+    const int pos = (w + NW * i) * 64 + l;
+    const int row = pos / NCH, pc = pos % NCH;
+    goff[i] = row * (D * 2) + ((pc ^ T::swz(row)) * 16);
+  }
+  auto dma = [&](int j, char* kb, char* vb) __attribute__((always_inline)) {
+    const int key0 = j * BC;
+    const int bytes = min(BC, N - key0) * (D * 2);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k + base + (size_t)key0 * D, bytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + base + (size_t)key0 * D, bytes);
 #pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int x = tid + i * NT, r = x / NCH, c = x % NCH;
-      const int off = T::chunk_off(r, c);
-      lds_write16(kb, off, stK[i]);
-      lds_write16(vb, off, stV[i]);
+    for (int i = 0; i < NLD; ++i) {
+      buf_load16_to_lds(rk, kb + (w + NW * i) * 1024, goff[i]);
+      buf_load16_to_lds(rv, vb + (w + NW * i) * 1024, goff[i]);
     }
   };
 
   const int g16 = l >> 4, j16 = l & 15;
   const int tr_row_lane = 4 * hf + (j16 >> 2);
   const int tr_col_lane = 16 * (g16 & 1) + 4 * (j16 & 3);
+  const int key_lim = CAUSAL ? min(q, N - 1) : N - 1;
+  const float c = p.c;
 
-  gload(0);
-  swrite(0);
-  __syncthreads();
-
-  for (int j = 0; j < n_kv; ++j) {
-    if (j + 1 < n_kv) gload(j + 1);
-    const char* kbuf = smem + (j & 1) * 2 * TILE_BYTES;
-    const char* vbuf = kbuf + TILE_BYTES;
+  // One key tile; MASK for diagonal and ragged tiles (compiled separately from the clean path).
+  auto compute = [&](auto mask_tag, int j, const char* kbuf, const char* vbuf) __attribute__((always_inline)) {
+    constexpr bool MASK = decltype(mask_tag)::value;
     const int key0 = j * BC;
-    const bool active = !CAUSAL || key0 <= q_w0 + 31;
-    if (active) {
-      f32x16 s[NKB], dp[NKB];
+    // (A wave whose rows all precede this tile's keys still runs it; the mask zeroes it.)
+    f32x16 s[NKB], dp[NKB];
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        s[kb] = f32x16{};
-        dp[kb] = f32x16{};
+    for (int kb = 0; kb < NKB; ++kb) {
+      s[kb] = f32x16{};
+      dp[kb] = f32x16{};
 #pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) {
-          const int off = T::chunk_off(32 * kb + lq, 2 * kk + hf);
-          s[kb] = mfma_bf16_32x32x16(lds_read16(kbuf, off), qreg[kk], s[kb]);
-          dp[kb] = mfma_bf16_32x32x16(lds_read16(vbuf, off), oreg[kk], dp[kb]);
-        }
+      for (int kk = 0; kk < NKK; ++kk) {
+        const int off = T::chunk_off(32 * kb + lq, 2 * kk + hf);
+        s[kb] = mfma_bf16_32x32x16(lds_read16(kbuf, off), qreg[kk], s[kb]);
+        dp[kb] = mfma_bf16_32x32x16(lds_read16(vbuf, off), oreg[kk], dp[kb]);
       }
-      const bool need_mask = (key0 + BC > N) || (CAUSAL && key0 + BC - 1 > q_w0);
-      bf16x8 dsb[NKS];
+    }
+    const int lim = key_lim - key0 - 4 * hf;
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
+    for (int ks = 0; ks < NKS; ++ks) {
+      bf16x8 dsb;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float pr = fast_exp2(s[kb][r] * p.c - lse2);
-          if (need_mask) {
-            const int kr = key0 + 32 * kb + (r >> 2) * 8 + 4 * hf + (r & 3);
-            if (kr >= N || (CAUSAL && kr > q)) pr = 0.f;
-          }
-          dsb[2 * kb + (r >> 3)][r & 7] = (bf16)(pr * (dp[kb][r] - dlt));
+      for (int e = 0; e < 8; ++e) {
+        const int r = (ks & 1) * 8 + e;
+        float pr = fast_exp2(fmaf(s[ks >> 1][r], c, -lse2));
+        if constexpr (MASK) {
+          const int krel = 32 * (ks >> 1) + (r >> 2) * 8 + (r & 3);
+          pr = krel <= lim ? pr : 0.f;
         }
+        dsb[e] = (bf16)(pr * (dp[ks >> 1][r] - dlt));
       }
       // dQ^T += K^T dS^T; k-step ks covers keys 16ks + {4hf..4hf+3, 8+4hf..8+4hf+3}.
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
         const int col = 32 * db + tr_col_lane;
-#pragma unroll
-        for (int ks = 0; ks < NKS; ++ks) {
-          const bf16x4 a0 = lds_read_tr16(kbuf, T::elem_off(16 * ks + tr_row_lane, col));
-          const bf16x4 a1 = lds_read_tr16(kbuf, T::elem_off(16 * ks + 8 + tr_row_lane, col));
-          dq[db] = mfma_bf16_32x32x16(cat4(a0, a1), dsb[ks], dq[db]);
-        }
+        const bf16x4 a0 = lds_read_tr16(kbuf, T::elem_off(16 * ks + tr_row_lane, col));
+        const bf16x4 a1 = lds_read_tr16(kbuf, T::elem_off(16 * ks + 8 + tr_row_lane, col));
+        dq[db] = mfma_bf16_32x32x16(cat4(a0, a1), dsb, dq[db]);
       }
     }
-    if (j + 1 < n_kv) swrite((j + 1) & 1);
+  };
+  // Key tiles below the workgroup's diagonal (and not the ragged last tile) run unmasked in the
+  // first loop; the remaining ones run the masked path. Both keep the two-buffer ping-pong.
+  int j_mask = CAUSAL ? (qt * BR) / BC : n_kv;
+  if (N % BC != 0) j_mask = min(j_mask, n_kv - 1);
+  j_mask = min(j_mask, n_kv);
+  auto pair = [&](auto mask_tag, int j, int j_end) __attribute__((always_inline)) {
+    if (j + 1 < n_kv) dma(j + 1, sk1, sv1);
+    compute(mask_tag, j, sk0, sv0);
+    wait_vmem();
     __syncthreads();
-  }
+    if (j + 1 < j_end) {
+      if (j + 2 < n_kv) dma(j + 2, sk0, sv0);
+      compute(mask_tag, j + 1, sk1, sv1);
+      wait_vmem();
+      __syncthreads();
+    }
+  };
+  dma(0, sk0, sv0);
+  wait_vmem();
+  __syncthreads();
+  int j = 0;
+#pragma unroll 1
+  for (; j + 1 < j_mask; j += 2) pair(std::false_type{}, j, j_mask);
+  // j is even here. A single clean tile may remain before the masked ones; it is run through the
+  // masked path (its mask is all-pass), which keeps the buffer parity simple.
+#pragma unroll 1
+  for (; j < n_kv; j += 2) pair(std::true_type{}, j, n_kv);
 
-  if (q < N) {
-    bf16* dQr = p.dq + base + (size_t)q * D;
+  const __amdgpu_buffer_rsrc_t rdq = make_rsrc(p.dq + base, head_bytes);
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
+  for (int db = 0; db < NDB; ++db) {
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        bf16x4 t;
+    for (int g = 0; g < 4; ++g) {
+      bf16x4 t;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) t[e] = (bf16)(dq[db][4 * g + e] * p.scale);
-        *reinterpret_cast<bf16x4*>(dQr + 32 * db + 8 * g + 4 * hf) = t;
-      }
+      for (int e = 0; e < 4; ++e) t[e] = (bf16)(dq[db][4 * g + e] * p.scale);
+      buf_store8(rdq, q * (D * 2) + (32 * db + 8 * g + 4 * hf) * 2, __builtin_bit_cast(u32x2, t));
     }
   }
 }
@@ -385,7 +423,12 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdParams p) {
 // host side
 // ---------------------------------------------------------------------------------------------
 namespace {
-constexpr int kDqNW = 4, kDqBC = 64, kKvNW = 4, kKvBQ = 64;
+// dQ kernel: 4 waves x 32 query rows; key tiles of 64 (32 at d = 128, where the score and
+// dP blocks of a 64-key tile would not fit beside the operands in 256 VGPRs).
+// dK/dV kernel: 4 waves x 32 keys; query tiles of 64.
+constexpr int kDqNW = 4, kKvNW = 4, kKvBQ = 64;
+template <int D>
+constexpr int dq_bc() { return D == 128 ? 32 : 64; }
 
 BwdParams make_params(const void* q, const void* k, const void* v, const void* o, const float* lse,
                       const void* dout, const float* delta, void* dq, void* dk, void* dv, int BH, int N,
@@ -428,7 +471,7 @@ hipError_t dkdv_d(BwdParams prm, hipStream_t stream) {
 template <int D, bool CAUSAL>
 hipError_t dq_d(BwdParams prm, hipStream_t stream) {
   prm.n_tiles = (prm.N + 32 * kDqNW - 1) / (32 * kDqNW);
-  hipLaunchKernelGGL((bwd_dq_kernel<D, kDqBC, kDqNW, CAUSAL>), dim3(prm.n_tiles * prm.nh), dim3(kDqNW * 64), 0,
+  hipLaunchKernelGGL((bwd_dq_kernel<D, dq_bc<D>(), kDqNW, CAUSAL>), dim3(prm.n_tiles * prm.nh), dim3(kDqNW * 64), 0,
                      stream, prm);
   return hipGetLastError();
 }

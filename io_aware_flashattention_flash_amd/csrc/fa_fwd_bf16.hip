@@ -121,7 +121,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdBf16Params p) {
     const int row = pos / NCH, pc = pos % NCH;
     goff[i] = row * (D * 2) + ((pc ^ T::swz(row)) * 16);
   }
-  auto dma = [&](int j, char* kb, char* vb) {
+  auto dma = [&](int j, char* kb, char* vb) __attribute__((always_inline)) {
     const int key0 = j * BC;
     const int bytes = min(BC, N - key0) * (D * 2);
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kh + (size_t)key0 * D, bytes);
@@ -146,7 +146,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdBf16Params p) {
   float m_run = -INFINITY, l_run = 0.f, lr_run = 0.f;
   const float c = p.c;
 
-  auto compute = [&](int j, const char* kbuf, const char* vbuf) {
+  auto compute = [&](int j, const char* kbuf, const char* vbuf) __attribute__((always_inline)) {
     const int key0 = j * BC;
     // (A wave whose rows all precede this tile's keys still runs it: the mask zeroes every
     // probability. Branching around it would cost more in register copies than the ~1.5% of
@@ -193,11 +193,14 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdBf16Params p) {
       for (int db = 0; db < NDB; ++db) acc_o[db] *= alpha;
     }
     const float neg_m = (m_run == -INFINITY) ? 0.f : -m_run;
-    // P^T = exp2(s*c - m), summed in fp32, rounded to bf16 as the B operand of V^T P^T.
-    bf16x8 pk[NKS];
+    // P^T = exp2(s*c - m), summed in fp32, rounded to bf16 as the B operand of O^T += V^T P^T.
+    // k-step ks covers keys 16ks + {4hf..4hf+3, 8+4hf..8+4hf+3}, i.e. accumulator registers
+    // (ks&1)*8 + 0..7 of block ks>>1. Each k-step's products are issued as soon as its eight
+    // probabilities exist, so the matrix cores work on step ks while the VALU forms step ks+1.
     float rs0 = 0.f, rs1 = 0.f, rr = 0.f;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
+      bf16x8 pkk;
 #pragma unroll
       for (int e = 0; e < 8; e += 2) {
         const float pa = fast_exp2(fmaf(s[ks >> 1][(ks & 1) * 8 + e], c, neg_m));
@@ -206,24 +209,19 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdBf16Params p) {
         rs1 += pb;
         const bf16x2 pr = {(bf16)pa, (bf16)pb};
         rr = dot2_ones(pr, rr);
-        pk[ks][e] = pr[0];
-        pk[ks][e + 1] = pr[1];
+        pkk[e] = pr[0];
+        pkk[e + 1] = pr[1];
+      }
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const int col = 32 * db + v_col_lane;
+        const bf16x4 a0 = lds_read_tr16(vbuf, T::elem_off(16 * ks + v_row_lane, col));
+        const bf16x4 a1 = lds_read_tr16(vbuf, T::elem_off(16 * ks + 8 + v_row_lane, col));
+        acc_o[db] = mfma_bf16_32x32x16(cat4(a0, a1), pkk, acc_o[db]);
       }
     }
     l_run += rs0 + rs1;
     lr_run += rr;
-    // O^T += V^T P^T. k-step ks covers keys 16ks + {4hf..4hf+3, 8+4hf..8+4hf+3}, matching
-    // accumulator registers (ks&1)*8 + 0..7 of block ks>>1.
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        const int col = 32 * db + v_col_lane;
-        const bf16x4 a0 = lds_read_tr16(vbuf, T::elem_off(16 * ks + v_row_lane, col));
-        const bf16x4 a1 = lds_read_tr16(vbuf, T::elem_off(16 * ks + 8 + v_row_lane, col));
-        acc_o[db] = mfma_bf16_32x32x16(cat4(a0, a1), pk[ks], acc_o[db]);
-      }
-    }
   };
 
   // Ping-pong over the two LDS buffers: tile j+1 streams in while tile j is computed.

@@ -96,7 +96,7 @@ __global__ __launch_bounds__(NW * 64, (D > 64 ? 1 : 2)) void bwd_dkdv_kernel(Bwd
   const int l = tid & 63, lq = l & 31, hf = l >> 5;
   const int N = p.N;
   int head, kt;
-  map_workgroup(blockIdx.x, p.n_tiles, p.nh, false, head, kt);  // causal: key tile 0 has the most work
+  map_workgroup(blockIdx.x, p.n_tiles, p.nh, CAUSAL ? Order::kLongestFirst : Order::kHeadMajor, false, head, kt);  // causal: key tile 0 has the most work
   const size_t base = (size_t)head * N * D;
   const size_t rbase = (size_t)head * N;
   const int head_bytes = N * D * 2;
@@ -283,7 +283,7 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdParams p) {
   const int l = tid & 63, lq = l & 31, hf = l >> 5;
   const int N = p.N;
   int head, qt;
-  map_workgroup(blockIdx.x, p.n_tiles, p.nh, CAUSAL, head, qt);
+  map_workgroup(blockIdx.x, p.n_tiles, p.nh, CAUSAL ? Order::kLongestFirst : Order::kHeadMajor, true, head, qt);
   const size_t base = (size_t)head * N * D;
   const size_t rbase = (size_t)head * N;
   const int head_bytes = N * D * 2;

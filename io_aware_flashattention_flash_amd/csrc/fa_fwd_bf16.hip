@@ -88,7 +88,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdBf16Params p) {
   const int N = p.N;
 
   int head, qt;
-  map_workgroup(blockIdx.x, p.n_qt, p.nh, CAUSAL, head, qt);
+  map_workgroup(blockIdx.x, p.n_qt, p.nh, CAUSAL ? Order::kLongestFirst : Order::kHeadMajor, true, head, qt);
   const size_t base = (size_t)head * N * D;
   const bf16* Kh = p.k + base;
   const bf16* Vh = p.v + base;
@@ -241,11 +241,16 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdBf16Params p) {
   }
   if (j < n_kv) compute(j, sk0, sv0);
 
-  // Epilogue: O = O_acc / l~, LSE = ln2 * (m + log2 l). Rows >= N fall outside the buffer
-  // descriptor and are dropped.
+  // Epilogue: O = O_acc / l~, LSE = ln2 * (m + log2 l). The accumulator holds one query row per
+  // lane, so O is staged through LDS (each wave in one of the now idle tile buffers, rows padded
+  // by 16 bytes) and written back as whole rows of 16-byte chunks. Rows >= N fall outside the
+  // buffer descriptors and are dropped.
   const float l_tot = half_swap_sum(l_run);
   const float inv = 1.0f / half_swap_sum(lr_run);
-  const __amdgpu_buffer_rsrc_t ro = make_rsrc(p.o + base, head_bytes);
+  constexpr int OPITCH = D * 2 + 16;
+  static_assert(32 * OPITCH <= TILE_BYTES, "a wave's output rows must fit in one tile buffer");
+  __syncthreads();  // every wave is done reading the last K/V tile
+  char* ostage = w == 0 ? sk0 : (w == 1 ? sv0 : (w == 2 ? sk1 : sv1));
 #pragma unroll
   for (int db = 0; db < NDB; ++db) {
 #pragma unroll
@@ -253,8 +258,17 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdBf16Params p) {
       bf16x4 t;
 #pragma unroll
       for (int e = 0; e < 4; ++e) t[e] = (bf16)(acc_o[db][4 * g + e] * inv);
-      buf_store8(ro, q * (D * 2) + (32 * db + 8 * g + 4 * hf) * 2, __builtin_bit_cast(u32x2, t));
+      *reinterpret_cast<bf16x4*>(ostage + lq * OPITCH + (32 * db + 8 * g + 4 * hf) * 2) = t;
     }
+  }
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
+  __builtin_amdgcn_wave_barrier();
+  const __amdgpu_buffer_rsrc_t ro = make_rsrc(p.o + base, head_bytes);
+#pragma unroll
+  for (int i = 0; i < 32 * NCH / 64; ++i) {
+    const int x = l + 64 * i, row = x / NCH, ch = x % NCH;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(ostage + row * OPITCH + ch * 16);
+    buf_store16(ro, (q_w0 + row) * (D * 2) + ch * 16, v);
   }
   if (p.lse && hf == 0) {
     const __amdgpu_buffer_rsrc_t rl = make_rsrc(p.lse + (size_t)head * N, N * 4);

@@ -36,7 +36,7 @@ __global__ __launch_bounds__(256) void fwd_fp32_kernel(FwdF32Params p) {
   const int w = tid >> 6, l = tid & 63, lq = l & 31, hf = l >> 5;
   const int N = p.N;
   int head, qt;
-  map_workgroup(blockIdx.x, p.n_qt, p.nh, CAUSAL, head, qt);
+  map_workgroup(blockIdx.x, p.n_qt, p.nh, CAUSAL ? Order::kLongestFirst : Order::kHeadMajor, true, head, qt);
   const size_t base = (size_t)head * N * D;
   const int q_w0 = qt * BR + 32 * w;
   const int q = q_w0 + lq;

@@ -24,24 +24,39 @@ hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const floa
                          float scale, bool causal, hipStream_t stream);
 
 // Work decomposition shared by the kernels: workgroup id -> (head, tile).
-// The hardware hands consecutive workgroup ids to the 8 XCDs round-robin, each with its
-// own L2. When the head count is a multiple of 8, heads are dealt to XCDs so that all tiles
-// of one head run on one XCD (K/V of that head stay in that L2); within an XCD the heads
-// are taken one after another. With `heavy_first` the tiles of a head are issued from the
-// one with the most work (the last, for a causal mask) to the least.
-__device__ __forceinline__ void map_workgroup(int wg, int n_tiles, int nh, bool heavy_first,
+// The hardware hands consecutive workgroup ids to the 8 XCDs round-robin, each with its own L2.
+// When the head count is a multiple of 8, heads are dealt to XCDs so that all tiles of one head
+// run on one XCD (its K/V stay in that XCD's L2).
+//   kHeadMajor: within an XCD, one head's tiles after another (equal-cost tiles: keeps the
+//               fewest heads in flight, best L2 reuse).
+//   kLongestFirst: within an XCD, tile-major over its heads, tiles ordered from the most work to
+//               the least (causal tiles: longest-processing-time-first dispatch, so the last
+//               workgroups to start are the short ones and the kernel ends without a long tail).
+//               `last_is_longest` says whether tile n_tiles-1 (forward, dQ) or tile 0 (dK/dV)
+//               carries the most work.
+enum class Order { kHeadMajor, kLongestFirst };
+__device__ __forceinline__ void map_workgroup(int wg, int n_tiles, int nh, Order order, bool last_is_longest,
                                               int& head, int& tile) {
   int rank;
   if ((nh & 7) == 0) {
-    const int xcd = wg & 7, pos = wg >> 3;
-    const int t = pos / n_tiles;
-    rank = pos - t * n_tiles;
+    const int xcd = wg & 7, pos = wg >> 3, hpx = nh >> 3;
+    int t;
+    if (order == Order::kLongestFirst) {
+      t = pos % hpx;
+      rank = pos / hpx;
+    } else {
+      t = pos / n_tiles;
+      rank = pos - t * n_tiles;
+    }
     head = xcd + 8 * t;
+  } else if (order == Order::kLongestFirst) {
+    head = wg % nh;
+    rank = wg / nh;
   } else {
     head = wg / n_tiles;
     rank = wg - head * n_tiles;
   }
-  tile = heavy_first ? n_tiles - 1 - rank : rank;
+  tile = last_is_longest ? n_tiles - 1 - rank : rank;
 }
 
 }  // namespace fa

@@ -2,7 +2,7 @@
 """Attention throughput on one MI355X: TFLOPS (fwd, fwd+bwd) and % of the dense bf16 MFMA peak.
 
 One step is one pass of the whole hot path over one batch of resident synthetic input: the fused
-forward (O, LSE) followed by the three backward stages (delta, dK/dV, dQ) of the causal bf16
+forward (O, LSE) followed by the two backward stages (dQ with delta, then dK/dV) of the causal bf16
 workload B=4 H=16 N=2048 d=64. FLOPs follow the workload definition: 4*B*H*N^2*d for the
 forward, halved for the causal mask, and 2.5x that for the backward (five N x N x d products).
 
@@ -32,7 +32,6 @@ HEADLINE = "fwdbwd_bf16_b4h16n2048d64_causal"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = {
     "fwd": "fa_fwd_bf16.hip",
-    "bwd_delta": "fa_bwd_bf16.hip",
     "bwd_dkdv": "fa_bwd_bf16.hip",
     "bwd_dq": "fa_bwd_bf16.hip",
 }
@@ -117,8 +116,8 @@ def main():
     import numpy as np
     import torch
 
-    from io_aware_flashattention_flash_amd import (flash_attn_bwd_delta, flash_attn_bwd_dkdv, flash_attn_bwd_dq,
-                                                   flash_attn_fwd, inputs, load_library)
+    from io_aware_flashattention_flash_amd import (flash_attn_bwd_dkdv, flash_attn_bwd_dq, flash_attn_fwd, inputs,
+                                                   load_library)
 
     load_library()  # raises if the HIP library is not built
     dev = torch.device("cuda:0")
@@ -147,21 +146,18 @@ def main():
         flash_attn_fwd(q, k, v, w.scale, True, out=o, lse=lse)
         if evs is not None:
             evs[1].record()
-        flash_attn_bwd_delta(o, do, delta)
+        flash_attn_bwd_dq(q, k, v, o, lse, do, w.scale, True, dq=dq, delta=delta)
         if evs is not None:
             evs[2].record()
         flash_attn_bwd_dkdv(q, k, v, lse, do, delta, w.scale, True, dk=dk, dv=dv)
         if evs is not None:
             evs[3].record()
-        flash_attn_bwd_dq(q, k, v, lse, do, delta, w.scale, True, dq=dq)
-        if evs is not None:
-            evs[4].record()
 
-    names = ["fwd", "bwd_delta", "bwd_dkdv", "bwd_dq"]
+    names = ["fwd", "bwd_dq", "bwd_dkdv"]
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -178,12 +174,11 @@ def main():
 
     f_fwd, f_bwd = w.fwd_flops(), w.bwd_flops()
     value = (f_fwd + f_bwd) / (ms_step * 1e-3) / 1e12
-    kflops = {"fwd": f_fwd, "bwd_delta": 0.0, "bwd_dkdv": 2.0 * f_fwd, "bwd_dq": 0.5 * f_fwd}
+    kflops = {"fwd": f_fwd, "bwd_dkdv": 2.0 * f_fwd, "bwd_dq": 0.5 * f_fwd}
     kbytes = {  # algorithmic HBM bytes per launch (each tensor moved once)
         "fwd": w.B * w.H * (4 * w.N * w.d * 2 + 4 * w.N),
-        "bwd_delta": w.B * w.H * (2 * w.N * w.d * 2 + 4 * w.N),
         "bwd_dkdv": w.B * w.H * (6 * w.N * w.d * 2 + 8 * w.N),
-        "bwd_dq": w.B * w.H * (5 * w.N * w.d * 2 + 8 * w.N),
+        "bwd_dq": w.B * w.H * (6 * w.N * w.d * 2 + 8 * w.N),  # also reads O and writes delta
     }
     dom = max(kern_ms, key=kern_ms.get)
     bound = "hbm" if kflops[dom] == 0 else "mfma"
@@ -198,7 +193,7 @@ def main():
     kernels = {n: {"avg_us": round(kern_ms[n] * 1e3, 2),
                    "tflops": round(kflops[n] / (kern_ms[n] * 1e-3) / 1e12, 1) if kflops[n] else None,
                    "gbps_algorithmic": round(kbytes[n] / (kern_ms[n] * 1e-3) / 1e9, 1)} for n in names}
-    bwd_ms = kern_ms["bwd_delta"] + kern_ms["bwd_dkdv"] + kern_ms["bwd_dq"]
+    bwd_ms = kern_ms["bwd_dkdv"] + kern_ms["bwd_dq"]
 
     # ------------------------------------------------------------------ forward-only workloads
     workloads = {}

@@ -95,8 +95,8 @@ size_t flash_attn_bwd_workspace_size(int B, int H, int N, int d, int dtype);
  *   workspace          device scratch of at least workspace_bytes >=
  *                      flash_attn_bwd_workspace_size(); its contents on entry
  *                      are ignored; on return it holds delta (float32 [B,H,N]).
- * Runs flash_attn_bwd_delta, flash_attn_bwd_dkdv and flash_attn_bwd_dq (below)
- * in that order on `stream`. Deterministic (no atomics). bf16 only.
+ * Runs flash_attn_bwd_dq and then flash_attn_bwd_dkdv (below) on `stream`.
+ * Deterministic (no atomics). bf16 only.
  */
 fa_status_t flash_attn_bwd(const void* q, const void* k, const void* v, const void* o,
                            const float* lse, const void* dout,
@@ -106,36 +106,39 @@ fa_status_t flash_attn_bwd(const void* q, const void* k, const void* v, const vo
                            int dtype, void* stream);
 
 /*
- * The three stages flash_attn_bwd runs, in this order, exposed so a caller can
- * run (or time) them separately. Same conventions and validation as
- * flash_attn_bwd; bf16 only; deterministic.
+ * Backward stages, exposed so a caller can run (or time) them separately. Same
+ * conventions and validation as flash_attn_bwd; bf16 only; deterministic.
+ * flash_attn_bwd runs flash_attn_bwd_dq and then flash_attn_bwd_dkdv.
  *
- * Stage 1: delta[b,h,i] = sum_c dout[b,h,i,c] * o[b,h,i,c] (float32 [B,H,N],
- *          written). This is the row term that the softmax Jacobian subtracts:
- *          it equals sum_j P_ij dP_ij.
+ * flash_attn_bwd_delta: delta[b,h,i] = sum_c dout[b,h,i,c] * o[b,h,i,c]
+ * (float32 [B,H,N], written). This is the row term the softmax Jacobian
+ * subtracts: it equals sum_j P_ij dP_ij. (flash_attn_bwd_dq computes the same
+ * values as a by-product; this stage exists for callers that want delta alone.)
  */
 fa_status_t flash_attn_bwd_delta(const void* o, const void* dout, float* delta,
                                  int B, int H, int N, int d, int dtype, void* stream);
 
 /*
- * Stage 2 (key-outer): for every key tile, recompute P = exp(scale*Q K^T - LSE)
- * and dP = dO V^T over all query tiles, and accumulate
- *   dV = P^T dO,   dK = scale * (P * (dP - delta))^T Q.
- * lse and delta are read only; dk and dv are written.
+ * Query-outer stage: for every query tile, compute delta from o and dout
+ * (written to `delta`, float32 [B,H,N]), recompute P = exp(scale*Q K^T - LSE)
+ * and dP = dO V^T over the key tiles, and accumulate
+ *   dQ = scale * (P * (dP - delta)) K.      dq is written.
+ */
+fa_status_t flash_attn_bwd_dq(const void* q, const void* k, const void* v, const void* o,
+                              const float* lse, const void* dout, float* delta, void* dq,
+                              int B, int H, int N, int d, float scale, int causal,
+                              int dtype, void* stream);
+
+/*
+ * Key-outer stage: for every key tile, recompute P and dP over all query tiles
+ * and accumulate dV = P^T dO and dK = scale * (P * (dP - delta))^T Q.
+ * lse and delta (as written by flash_attn_bwd_dq or flash_attn_bwd_delta) are
+ * read only; dk and dv are written.
  */
 fa_status_t flash_attn_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse,
                                 const void* dout, const float* delta, void* dk, void* dv,
                                 int B, int H, int N, int d, float scale, int causal,
                                 int dtype, void* stream);
-
-/*
- * Stage 3 (query-outer): for every query tile, recompute P and dP over the key
- * tiles and accumulate dQ = scale * (P * (dP - delta)) K. dq is written.
- */
-fa_status_t flash_attn_bwd_dq(const void* q, const void* k, const void* v, const float* lse,
-                              const void* dout, const float* delta, void* dq,
-                              int B, int H, int N, int d, float scale, int causal,
-                              int dtype, void* stream);
 
 /* Static, NUL-terminated description of a status code (never NULL). */
 const char* flash_attn_status_string(int status);

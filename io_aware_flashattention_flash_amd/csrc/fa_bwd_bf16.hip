@@ -9,8 +9,9 @@
 // (the chain rule through the row softmax; the pages give the recompute idea,
 // not the formulas).
 //
-// Three kernels, launched in order on one stream, no atomics (deterministic):
-//  1. delta kernel: one fp32 value per query row into the workspace.
+// Kernels (no atomics, deterministic). The full backward launches 3 then 2 on one stream; 1 is a
+// standalone stage computing only delta.
+//  1. delta kernel: one fp32 value per query row.
 //  2. dK/dV kernel (key-outer): a workgroup owns 32*NW keys, a wave owns 32 of
 //     them and keeps K^T / V^T operands and the dK^T / dV^T accumulators in
 //     registers while Q, dO, LSE and delta tiles stream through LDS. It uses
@@ -19,7 +20,8 @@
 //     B operands of dV^T += dO^T P and dK^T += Q^T dS, whose A operands
 //     (dO^T, Q^T) come from the LDS transpose read.
 //  3. dQ kernel (query-outer): the forward's layout (S^T = K Q^T, a lane holds
-//     one query); recomputes P and dP, forms dS^T and accumulates
+//     one query); computes its rows' delta from O and dO (and publishes it for
+//     kernel 2), recomputes P and dP, forms dS^T and accumulates
 //     dQ^T += K^T dS^T with K^T from the LDS transpose read.
 #include <type_traits>
 
@@ -51,22 +53,35 @@ struct BwdParams {
 // ---------------------------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdParams p) {
-  constexpr int TPR = D / 8;        // threads per row, one 16-byte chunk each
-  constexpr int RPB = 256 / TPR;    // rows per block
+  constexpr int TPR = D / 8;               // threads per row, one 16-byte chunk each
+  constexpr int RPI = 256 / TPR;           // rows per block per step
+  constexpr int STEPS = 4;                 // rows per thread (independent loads in flight)
   const int tid = threadIdx.x;
-  const size_t rows = (size_t)p.nh * p.N;
-  const size_t row = (size_t)blockIdx.x * RPB + tid / TPR;
+  const long rows = (long)p.nh * p.N;
+  const long row0 = (long)blockIdx.x * RPI * STEPS + tid / TPR;
   const int c = tid % TPR;
-  float acc = 0.f;
-  if (row < rows) {
-    const bf16x8 a = __builtin_bit_cast(bf16x8, ld_global16(p.o + row * D + 8 * c));
-    const bf16x8 b = __builtin_bit_cast(bf16x8, ld_global16(p.dout + row * D + 8 * c));
+  u32x4 a[STEPS], b[STEPS];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc += (float)a[e] * (float)b[e];
+  for (int i = 0; i < STEPS; ++i) {
+    const long row = row0 + (long)i * RPI;
+    a[i] = u32x4{0, 0, 0, 0};
+    b[i] = u32x4{0, 0, 0, 0};
+    if (row < rows) {
+      a[i] = ld_global16(p.o + row * D + 8 * c);
+      b[i] = ld_global16(p.dout + row * D + 8 * c);
+    }
   }
 #pragma unroll
-  for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-  if (row < rows && c == 0) p.delta[row] = acc;
+  for (int i = 0; i < STEPS; ++i) {
+    const bf16x8 av = __builtin_bit_cast(bf16x8, a[i]), bv = __builtin_bit_cast(bf16x8, b[i]);
+    float acc = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc += (float)av[e] * (float)bv[e];
+#pragma unroll
+    for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+    const long row = row0 + (long)i * RPI;
+    if (row < rows && c == 0) p.delta[row] = acc;
+  }
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -241,23 +256,11 @@ __global__ __launch_bounds__(NW * 64, (D > 64 ? 1 : 2)) void bwd_dkdv_kernel(Bwd
     for (; i < n_qt; i += 2) pair(std::false_type{}, i);
   }
 
-  const __amdgpu_buffer_rsrc_t rdk = make_rsrc(p.dk + base, head_bytes);
-  const __amdgpu_buffer_rsrc_t rdv = make_rsrc(p.dv + base, head_bytes);
-#pragma unroll
-  for (int db = 0; db < NDB; ++db) {
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      bf16x4 a, b;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        a[e] = (bf16)(dk[db][4 * g + e] * p.scale);
-        b[e] = (bf16)dv[db][4 * g + e];
-      }
-      const int off = key * (D * 2) + (32 * db + 8 * g + 4 * hf) * 2;
-      buf_store8(rdk, off, __builtin_bit_cast(u32x2, a));
-      buf_store8(rdv, off, __builtin_bit_cast(u32x2, b));
-    }
-  }
+  // dK = scale * dK^T^T and dV, written as whole rows through this wave's idle tile buffer.
+  __syncthreads();  // every wave is done reading the last Q / dO tile
+  char* stage = w == 0 ? sq0 : (w == 1 ? so0 : (w == 2 ? sq1 : so1));
+  store_rows_via_lds<D, TILE_BYTES>(stage, dk, p.scale, make_rsrc(p.dk + base, head_bytes), key_w0, l);
+  store_rows_via_lds<D, TILE_BYTES>(stage, dv, 1.0f, make_rsrc(p.dv + base, head_bytes), key_w0, l);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -290,19 +293,29 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdParams p) {
   const int q_w0 = qt * BR + 32 * w;
   const int q = q_w0 + lq;
 
+  // Q^T and dO^T operands: lane (q, hf) holds columns 16*kk + 8*hf .. +7 of its row. The same
+  // lanes load the matching half of O's row, so delta = rowsum(dO * O) for this row is a dot
+  // product over the lane's 8*NKK columns plus one exchange with the lane 32 apart; it is
+  // written to the delta buffer for the dK/dV kernel, which runs after this one.
   bf16x8 qreg[NKK], oreg[NKK];
   float lse2, dlt;
   {
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + base, head_bytes);
-    const __amdgpu_buffer_rsrc_t ro = make_rsrc(p.dout + base, head_bytes);
+    const __amdgpu_buffer_rsrc_t rdo = make_rsrc(p.dout + base, head_bytes);
+    const __amdgpu_buffer_rsrc_t rof = make_rsrc(p.o + base, head_bytes);
+    float part = 0.f;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
       const int off = q * (D * 2) + (16 * kk + 8 * hf) * 2;
       qreg[kk] = __builtin_bit_cast(bf16x8, buf_load16(rq, off));
-      oreg[kk] = __builtin_bit_cast(bf16x8, buf_load16(ro, off));
+      oreg[kk] = __builtin_bit_cast(bf16x8, buf_load16(rdo, off));
+      const bf16x8 ov = __builtin_bit_cast(bf16x8, buf_load16(rof, off));
+#pragma unroll
+      for (int e = 0; e < 8; ++e) part = fmaf((float)oreg[kk][e], (float)ov[e], part);
     }
+    dlt = half_swap_sum(part);
     lse2 = buf_load4f(make_rsrc(p.lse + rbase, N * 4), q * 4) * kLog2e;
-    dlt = buf_load4f(make_rsrc(p.delta + rbase, N * 4), q * 4);
+    if (hf == 0) buf_store4(make_rsrc(p.delta + rbase, N * 4), q * 4, dlt);
   }
 
   int n_kv = (N + BC - 1) / BC;
@@ -406,17 +419,9 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdParams p) {
 #pragma unroll 1
   for (; j < n_kv; j += 2) pair(std::true_type{}, j, n_kv);
 
-  const __amdgpu_buffer_rsrc_t rdq = make_rsrc(p.dq + base, head_bytes);
-#pragma unroll
-  for (int db = 0; db < NDB; ++db) {
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      bf16x4 t;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) t[e] = (bf16)(dq[db][4 * g + e] * p.scale);
-      buf_store8(rdq, q * (D * 2) + (32 * db + 8 * g + 4 * hf) * 2, __builtin_bit_cast(u32x2, t));
-    }
-  }
+  __syncthreads();  // every wave is done reading the last K / V tile
+  char* stage = w == 0 ? sk0 : (w == 1 ? sv0 : (w == 2 ? sk1 : sv1));
+  store_rows_via_lds<D, TILE_BYTES>(stage, dq, p.scale, make_rsrc(p.dq + base, head_bytes), q_w0, l);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -454,7 +459,7 @@ BwdParams make_params(const void* q, const void* k, const void* v, const void* o
 
 template <int D>
 hipError_t delta_d(BwdParams prm, hipStream_t stream) {
-  constexpr int RPB = 256 / (D / 8);
+  constexpr int RPB = 256 / (D / 8) * 4;  // rows per block (4 per thread group)
   const long rows = (long)prm.nh * prm.N;
   hipLaunchKernelGGL((bwd_delta_kernel<D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, stream, prm);
   return hipGetLastError();
@@ -495,10 +500,10 @@ hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const fl
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const float* lse, const void* dout,
-                         const float* delta, void* dq, int BH, int N, int d, float scale, bool causal,
+hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                         const void* dout, float* delta, void* dq, int BH, int N, int d, float scale, bool causal,
                          hipStream_t stream) {
-  BwdParams prm = make_params(q, k, v, nullptr, lse, dout, delta, dq, nullptr, nullptr, BH, N, scale);
+  BwdParams prm = make_params(q, k, v, o, lse, dout, delta, dq, nullptr, nullptr, BH, N, scale);
   if (d == 64) return causal ? dq_d<64, true>(prm, stream) : dq_d<64, false>(prm, stream);
   if (d == 128) return causal ? dq_d<128, true>(prm, stream) : dq_d<128, false>(prm, stream);
   return hipErrorInvalidValue;

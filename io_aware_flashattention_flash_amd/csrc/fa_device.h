@@ -135,6 +135,47 @@ __device__ __forceinline__ bf16x8 cat4(bf16x4 a, bf16x4 b) {
   return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
 
+// Write a wave's 32 x D block from the MFMA accumulator layout (lane l holds row l % 32, and
+// register r of block db holds column 32*db + 8*(r/4) + 4*(l/32) + r%4) to rows row0..row0+31 of a
+// row-major bf16 [rows, D] tensor, scaled by `mul`. The block is staged through `stage` (LDS
+// owned by this wave, STAGE_BYTES long; rows padded by 16 bytes against bank conflicts; two
+// passes of 16 rows when 32 rows do not fit) so global stores are whole rows of 16-byte chunks.
+// Rows beyond the descriptor's range are dropped.
+template <int D, int STAGE_BYTES>
+__device__ __forceinline__ void store_rows_via_lds(char* stage, const f32x16 (&acc)[D / 32], float mul,
+                                                   __amdgpu_buffer_rsrc_t r, int row0, int lane) {
+  constexpr int PITCH = D * 2 + 16, NCH = D / 8;
+  constexpr int ROWS = 32 * PITCH <= STAGE_BYTES ? 32 : 16;  // rows staged per pass
+  static_assert(ROWS * PITCH <= STAGE_BYTES, "staging area too small");
+  const int lq = lane & 31, hf = lane >> 5;
+#pragma unroll
+  for (int pass = 0; pass < 32 / ROWS; ++pass) {
+    if ((lq / ROWS) == pass) {
+      const int srow = lq % ROWS;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          bf16x4 t;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) t[e] = (bf16)(acc[db][4 * g + e] * mul);
+          *reinterpret_cast<bf16x4*>(stage + srow * PITCH + (32 * db + 8 * g + 4 * hf) * 2) = t;
+        }
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes have landed
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int i = 0; i < ROWS * NCH / 64; ++i) {
+      const int x = lane + 64 * i, row = x / NCH, ch = x % NCH;
+      buf_store16(r, (row0 + pass * ROWS + row) * (D * 2) + ch * 16,
+                  *reinterpret_cast<const u32x4*>(stage + row * PITCH + ch * 16));
+    }
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // the staging area may be reused once the reads are done
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
 // Sum of the two bf16 values of a packed pair, accumulated in fp32.
 __device__ __forceinline__ float dot2_ones(bf16x2 p, float acc) {
   const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};

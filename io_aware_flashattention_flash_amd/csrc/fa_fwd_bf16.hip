@@ -247,29 +247,9 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdBf16Params p) {
   // buffer descriptors and are dropped.
   const float l_tot = half_swap_sum(l_run);
   const float inv = 1.0f / half_swap_sum(lr_run);
-  constexpr int OPITCH = D * 2 + 16;
-  static_assert(32 * OPITCH <= TILE_BYTES, "a wave's output rows must fit in one tile buffer");
   __syncthreads();  // every wave is done reading the last K/V tile
   char* ostage = w == 0 ? sk0 : (w == 1 ? sv0 : (w == 2 ? sk1 : sv1));
-#pragma unroll
-  for (int db = 0; db < NDB; ++db) {
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      bf16x4 t;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) t[e] = (bf16)(acc_o[db][4 * g + e] * inv);
-      *reinterpret_cast<bf16x4*>(ostage + lq * OPITCH + (32 * db + 8 * g + 4 * hf) * 2) = t;
-    }
-  }
-  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
-  __builtin_amdgcn_wave_barrier();
-  const __amdgpu_buffer_rsrc_t ro = make_rsrc(p.o + base, head_bytes);
-#pragma unroll
-  for (int i = 0; i < 32 * NCH / 64; ++i) {
-    const int x = l + 64 * i, row = x / NCH, ch = x % NCH;
-    const u32x4 v = *reinterpret_cast<const u32x4*>(ostage + row * OPITCH + ch * 16);
-    buf_store16(ro, (q_w0 + row) * (D * 2) + ch * 16, v);
-  }
+  store_rows_via_lds<D, TILE_BYTES>(ostage, acc_o, inv, make_rsrc(p.o + base, head_bytes), q_w0, l);
   if (p.lse && hf == 0) {
     const __amdgpu_buffer_rsrc_t rl = make_rsrc(p.lse + (size_t)head * N, N * 4);
     buf_store4(rl, q * 4, (m_run + __log2f(l_tot)) * kLn2);

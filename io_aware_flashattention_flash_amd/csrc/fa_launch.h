@@ -19,9 +19,9 @@ hipError_t launch_bwd_delta(const void* o, const void* dout, float* delta, int B
 hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse,
                            const void* dout, const float* delta, void* dk, void* dv, int BH, int N,
                            int d, float scale, bool causal, hipStream_t stream);
-hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const float* lse,
-                         const void* dout, const float* delta, void* dq, int BH, int N, int d,
-                         float scale, bool causal, hipStream_t stream);
+hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void* o,
+                         const float* lse, const void* dout, float* delta, void* dq, int BH, int N,
+                         int d, float scale, bool causal, hipStream_t stream);
 
 // Work decomposition shared by the kernels: workgroup id -> (head, tile).
 // The hardware hands consecutive workgroup ids to the 8 XCDs round-robin, each with its own L2.

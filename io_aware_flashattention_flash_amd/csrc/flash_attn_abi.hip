@@ -84,16 +84,16 @@ fa_status_t flash_attn_bwd_dkdv(const void* q, const void* k, const void* v, con
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
-fa_status_t flash_attn_bwd_dq(const void* q, const void* k, const void* v, const float* lse, const void* dout,
-                              const float* delta, void* dq, int B, int H, int N, int d, float scale, int causal,
-                              int dtype, void* stream) {
-  if (!q || !k || !v || !lse || !dout || !delta || !dq) return FA_ERR_NULL_POINTER;
+fa_status_t flash_attn_bwd_dq(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                              const void* dout, float* delta, void* dq, int B, int H, int N, int d, float scale,
+                              int causal, int dtype, void* stream) {
+  if (!q || !k || !v || !o || !lse || !dout || !delta || !dq) return FA_ERR_NULL_POINTER;
   fa_status_t st = check_bwd_common(B, H, N, d, scale, dtype);
   if (st != FA_OK) return st;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dout) || !aligned16(dq) || !aligned4(lse) ||
-      !aligned4(delta))
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) || !aligned16(dq) ||
+      !aligned4(lse) || !aligned4(delta))
     return FA_ERR_MISALIGNED;
-  hipError_t e = fa::launch_bwd_dq(q, k, v, lse, dout, delta, dq, B * H, N, d, scale, causal != 0,
+  hipError_t e = fa::launch_bwd_dq(q, k, v, o, lse, dout, delta, dq, B * H, N, d, scale, causal != 0,
                                    static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
@@ -111,9 +111,8 @@ fa_status_t flash_attn_bwd(const void* q, const void* k, const void* v, const vo
   if (!aligned16(workspace)) return FA_ERR_MISALIGNED;
   hipStream_t s = static_cast<hipStream_t>(stream);
   float* delta = static_cast<float*>(workspace);
-  hipError_t e = fa::launch_bwd_delta(o, dout, delta, B * H, N, d, s);
+  hipError_t e = fa::launch_bwd_dq(q, k, v, o, lse, dout, delta, dq, B * H, N, d, scale, causal != 0, s);
   if (e == hipSuccess) e = fa::launch_bwd_dkdv(q, k, v, lse, dout, delta, dk, dv, B * H, N, d, scale, causal != 0, s);
-  if (e == hipSuccess) e = fa::launch_bwd_dq(q, k, v, lse, dout, delta, dq, B * H, N, d, scale, causal != 0, s);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

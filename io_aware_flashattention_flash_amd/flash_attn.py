@@ -33,7 +33,7 @@ SIGNATURES = {
     "flash_attn_bwd_delta": (_int, [_vp, _vp, _vp, _int, _int, _int, _int, _int, _vp]),
     "flash_attn_bwd_dkdv": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                    _int, _int, _int, _int, _float, _int, _int, _vp]),
-    "flash_attn_bwd_dq": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp,
+    "flash_attn_bwd_dq": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                  _int, _int, _int, _int, _float, _int, _int, _vp]),
     "flash_attn_status_string": (ctypes.c_char_p, [_int]),
 }
@@ -189,21 +189,22 @@ def flash_attn_bwd_dkdv(q, k, v, lse, dout, delta, scale=None, causal=False, dk=
     return dk, dv
 
 
-def flash_attn_bwd_dq(q, k, v, lse, dout, delta, scale=None, causal=False, dq=None):
-    """Backward stage 3 (query-outer recompute): dQ."""
+def flash_attn_bwd_dq(q, k, v, o, lse, dout, scale=None, causal=False, dq=None, delta=None):
+    """Backward query-outer stage: dQ, plus delta = rowsum(dout * o) for the dK/dV stage."""
     _check_tensor("q", q)
-    for name, t in (("k", k), ("v", v), ("dout", dout)):
+    for name, t in (("k", k), ("v", v), ("o", o), ("dout", dout)):
         _check_tensor(name, t, q)
     _check_rows("lse", lse, q)
-    _check_rows("delta", delta, q)
     B, H, N, d = q.shape
     scale = float(d) ** -0.5 if scale is None else float(scale)
     dq = torch.empty_like(q) if dq is None else dq
+    delta = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if delta is None else delta
     _check_tensor("dq", dq, q)
-    _check(load_library().flash_attn_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(lse), _ptr(dout), _ptr(delta),
+    _check_rows("delta", delta, q)
+    _check(load_library().flash_attn_bwd_dq(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(delta),
                                             _ptr(dq), B, H, N, d, scale, int(bool(causal)), _DTYPES[q.dtype],
                                             _stream_handle(q)))
-    return dq
+    return dq, delta
 
 
 class FlashAttnFunction(torch.autograd.Function):

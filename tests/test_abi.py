@@ -146,7 +146,7 @@ def test_signature_table_matches_header_parameter_counts():
 
 
 def _stage_args(**kw):
-    a = dict(q=A, k=A, v=A, lse=A, do=A, delta=A, dk=A, dv=A, dq=A, B=1, H=1, N=8, d=64, scale=0.125, causal=0,
+    a = dict(q=A, k=A, v=A, o=A, lse=A, do=A, delta=A, dk=A, dv=A, dq=A, B=1, H=1, N=8, d=64, scale=0.125, causal=0,
              dtype=1)
     a.update(kw)
     return a
@@ -160,8 +160,8 @@ def _dkdv(lib, **kw):
 
 def _dq(lib, **kw):
     a = _stage_args(**kw)
-    return lib.flash_attn_bwd_dq(a["q"], a["k"], a["v"], a["lse"], a["do"], a["delta"], a["dq"], a["B"], a["H"],
-                                 a["N"], a["d"], a["scale"], a["causal"], a["dtype"], None)
+    return lib.flash_attn_bwd_dq(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["delta"], a["dq"], a["B"],
+                                 a["H"], a["N"], a["d"], a["scale"], a["causal"], a["dtype"], None)
 
 
 def test_bwd_stage_validation(lib):
@@ -180,3 +180,5 @@ def test_bwd_stage_validation(lib):
         assert fn(lib, lse=A + 1) == ALIGN
     assert _dkdv(lib, dv=None) == NULLP
     assert _dq(lib, dq=A + 8) == ALIGN
+    assert _dq(lib, o=None) == NULLP
+    assert _dq(lib, o=A + 4) == ALIGN

@@ -308,3 +308,24 @@ def test_nonfinite_inputs_do_not_crash():
     oh = host(o)
     assert np.isnan(oh[0, 0, 5]).all()
     assert np.isfinite(np.delete(oh[0, 0], 5, axis=0)).all()
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_staged_backward_matches_fused(d, causal):
+    """flash_attn_bwd_dq then flash_attn_bwd_dkdv reproduce flash_attn_bwd bit for bit; the delta
+    they pass between them equals the standalone delta stage and rowsum(dO * O) in float64."""
+    from io_aware_flashattention_flash_amd import flash_attn_bwd_delta, flash_attn_bwd_dkdv, flash_attn_bwd_dq
+    w = inputs.Workload("t", "bf16", 2, 2, 333, d, causal, True)
+    x = inputs.make_inputs(w, seed=16 + d)
+    q, k, v, do = (dev(x[n], torch.bfloat16) for n in ("q", "k", "v", "do"))
+    o, lse = flash_attn_fwd(q, k, v, w.scale, causal)
+    dq, dk, dv = flash_attn_bwd(do, q, k, v, o, lse, w.scale, causal)
+    dq2, delta = flash_attn_bwd_dq(q, k, v, o, lse, do, w.scale, causal)
+    dk2, dv2 = flash_attn_bwd_dkdv(q, k, v, lse, do, delta, w.scale, causal)
+    torch.cuda.synchronize()
+    assert torch.equal(dq, dq2) and torch.equal(dk, dk2) and torch.equal(dv, dv2)
+    delta_only = flash_attn_bwd_delta(o, do)
+    ref = np.sum(host(o) * x["do"].astype(np.float64), axis=-1)
+    assert np.abs(host(delta) - ref).max() <= 1e-4 * max(1.0, np.abs(ref).max())
+    assert np.abs(host(delta_only) - ref).max() <= 1e-4 * max(1.0, np.abs(ref).max())

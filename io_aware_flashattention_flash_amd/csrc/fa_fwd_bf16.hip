@@ -5,9 +5,9 @@
 // workgroup owns a tile of BR query rows of one (batch, head). It keeps that Q
 // tile in registers and streams the K/V tiles of the same head through LDS.
 // Per K/V tile it forms the scores on the matrix cores, applies the scale and
-// the causal / ragged-tail mask, updates every row's running maximum m and
-// running sum l of exponentials (rescaling the earlier output accumulation
-// when m grows), and accumulates P V on the matrix cores. Only O and the
+// the causal / ragged-tail mask, keeps every row's running reference maximum m
+// and running sum l of exponentials (rescaling the earlier output accumulation
+// when m moves), and accumulates P V on the matrix cores. Only O and the
 // per-row log-sum-exp LSE = m + ln l leave the chip; the N x N score matrix
 // never exists in HBM.
 //
@@ -15,33 +15,53 @@
 //  * a wave owns 32 query rows and computes the transposed score block
 //    S^T = K Q^T with v_mfma_f32_32x32x16_bf16, so each lane holds the scores
 //    of ONE query (its column) for 16 of every 32 keys; the other 16 sit in
-//    the lane 32 apart. Row max is an in-register max plus one permlane32 swap;
-//    the row sum is kept per half and combined once at the end.
+//    the lane 32 apart.
 //  * the same accumulator registers, rounded to bf16, are the B operand of
 //    O^T += V^T P^T; V^T comes from the row-major V tile in LDS through the
 //    gfx950 LDS transpose read (ds_read_b64_tr_b16), with the key order chosen
 //    to match the accumulator's row order.
-//  * K/V tiles go from HBM straight into the swizzled LDS layout with
+//  * K/V tiles of 64 keys go from HBM straight into the swizzled LDS layout with
 //    buffer_load ... lds (no staging registers, no LDS write instructions); a
 //    per-tile buffer descriptor bounds the ragged last tile, whose missing rows
-//    arrive as zeros. Two LDS buffers alternate: tile j+1 is in flight while
-//    tile j is computed, with one barrier per tile.
-//  * softmax in the log2 domain: one FMA per score, p = exp2(s*c - m*c) with
-//    c = |scale| * log2(e) (a negative scale is applied by negating Q, which is
-//    exact in bf16). The running max is raised only when a tile's max exceeds
-//    it by more than 2^8, so the O / l rescale runs on a handful of tiles
-//    instead of every tile; p then stays below 2^8, far inside fp32/bf16 range,
-//    and O / l uses the same reference max in numerator and denominator, so the
-//    result is unchanged.
+//    arrive as zeros.
+//  * software pipeline over 32-key halves. A matrix instruction takes 32 cycles,
+//    and the VALU work of the softmax (about five issue slots per score) only
+//    hides behind it if the two are interleaved in the instruction stream. Each
+//    tile j is therefore split into halves and processed in two phases:
+//      A(j): S(j, keys 32-63) and O += P(j-1, keys 32-63) V on the matrix cores,
+//            probabilities of S(j, keys 0-31) on the VALU;
+//      B(j): S(j+1, keys 0-31) and O += P(j, keys 0-31) V on the matrix cores,
+//            probabilities of S(j, keys 32-63) on the VALU.
+//    Inside a phase every matrix instruction is followed by a slice of the
+//    element work (exponent argument, exp2, sums, bf16 packing) of different
+//    scores, each stage a step after the previous one, and LDS fragments are
+//    fetched four instructions ahead; scheduling barriers keep this order.
+//    One barrier per tile: K(j+2) and V(j+1) are issued right after the barrier
+//    that follows A(j), the last reader of the buffers they overwrite.
+//  * softmax in the log2 domain: p = exp2(s*c - m) with c = |scale| * log2(e)
+//    (a negative scale is applied by negating Q, which is exact in bf16). There
+//    is no per-tile row maximum: any reference m gives the same O = sum p V /
+//    sum p and LSE = m + log l, so m is only moved when it has to be. The
+//    per-lane sum of a half's 16 probabilities (needed anyway for l) bounds each
+//    of them; when it exceeds 2^16 (always on a row's first half, where m is
+//    still a placeholder, and later only if the scores climb by more than ~16
+//    log2 units) the half takes a slow path that raises m to the half's max,
+//    rescales O and the sums, and recomputes. Probabilities therefore stay
+//    below 2^16, far inside fp32/bf16 range, and the maximum reduction leaves
+//    the common path.
 //  * two row sums are kept: l over the fp32 probabilities (for LSE: summing the
-//    rounded values would put up to ~1.6e-3 of error into LSE on rows dominated
+//    rounded values would put up to ~2e-3 of error into LSE on rows dominated
 //    by a few keys), and l~ over the bf16-rounded probabilities that actually
 //    multiply V (v_dot2_f32_bf16, half an instruction per score). O is divided
-//    by l~, so the weights applied to V sum to one exactly; with a stale
-//    reference max the dominant probability is no longer exactly 1, and
+//    by l~, so the weights applied to V sum to one exactly; with a reference
+//    max that is not the row max the dominant probability is not exactly 1, and
 //    dividing by l would leave its rounding error (up to 2^-9 |V|) in O.
-//  * causal: tiles entirely above the diagonal are never loaded; only diagonal
-//    and ragged tiles evaluate the mask, with a branch-free compare per score.
+//  * causal: tiles entirely above the workgroup's last row are never loaded;
+//    only diagonal and ragged halves evaluate the mask, with a branch-free
+//    compare per score. The tile count is padded to even so the two-tile loop
+//    body needs no exit in its middle; the padded tile is fully masked.
+#include <type_traits>
+
 #include "fa_device.h"
 #include "fa_launch.h"
 
@@ -60,21 +80,22 @@ struct FwdBf16Params {
   uint32_t qsign;  // 0x80008000 to negate Q (negative scale), else 0
 };
 
-// Threshold (log2 units) by which a tile's max must exceed the running max before the
-// running max is raised and the accumulators rescaled.
-constexpr float kRescaleThreshold = 8.0f;
+// A block's per-lane probability sum above this bound means some probability may have left the
+// safe range (or the running max is still the initial placeholder): the block then takes the
+// slow path, which raises the running max to the block's max and recomputes.
+constexpr float kOverflowSum = 65536.0f;
+constexpr float kInitMax = -1e30f;
 
 template <int D, int BC, int NW, bool CAUSAL>
 __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdBf16Params p) {
+  static_assert(BC == 64, "two 32-key halves per tile");
   constexpr int BR = 32 * NW;
   constexpr int NCH = D / 8;
   constexpr int TILE_BYTES = BC * D * 2;
-  constexpr int NLD = BC * NCH / (64 * NW);  // LDS-DMA instructions per wave per tensor per tile
+  constexpr int NLD = BC * NCH / (64 * NW);
   static_assert(NLD * 64 * NW == BC * NCH, "tile must split evenly over the workgroup's waves");
-  constexpr int NKB = BC / 32;  // 32-key blocks per tile
-  constexpr int NDB = D / 32;   // 32-row blocks of O^T
-  constexpr int NKK = D / 16;   // k-steps of K Q^T
-  constexpr int NKS = BC / 16;  // k-steps of V^T P^T
+  constexpr int NDB = D / 32;
+  constexpr int NKK = D / 16;
   using T = SwizzledTile<D>;
 
   __shared__ __attribute__((aligned(16))) char sk0[TILE_BYTES];
@@ -93,9 +114,8 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdBf16Params p) {
   const bf16* Kh = p.k + base;
   const bf16* Vh = p.v + base;
   const int head_bytes = N * D * 2;
-
-  const int q_w0 = qt * BR + 32 * w;  // first query row of this wave
-  const int q = q_w0 + lq;            // this lane's query row
+  const int q_w0 = qt * BR + 32 * w;
+  const int q = q_w0 + lq;
 
   // Q^T operand: lane (q, hf) holds Q[q][16*kk + 8*hf .. +7]; rows >= N read as zero.
   bf16x8 qreg[NKK];
@@ -108,12 +128,12 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdBf16Params p) {
       qreg[kk] = __builtin_bit_cast(bf16x8, t);
     }
   }
-
   int n_kv = (N + BC - 1) / BC;
   if (CAUSAL) n_kv = min(n_kv, (min(N, (qt + 1) * BR) - 1) / BC + 1);
 
   // Byte offsets (within a tile) of the 16-byte chunks this lane deposits: DMA instruction i of
   // wave w fills LDS chunk positions (w + NW*i)*64 + lane, i.e. swizzled (row, chunk) slots.
+  // Tiles past the end of the head load zeros.
   int goff[NLD];
 #pragma unroll
   for (int i = 0; i < NLD; ++i) {
@@ -121,125 +141,206 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdBf16Params p) {
     const int row = pos / NCH, pc = pos % NCH;
     goff[i] = row * (D * 2) + ((pc ^ T::swz(row)) * 16);
   }
-  auto dma = [&](int j, char* kb, char* vb) __attribute__((always_inline)) {
+  auto dma = [&](const bf16* src, int j, char* dst) __attribute__((always_inline)) {
     const int key0 = j * BC;
-    const int bytes = min(BC, N - key0) * (D * 2);
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kh + (size_t)key0 * D, bytes);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vh + (size_t)key0 * D, bytes);
+    const int rows = __builtin_amdgcn_readfirstlane(max(0, min(BC, N - key0)));
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(src + (size_t)min(key0, N) * D, rows * (D * 2));
 #pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      buf_load16_to_lds(rk, kb + (w + NW * i) * 1024, goff[i]);
-      buf_load16_to_lds(rv, vb + (w + NW * i) * 1024, goff[i]);
-    }
+    for (int i = 0; i < NLD; ++i) buf_load16_to_lds(r, dst + (w + NW * i) * 1024, goff[i]);
   };
 
   // Lane-constant parts of the LDS read addresses.
   const int g16 = l >> 4, j16 = l & 15;
   const int v_row_lane = 4 * hf + (j16 >> 2);
   const int v_col_lane = 16 * (g16 & 1) + 4 * (j16 & 3);
-  // Largest key index this lane's query may see (causal and ragged tail).
   const int key_lim = CAUSAL ? min(q, N - 1) : N - 1;
 
   f32x16 acc_o[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) acc_o[db] = f32x16{};
-  float m_run = -INFINITY, l_run = 0.f, lr_run = 0.f;
+  float m_run = kInitMax, l_run = 0.f, lr_run = 0.f;
   const float c = p.c;
 
-  auto compute = [&](int j, const char* kbuf, const char* vbuf) __attribute__((always_inline)) {
-    const int key0 = j * BC;
-    // (A wave whose rows all precede this tile's keys still runs it: the mask zeroes every
-    // probability. Branching around it would cost more in register copies than the ~1.5% of
-    // matrix work it saves.)
-    // S^T = K Q^T for the NKB 32-key blocks of this tile.
-    f32x16 s[NKB];
+  // S^T for the 32-key half `h` of a K tile.
+  auto s_half = [&](f32x16& s, const char* kbuf, int h) __attribute__((always_inline)) {
+    s = f32x16{};
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      s[kb] = f32x16{};
-#pragma unroll
-      for (int kk = 0; kk < NKK; ++kk)
-        s[kb] = mfma_bf16_32x32x16(lds_read16(kbuf, T::chunk_off(32 * kb + lq, 2 * kk + hf)), qreg[kk], s[kb]);
-    }
-    // Mask (diagonal / ragged tiles only): key index relative to the tile vs this lane's limit.
-    if ((key0 + BC > N) || (CAUSAL && key0 + BC - 1 > q_w0)) {
+    for (int kk = 0; kk < NKK; ++kk)
+      s = mfma_bf16_32x32x16(lds_read16(kbuf, T::chunk_off(32 * h + lq, 2 * kk + hf)), qreg[kk], s);
+  };
+  // Causal / ragged mask of the 32-key half `h` of tile j (only where it can bite).
+  auto mask_half = [&](f32x16& s, int j, int h) __attribute__((always_inline)) {
+    const int key0 = j * BC + 32 * h;
+    if ((key0 + 32 > N) || (CAUSAL && key0 + 31 > q_w0)) {
       const int lim = key_lim - key0 - 4 * hf;
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int krel = 32 * kb + (r >> 2) * 8 + (r & 3);
-          s[kb][r] = krel <= lim ? s[kb][r] : -INFINITY;
-        }
+      for (int r = 0; r < 16; ++r) {
+        const int krel = (r >> 2) * 8 + (r & 3);
+        s[r] = krel <= lim ? s[r] : -INFINITY;
+      }
     }
-    // Row max of the raw scores (c > 0), across both halves of the 32-key blocks. The
-    // NaN-propagating maximum maps to v_maximum3_f32 and needs no quieting of the MFMA outputs.
-    float mx0 = -INFINITY, mx1 = -INFINITY;
+  };
+  f32x16 s0, s1;
+  bf16x8 p0[2], p1[2];
+  float rs, rr;
+  // One pipeline phase: NS = NKK MFMAs of S^T for K half `hs` (into s_out), NPV = 2 * NDB MFMAs of
+  // O^T += V^T P^T for V half `hv` (from p_in), and the probabilities of s_in (into p_out), with
+  // their fp32 sum in rs and the sum of their bf16 roundings in rr. The work is issued in a fixed
+  // interleave, fenced by scheduling barriers.
+  auto phase = [&](auto with_pv, f32x16& s_out, const char* kbuf, int hs, const bf16x8 (&p_in)[2],
+                   const char* vbuf, int hv, const f32x16& s_in, bf16x8 (&p_out)[2]) __attribute__((always_inline)) {
+    constexpr bool PV = decltype(with_pv)::value;
+    constexpr int NS = NKK, NPV = PV ? 2 * NDB : 0, NM = NS + NPV;
+    auto frag = [&](int i) __attribute__((always_inline)) -> bf16x8 {
+      if (i < NS) return lds_read16(kbuf, T::chunk_off(32 * hs + lq, 2 * i + hf));
+      const int t = (i - NS) / NDB, db = (i - NS) % NDB, ks = 2 * hv + t;
+      const int col = 32 * db + v_col_lane;
+      const bf16x4 a0 = lds_read_tr16(vbuf, T::elem_off(16 * ks + v_row_lane, col));
+      const bf16x4 a1 = lds_read_tr16(vbuf, T::elem_off(16 * ks + 8 + v_row_lane, col));
+      return cat4(a0, a1);
+    };
+    const float neg_m = -m_run;
+    float a0 = 0.f, a1 = 0.f, r0 = 0.f;
+    // Element k of the 16 probabilities goes through three stages, each in a later matrix step
+    // than the previous so no stage waits on the latency of the one before: x = s*c - m,
+    // p = exp2(x), then the sums and (odd k) the bf16 pair.
+    float xv[16], pv[16];
+    auto st_fma = [&](int k) __attribute__((always_inline)) {
+      xv[k] = fmaf(s_in[k], c, neg_m);
+      asm volatile("" ::"v"(xv[k]));
+    };
+    auto st_exp = [&](int k) __attribute__((always_inline)) {
+      pv[k] = fast_exp2(xv[k]);
+      asm volatile("" ::"v"(pv[k]));
+    };
+    auto st_acc = [&](int k) __attribute__((always_inline)) {
+      const int t = k >> 3, e = k & 7;
+      if ((k & 1) == 0) {
+        a0 += pv[k];
+        asm volatile("" ::"v"(a0));
+      } else {
+        a1 += pv[k];
+        const bf16x2 pr = {(bf16)pv[k - 1], (bf16)pv[k]};
+        r0 = dot2_ones(pr, r0);
+        p_out[t][e - 1] = pr[0];
+        p_out[t][e] = pr[1];
+        asm volatile("" ::"v"(a1), "v"(r0), "v"(pr));
+      }
+    };
+    constexpr int PF = 4;          // LDS fragment prefetch distance (matrix steps)
+    constexpr int NSTEP = NM + 2;  // two extra steps drain the element pipeline
+    bf16x8 fr[NM];
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
+    for (int i = 0; i < PF && i < NM; ++i) fr[i] = frag(i);
+#pragma unroll
+    for (int i = 0; i < NSTEP; ++i) {
+      if (i + PF < NM) fr[i + PF] = frag(i + PF);
+      if (i < NS) {
+        s_out = mfma_bf16_32x32x16(fr[i], qreg[i], i == 0 ? f32x16{} : s_out);
+      } else if (i < NM) {
+        const int t = (i - NS) / NDB, db = (i - NS) % NDB;
+        acc_o[db] = mfma_bf16_32x32x16(fr[i], p_in[t], acc_o[db]);
+      }
+      // element work per step: stage f of element k runs at step (k * NM / 16) + f
+      // (stages: 0 fma, 1 exp, 2 sums)
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const int s0_ = k * NM / 16;
+        if (s0_ + 2 == i) st_acc(k);
+        if (s0_ + 1 == i) st_exp(k);
+        if (s0_ == i) st_fma(k);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    rs = a0 + a1;
+    rr = r0;
+    // keep the fast-path results in this block (not sunk past the overflow check)
+    asm volatile("" : "+v"(p_out[0]), "+v"(p_out[1]), "+v"(rs), "+v"(rr));
+  };
+  // Slow-path recomputation of one half's probabilities against the current m.
+  auto probs = [&](const f32x16& s, bf16x8 (&pk)[2], float& rs_, float& rr_) __attribute__((always_inline)) {
+    const float neg_m = -m_run;
+    float a0 = 0.f, a1 = 0.f, r0 = 0.f;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int e = 0; e < 8; e += 2) {
+        const float pa = fast_exp2(fmaf(s[8 * t + e], c, neg_m));
+        const float pb = fast_exp2(fmaf(s[8 * t + e + 1], c, neg_m));
+        a0 += pa;
+        a1 += pb;
+        const bf16x2 pr = {(bf16)pa, (bf16)pb};
+        r0 = dot2_ones(pr, r0);
+        pk[t][e] = pr[0];
+        pk[t][e + 1] = pr[1];
+      }
+    rs_ = a0 + a1;
+    rr_ = r0;
+  };
+  // Accept a half's probabilities, or (some lane's sum above kOverflowSum) raise m to the half's
+  // max for the affected rows (both lanes of a row decide together), rescale O, l and l~, and
+  // recompute the half.
+  auto settle = [&](const f32x16& s, bf16x8 (&pk)[2]) __attribute__((always_inline)) {
+    if (__builtin_amdgcn_ballot_w64(rs > kOverflowSum)) {
+      const float trig = half_swap_max(rs > kOverflowSum ? 1.f : 0.f);
+      float mx0 = -INFINITY, mx1 = -INFINITY;
 #pragma unroll
       for (int r = 0; r < 16; r += 4) {
-        mx0 = vmax3(mx0, s[kb][r], s[kb][r + 1]);
-        mx1 = vmax3(mx1, s[kb][r + 2], s[kb][r + 3]);
+        mx0 = vmax3(mx0, s[r], s[r + 1]);
+        mx1 = vmax3(mx1, s[r + 2], s[r + 3]);
       }
-    const float mx = half_swap_max(vmax(mx0, mx1)) * c;
-    // Raise the running max only when this tile exceeds it by more than the threshold.
-    const bool raise = mx > m_run + kRescaleThreshold;
-    if (__builtin_amdgcn_ballot_w64(raise)) {
-      const float alpha = raise ? fast_exp2(m_run - mx) : 1.0f;
-      m_run = raise ? mx : m_run;
+      const float mx = half_swap_max(vmax(mx0, mx1)) * c;
+      const float m_new = trig > 0.5f ? vmax(m_run, mx) : m_run;
+      const float alpha = fast_exp2(m_run - m_new);
+      m_run = m_new;
       l_run *= alpha;
       lr_run *= alpha;
 #pragma unroll
       for (int db = 0; db < NDB; ++db) acc_o[db] *= alpha;
+      probs(s, pk, rs, rr);
     }
-    const float neg_m = (m_run == -INFINITY) ? 0.f : -m_run;
-    // P^T = exp2(s*c - m), summed in fp32, rounded to bf16 as the B operand of O^T += V^T P^T.
-    // k-step ks covers keys 16ks + {4hf..4hf+3, 8+4hf..8+4hf+3}, i.e. accumulator registers
-    // (ks&1)*8 + 0..7 of block ks>>1. Each k-step's products are issued as soon as its eight
-    // probabilities exist, so the matrix cores work on step ks while the VALU forms step ks+1.
-    float rs0 = 0.f, rs1 = 0.f, rr = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      bf16x8 pkk;
-#pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        const float pa = fast_exp2(fmaf(s[ks >> 1][(ks & 1) * 8 + e], c, neg_m));
-        const float pb = fast_exp2(fmaf(s[ks >> 1][(ks & 1) * 8 + e + 1], c, neg_m));
-        rs0 += pa;
-        rs1 += pb;
-        const bf16x2 pr = {(bf16)pa, (bf16)pb};
-        rr = dot2_ones(pr, rr);
-        pkk[e] = pr[0];
-        pkk[e + 1] = pr[1];
-      }
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const int col = 32 * db + v_col_lane;
-        const bf16x4 a0 = lds_read_tr16(vbuf, T::elem_off(16 * ks + v_row_lane, col));
-        const bf16x4 a1 = lds_read_tr16(vbuf, T::elem_off(16 * ks + 8 + v_row_lane, col));
-        acc_o[db] = mfma_bf16_32x32x16(cat4(a0, a1), pkk, acc_o[db]);
-      }
-    }
-    l_run += rs0 + rs1;
+    l_run += rs;
     lr_run += rr;
   };
-
-  // Ping-pong over the two LDS buffers: tile j+1 streams in while tile j is computed.
-  dma(0, sk0, sv0);
+  using yes = std::integral_constant<bool, true>;
+  using no = std::integral_constant<bool, false>;
+  auto phase_a = [&](int j, const char* kbuf, const char* vprev, auto with_pv) __attribute__((always_inline)) {
+    mask_half(s0, j, 0);
+    phase(with_pv, s1, kbuf, 1, p1, vprev, 1, s0, p0);
+    settle(s0, p0);
+  };
+  auto phase_b = [&](int j, const char* knext, const char* vcur) __attribute__((always_inline)) {
+    mask_half(s1, j, 1);
+    phase(yes{}, s0, knext, 0, p0, vcur, 0, s1, p1);
+    settle(s1, p1);
+  };
+  // K(j) and V(j) live in buffer j % 2. K(j+2) / V(j+1) are issued right after the barrier that
+  // follows phase A(j), the last reader of K(j) and V(j-1), and are awaited one tile later. The
+  // tile count is padded to even; a padded tile is fully masked (its probabilities are zero) and
+  // its V rows are real data or zeros, so it leaves O and l unchanged.
+  const int n_eff = (n_kv + 1) & ~1;
+  dma(Kh, 0, sk0);
+  dma(Vh, 0, sv0);
+  if (n_kv > 1) dma(Kh, 1, sk1);
   wait_vmem();
   __syncthreads();
-  int j = 0;
-  for (; j + 1 < n_kv; j += 2) {
-    dma(j + 1, sk1, sv1);
-    compute(j, sk0, sv0);
+  s_half(s0, sk0, 0);
+  phase_a(0, sk0, sv1, no{});
+#pragma unroll 1
+  for (int j = 0; j < n_eff; j += 2) {
     wait_vmem();
     __syncthreads();
-    if (j + 2 < n_kv) dma(j + 2, sk0, sv0);
-    compute(j + 1, sk1, sv1);
+    if (j + 2 < n_kv) dma(Kh, j + 2, sk0);
+    dma(Vh, j + 1, sv1);
+    phase_b(j, sk1, sv0);
+    phase_a(j + 1, sk1, sv0, yes{});
     wait_vmem();
     __syncthreads();
+    if (j + 3 < n_kv) dma(Kh, j + 3, sk1);
+    if (j + 2 < n_eff) dma(Vh, j + 2, sv0);
+    phase_b(j + 1, sk0, sv1);
+    phase_a(j + 2, sk0, sv1, yes{});
   }
-  if (j < n_kv) compute(j, sk0, sv0);
 
   // Epilogue: O = O_acc / l~, LSE = ln2 * (m + log2 l). The accumulator holds one query row per
   // lane, so O is staged through LDS (each wave in one of the now idle tile buffers, rows padded
@@ -247,7 +348,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdBf16Params p) {
   // buffer descriptors and are dropped.
   const float l_tot = half_swap_sum(l_run);
   const float inv = 1.0f / half_swap_sum(lr_run);
-  __syncthreads();  // every wave is done reading the last K/V tile
+  __syncthreads();  // every wave is done reading the last K/V tiles
   char* ostage = w == 0 ? sk0 : (w == 1 ? sv0 : (w == 2 ? sk1 : sv1));
   store_rows_via_lds<D, TILE_BYTES>(ostage, acc_o, inv, make_rsrc(p.o + base, head_bytes), q_w0, l);
   if (p.lse && hf == 0) {

@@ -215,6 +215,27 @@ def test_fwd_bf16_scales(scale, causal):
     assert np.abs(host(lse) - L).max() <= BF16_LSE * max(1.0, abs(scale))
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_fwd_bf16_rising_scores(d, causal):
+    """Scores that climb by well over 2^16 in probability ratio at keys 90, 170, 300 and 400
+    (first and second 32-key halves of different tiles): the running reference max must move
+    mid-row, rescaling the accumulated O and row sums, in both halves of the tile pipeline."""
+    w = inputs.Workload("t", "bf16", 1, 2, 520, d, causal, False)
+    x = inputs.make_inputs(w, seed=17)
+    factor = np.ones(520, dtype=np.float32)
+    for b, f in ((90, 6.0), (170, 11.0), (300, 16.0), (400, 21.0)):
+        factor[b:] = f
+    x["k"] = inputs.round_to_bf16(x["k"] * factor[None, None, :, None])
+    o, lse = gpu_fwd(x, w)
+    O, L = attn_fwd(x["q"], x["k"], x["v"], w.scale, causal)
+    err, beyond = float(np.abs(host(o) - O).max()), beyond_rounding(host(o), O)
+    lerr = float(np.abs(host(lse) - L).max())
+    print(f"d {d} causal {causal}: O err {err:.3e}, beyond output rounding {beyond:.3e}, LSE err {lerr:.3e}")
+    assert beyond <= BF16_O
+    assert lerr <= BF16_LSE
+
+
 def test_zero_scale_is_mean_of_visible_values():
     """scale = 0 makes every visible score equal: O_i = mean of V_0..V_i (causal), LSE_i = ln(i+1)."""
     w = inputs.Workload("t", "fp32", 1, 1, 257, 64, True, False)

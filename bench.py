@@ -17,7 +17,6 @@ Prints ONE JSON line. Besides the headline it carries:
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -30,11 +29,6 @@ PEAK_BF16_TFLOPS = 2516.6   # 256 CUs x 2.4 GHz x 4096 flop/clk/CU (dense)
 PEAK_FP32_TFLOPS = 157.3
 HEADLINE = "fwdbwd_bf16_b4h16n2048d64_causal"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCES = {
-    "fwd": "fa_fwd_bf16.hip",
-    "bwd_dkdv": "fa_bwd_bf16.hip",
-    "bwd_dq": "fa_bwd_bf16.hip",
-}
 
 
 def parse():
@@ -48,25 +42,21 @@ def parse():
     ap.add_argument("--workload", default=None,
                     help="time only this workload (any name in inputs.WORKLOADS) and print its own JSON line; "
                          "used to profile one kernel at a time")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run --steps plain device copies of 256 MiB (reference for the HBM byte counters)")
     return ap.parse_args()
-
-
-def source_digest(fname: str) -> str:
-    h = hashlib.sha256()
-    for f in (fname, "fa_device.h", "fa_launch.h"):
-        with open(os.path.join(ROOT, "io_aware_flashattention_flash_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
-    return h.hexdigest()[:16]
 
 
 def traffic_for(kernel: str):
     """HBM bytes per launch from the committed counter summary, if it matches the current source."""
+    from io_aware_flashattention_flash_amd.profiling import source_digest
+
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f).get(kernel)
     except (OSError, ValueError):
         return None
-    if not rec or rec.get("source_digest") != source_digest(KERNEL_SOURCES[kernel]):
+    if not rec or rec.get("source_digest") != source_digest(kernel):
         return None
     return rec.get("bytes_per_launch")
 
@@ -126,6 +116,16 @@ def main():
 
     def to_dev(a, dt):
         return torch.from_numpy(a).to(dev).to(dt)
+
+    if args.copy_calibration:
+        nbytes = 256 << 20
+        src = torch.ones(nbytes, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(max(1, args.steps)):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_per_launch": nbytes, "launches": max(1, args.steps)}))
+        return
 
     if args.workload is not None and args.workload != HEADLINE:
         print(json.dumps(time_forward(args.workload, args.steps, args.warmup, dev, to_dev)))

@@ -1,0 +1,135 @@
+"""Turn rocprofv3 output into the short text summaries kept under profiles/.
+
+  python -m io_aware_flashattention_flash_amd.profiling trace STATS_CSV OUT_MD "COMMAND" "TITLE"
+      kernel-trace summary (calls, average / min / max duration, share) of this library's kernels
+
+  python -m io_aware_flashattention_flash_amd.profiling traffic --fetch DIR --write DIR \
+      --copy-fetch DIR --copy-write DIR --copy-bytes N --out-json JSON --out-md MD --commands "..."
+      HBM traffic per launch of each attention kernel from FETCH_SIZE / WRITE_SIZE (KiB per
+      dispatch), each scaled by what the same counter reports for a plain device copy of N bytes
+      (bench.py --copy-calibration), stored with a digest of the kernel's source so that a stale
+      figure is never reported for a changed kernel.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+from collections import defaultdict
+
+CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
+KERNEL_SOURCES = {"fwd": "fa_fwd_bf16.hip", "bwd_dq": "fa_bwd_bf16.hip", "bwd_dkdv": "fa_bwd_bf16.hip"}
+KERNEL_PREFIX = {"fwd": "fa::fwd_bf16_kernel", "bwd_dq": "fa::bwd_dq_kernel", "bwd_dkdv": "fa::bwd_dkdv_kernel"}
+
+
+def source_digest(kernel: str) -> str:
+    """Digest of the source file that defines `kernel` plus the shared device headers."""
+    h = hashlib.sha256()
+    for f in (KERNEL_SOURCES[kernel], "fa_device.h", "fa_launch.h"):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def kernel_key(name: str):
+    short = name.replace("void ", "")
+    for key, prefix in KERNEL_PREFIX.items():
+        if short.startswith(prefix):
+            return key
+    return None
+
+
+def counter_per_dispatch(directory: str, counter: str, match) -> dict:
+    """Average of `counter` per dispatch for every kernel name accepted by `match` (name -> key)."""
+    path = glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True)
+    if not path:
+        raise FileNotFoundError(f"no counter_collection.csv under {directory}")
+    total, dispatches = defaultdict(float), defaultdict(set)
+    for row in csv.DictReader(open(path[0])):
+        if row["Counter_Name"] != counter:
+            continue
+        key = match(row["Kernel_Name"])
+        if key is None:
+            continue
+        total[key] += float(row["Counter_Value"])
+        dispatches[key].add(row["Dispatch_Id"])
+    return {k: total[k] / len(dispatches[k]) for k in total}
+
+
+def trace(stats_csv: str, out_md: str, command: str, title: str) -> str:
+    rows = list(csv.DictReader(open(stats_csv)))
+    lines = [f"# {title}", "", "Command (run from the repository root on one MI355X):", "", "```", command, "```", "",
+             "| kernel | calls | avg µs | min µs | max µs | share of GPU time |", "|---|---|---|---|---|---|"]
+    for r in rows:
+        if "fa::" not in r["Name"]:
+            continue
+        short = r["Name"].replace("void ", "").split("(")[0]
+        lines.append(f"| `{short}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
+                     f"{float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.2f}% |")
+    text = "\n".join(lines) + "\n"
+    with open(out_md, "w") as f:
+        f.write(text)
+    return text
+
+
+def traffic(a) -> dict:
+    # the runtime's device-to-device blit kernel that a same-device torch copy launches
+    copy = lambda n: "copy" if "copybuffer" in n.lower() else None
+    cf = counter_per_dispatch(a.copy_fetch, "FETCH_SIZE", copy).get("copy")
+    cw = counter_per_dispatch(a.copy_write, "WRITE_SIZE", copy).get("copy")
+    if not cf or not cw:
+        raise RuntimeError("copy calibration kernel not found in the counter output")
+    # a copy of N bytes fetches N and writes N: KiB reported per byte moved
+    f_scale, w_scale = cf * 1024.0 / a.copy_bytes, cw * 1024.0 / a.copy_bytes
+    fetch = counter_per_dispatch(a.fetch, "FETCH_SIZE", kernel_key)
+    write = counter_per_dispatch(a.write, "WRITE_SIZE", kernel_key)
+    out = {"_calibration": {"copy_bytes": a.copy_bytes, "fetch_kib_per_dispatch": cf, "write_kib_per_dispatch": cw,
+                            "fetch_scale": f_scale, "write_scale": w_scale}}
+    for k in sorted(set(fetch) & set(write)):
+        fb, wb = fetch[k] * 1024.0 / f_scale, write[k] * 1024.0 / w_scale
+        out[k] = {"source_digest": source_digest(k), "fetch_bytes_per_launch": round(fb),
+                  "write_bytes_per_launch": round(wb), "bytes_per_launch": round(fb + wb)}
+    with open(a.out_json, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    lines = ["# HBM traffic per launch (rocprofv3 FETCH_SIZE / WRITE_SIZE, copy-calibrated)", "",
+             "Commands (run from the repository root on one MI355X; one counter per pass):", "", "```",
+             a.commands, "```", "",
+             f"Calibration: a device copy of {a.copy_bytes} bytes reads FETCH_SIZE {cf:.0f} KiB and WRITE_SIZE "
+             f"{cw:.0f} KiB per dispatch, i.e. {f_scale:.4f} / {w_scale:.4f} of the bytes moved; kernel figures "
+             "below are divided by these factors.", "",
+             "| kernel | fetch MB / launch | write MB / launch | total MB / launch |", "|---|---|---|---|"]
+    for k, v in out.items():
+        if k.startswith("_"):
+            continue
+        lines.append(f"| {k} | {v['fetch_bytes_per_launch'] / 1e6:.2f} | {v['write_bytes_per_launch'] / 1e6:.2f} | "
+                     f"{v['bytes_per_launch'] / 1e6:.2f} |")
+    with open(a.out_md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    t = sub.add_parser("trace")
+    t.add_argument("stats_csv")
+    t.add_argument("out_md")
+    t.add_argument("command")
+    t.add_argument("title")
+    r = sub.add_parser("traffic")
+    for name in ("--fetch", "--write", "--copy-fetch", "--copy-write", "--out-json", "--out-md", "--commands"):
+        r.add_argument(name, required=True)
+    r.add_argument("--copy-bytes", type=int, required=True)
+    a = ap.parse_args()
+    if a.cmd == "trace":
+        print(trace(a.stats_csv, a.out_md, a.command, a.title))
+    else:
+        print(json.dumps(traffic(a), indent=1))
+
+
+if __name__ == "__main__":
+    main()

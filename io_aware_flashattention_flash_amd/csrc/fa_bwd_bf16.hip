@@ -44,6 +44,7 @@ struct BwdParams {
   int N;
   int nh;
   int n_tiles;
+  int n_units;  // workgroups per head (dQ: n_tiles, or (n_tiles + 1) / 2 when causal tiles are paired)
   float c;      // scale * log2(e)
   float scale;
 };
@@ -285,8 +286,19 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdParams p) {
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l = tid & 63, lq = l & 31, hf = l >> 5;
   const int N = p.N;
-  int head, qt;
-  map_workgroup(blockIdx.x, p.n_tiles, p.nh, CAUSAL ? Order::kLongestFirst : Order::kHeadMajor, true, head, qt);
+  // Large causal launches pair query tiles: workgroup (head, u) takes tiles n_tiles-1-u and u one
+  // after the other, so every workgroup does the same work and the launch has no tail of short
+  // workgroups. (With few workgroups per CU the pairing would only serialise work, so it is off;
+  // then tiles are dispatched longest-first.)
+  const bool paired = CAUSAL && p.n_units != p.n_tiles;
+  int head, unit;
+  map_workgroup(blockIdx.x, p.n_units, p.nh, paired ? Order::kHeadMajor : (CAUSAL ? Order::kLongestFirst : Order::kHeadMajor),
+                !paired, head, unit);
+  const int n_items = (paired && p.n_tiles - 1 - unit != unit) ? 2 : 1;
+#pragma unroll 1
+  for (int item = 0; item < n_items; ++item) {
+  const int qt = (paired && item == 0) ? p.n_tiles - 1 - unit : unit;
+  if (item > 0) __syncthreads();  // the previous item's staging reads are done before tiles land
   const size_t base = (size_t)head * N * D;
   const size_t rbase = (size_t)head * N;
   const int head_bytes = N * D * 2;
@@ -422,6 +434,7 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdParams p) {
   __syncthreads();  // every wave is done reading the last K / V tile
   char* stage = w == 0 ? sk0 : (w == 1 ? sv0 : (w == 2 ? sk1 : sv1));
   store_rows_via_lds<D, TILE_BYTES>(stage, dq, p.scale, make_rsrc(p.dq + base, head_bytes), q_w0, l);
+  }  // item
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -452,9 +465,23 @@ BwdParams make_params(const void* q, const void* k, const void* v, const void* o
   prm.N = N;
   prm.nh = BH;
   prm.n_tiles = 0;
+  prm.n_units = 0;
   prm.c = scale * kLog2e;
   prm.scale = scale;
   return prm;
+}
+
+// Compute units of the current device (cached per device; a benign race writes the same value).
+static int num_cus() {
+  static int cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
 }
 
 template <int D>
@@ -476,7 +503,9 @@ hipError_t dkdv_d(BwdParams prm, hipStream_t stream) {
 template <int D, bool CAUSAL>
 hipError_t dq_d(BwdParams prm, hipStream_t stream) {
   prm.n_tiles = (prm.N + 32 * kDqNW - 1) / (32 * kDqNW);
-  hipLaunchKernelGGL((bwd_dq_kernel<D, dq_bc<D>(), kDqNW, CAUSAL>), dim3(prm.n_tiles * prm.nh), dim3(kDqNW * 64), 0,
+  // Pair causal tiles when there are at least four workgroups per CU to begin with.
+  prm.n_units = (CAUSAL && (long)prm.n_tiles * prm.nh >= 4L * num_cus()) ? (prm.n_tiles + 1) / 2 : prm.n_tiles;
+  hipLaunchKernelGGL((bwd_dq_kernel<D, dq_bc<D>(), kDqNW, CAUSAL>), dim3(prm.n_units * prm.nh), dim3(kDqNW * 64), 0,
                      stream, prm);
   return hipGetLastError();
 }

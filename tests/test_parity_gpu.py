@@ -157,7 +157,7 @@ def test_fwdbwd_bf16_b4h16n2048d64_causal_full_compare():
 # ---------------------------------------------------------------------------------------------
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("N", [1, 17, 100, 129, 200, 1000, 1031])
+@pytest.mark.parametrize("N", [1, 17, 32, 33, 64, 65, 100, 127, 129, 200, 256, 1000, 1031])
 def test_fwd_bf16_ragged(N, causal, d):
     w = inputs.Workload("t", "bf16", 2, 2, N, d, causal, False)
     x = inputs.make_inputs(w, seed=N + d)
@@ -193,6 +193,24 @@ def test_bwd_bf16_ragged(N, causal, d):
     dQ, dK, dV, _ = attn_bwd(x["q"], x["k"], x["v"], x["do"], w.scale, causal)
     for name, g, r in (("dQ", dq, dQ), ("dK", dk, dK), ("dV", dv, dV)):
         e_inf, e_fro = grad_errors(host(g), r)
+        assert e_inf <= GRAD and e_fro <= GRAD, (name, e_inf, e_fro)
+
+
+def test_bwd_bf16_paired_query_tiles_odd_count():
+    """A causal backward large enough (9 query tiles of 128 x 128 heads >= 4 workgroups per CU) for
+    the dQ kernel to pair tiles u and n-1-u in one workgroup, with an odd tile count so the middle
+    tile runs alone; checked against the oracle on a sample of heads."""
+    w = inputs.Workload("t", "bf16", 1, 128, 1100, 64, True, True)
+    x = inputs.make_inputs(w, seed=18)
+    q, k, v, do = (dev(x[n], torch.bfloat16) for n in ("q", "k", "v", "do"))
+    o, lse = flash_attn_fwd(q, k, v, w.scale, True)
+    dq, dk, dv = flash_attn_bwd(do, q, k, v, o, lse, w.scale, True)
+    torch.cuda.synchronize()
+    heads = [0, 1, 7, 64, 127]
+    sl = (slice(None), heads)
+    dQ, dK, dV, _ = attn_bwd(x["q"][sl], x["k"][sl], x["v"][sl], x["do"][sl], w.scale, True)
+    for name, g, r in (("dQ", dq, dQ), ("dK", dk, dK), ("dV", dv, dV)):
+        e_inf, e_fro = grad_errors(host(g)[sl], r)
         assert e_inf <= GRAD and e_fro <= GRAD, (name, e_inf, e_fro)
 
 

@@ -13,6 +13,7 @@ Prints ONE JSON line. Besides the headline it carries:
                 committed rocprofv3 counter summary, or null if that kernel's source changed since
   cpu_baseline  the float64 CPU oracle timed on the host cores over a bounded sample of heads
   workloads     forward-only TFLOPS of the other bf16 workloads and the fp32 workload's latency
+  extras_fp16   the same kernels on fp16 storage: the long causal forward and the fwd+bwd step
 """
 from __future__ import annotations
 
@@ -61,15 +62,27 @@ def traffic_for(kernel: str):
     return rec.get("bytes_per_launch")
 
 
-def time_forward(name, reps, warmup, dev, to_dev):
+TORCH_DTYPE = {"bf16": "bfloat16", "fp16": "float16", "fp32": "float32"}
+# Extra lines (not workloads of the metric): the fp16 storage path on the same shapes.
+EXTRAS = ("fwd_fp16_b2h32n4096d128_causal", "fwdbwd_fp16_b4h16n2048d64_causal")
+
+
+def extra_workload(name):
+    from io_aware_flashattention_flash_amd import inputs
+
+    base = inputs.WORKLOADS[name.replace("fp16", "bf16")]
+    return inputs.Workload(name, "fp16", base.B, base.H, base.N, base.d, base.causal, base.backward, base.q_mult)
+
+
+def time_forward(name, reps, warmup, dev, to_dev, wl=None):
     """Forward-only timing of one workload (HIP events around `reps` back-to-back launches)."""
     import torch
 
     from io_aware_flashattention_flash_amd import flash_attn_fwd, inputs
 
-    wl = inputs.WORKLOADS[name]
+    wl = inputs.WORKLOADS[name] if wl is None else wl
     xi = inputs.make_inputs(wl)
-    dt = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    dt = getattr(torch, TORCH_DTYPE[wl.dtype])
     qi, ki, vi = (to_dev(xi[n], dt) for n in ("q", "k", "v"))
     oi = torch.empty_like(qi)
     li = torch.empty(wl.B, wl.H, wl.N, device=dev)
@@ -91,10 +104,57 @@ def time_forward(name, reps, warmup, dev, to_dev):
     torch.cuda.synchronize()
     us = a.elapsed_time(b) / reps * 1e3
     tf = wl.fwd_flops() / (us * 1e-6) / 1e12
-    peak = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_FP32_TFLOPS
-    nbytes = wl.B * wl.H * (4 * wl.N * wl.d * (2 if dt == torch.bfloat16 else 4) + 4 * wl.N)
+    peak = PEAK_FP32_TFLOPS if wl.dtype == "fp32" else PEAK_BF16_TFLOPS  # fp16 dense MFMA peak = bf16's
+    nbytes = wl.B * wl.H * (4 * wl.N * wl.d * (4 if wl.dtype == "fp32" else 2) + 4 * wl.N)
     return {"workload": name, "pass": "fwd", "reps": reps, "us": round(us, 2), "tflops": round(tf, 1),
             "pct_of_peak": round(100 * tf / peak, 2), "gbps_algorithmic": round(nbytes / (us * 1e-6) / 1e9, 1)}
+
+
+def time_fwdbwd(w, x, steps, warmup, dev, to_dev):
+    """One step = forward, dQ (with delta), dK/dV on resident inputs of a 16-bit workload. Returns
+    (ms per step over `steps` timed steps, {stage: average ms}) from HIP events on the stream."""
+    import torch
+
+    from io_aware_flashattention_flash_amd import flash_attn_bwd_dkdv, flash_attn_bwd_dq, flash_attn_fwd
+
+    dt = getattr(torch, TORCH_DTYPE[w.dtype])
+    q, k, v, do = (to_dev(x[n], dt) for n in ("q", "k", "v", "do"))
+    o = torch.empty_like(q)
+    lse = torch.empty(w.B, w.H, w.N, device=dev)
+    delta = torch.empty_like(lse)
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+
+    def step(evs=None):
+        if evs is not None:
+            evs[0].record()
+        flash_attn_fwd(q, k, v, w.scale, w.causal, out=o, lse=lse)
+        if evs is not None:
+            evs[1].record()
+        flash_attn_bwd_dq(q, k, v, o, lse, do, w.scale, w.causal, dq=dq, delta=delta)
+        if evs is not None:
+            evs[2].record()
+        flash_attn_bwd_dkdv(q, k, v, lse, do, delta, w.scale, w.causal, dk=dk, dv=dv)
+        if evs is not None:
+            evs[3].record()
+
+    names = ["fwd", "bwd_dq", "bwd_dkdv"]
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0.record()
+    for i in range(steps):
+        step(ev[i])
+    t1.record()
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / steps
+    kern_ms = {n: sum(e[j].elapsed_time(e[j + 1]) for e in ev) / steps for j, n in enumerate(names)}
+    if not (torch.isfinite(o.float()).all() and torch.isfinite(dq.float()).all()):
+        raise RuntimeError("non-finite output in the benchmark step")
+    return ms_step, kern_ms
 
 
 def main():
@@ -103,11 +163,9 @@ def main():
         print(json.dumps({"error": "this library runs on one GPU; --gpus must be 1 (no multi-GPU path exists)"}))
         sys.exit(2)
 
-    import numpy as np
     import torch
 
-    from io_aware_flashattention_flash_amd import (flash_attn_bwd_dkdv, flash_attn_bwd_dq, flash_attn_fwd, inputs,
-                                                   load_library)
+    from io_aware_flashattention_flash_amd import inputs, load_library
 
     load_library()  # raises if the HIP library is not built
     dev = torch.device("cuda:0")
@@ -134,43 +192,8 @@ def main():
     # ------------------------------------------------------------------ headline: fwd + bwd
     w = inputs.WORKLOADS[HEADLINE]
     x = inputs.make_inputs(w)
-    q, k, v, do = (to_dev(x[n], torch.bfloat16) for n in ("q", "k", "v", "do"))
-    o = torch.empty_like(q)
-    lse = torch.empty(w.B, w.H, w.N, device=dev)
-    delta = torch.empty_like(lse)
-    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
-
-    def step(evs=None):
-        if evs is not None:
-            evs[0].record()
-        flash_attn_fwd(q, k, v, w.scale, True, out=o, lse=lse)
-        if evs is not None:
-            evs[1].record()
-        flash_attn_bwd_dq(q, k, v, o, lse, do, w.scale, True, dq=dq, delta=delta)
-        if evs is not None:
-            evs[2].record()
-        flash_attn_bwd_dkdv(q, k, v, lse, do, delta, w.scale, True, dk=dk, dv=dv)
-        if evs is not None:
-            evs[3].record()
-
+    ms_step, kern_ms = time_fwdbwd(w, x, args.steps, args.warmup, dev, to_dev)
     names = ["fwd", "bwd_dq", "bwd_dkdv"]
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(args.steps)]
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0.record()
-    for i in range(args.steps):
-        step(ev[i])
-    t1.record()
-    torch.cuda.synchronize()
-    total_ms = t0.elapsed_time(t1)
-    ms_step = total_ms / args.steps
-    kern_ms = {n: sum(e[j].elapsed_time(e[j + 1]) for e in ev) / args.steps for j, n in enumerate(names)}
-    if not (torch.isfinite(o.float()).all() and torch.isfinite(dq.float()).all()):
-        raise RuntimeError("non-finite output in the benchmark step")
 
     f_fwd, f_bwd = w.fwd_flops(), w.bwd_flops()
     value = (f_fwd + f_bwd) / (ms_step * 1e-3) / 1e12
@@ -201,6 +224,20 @@ def main():
         for name, wl in inputs.WORKLOADS.items():
             if not wl.backward:
                 workloads[name] = time_forward(name, None, 10, dev, to_dev)
+        torch.cuda.empty_cache()
+
+    # ------------------------------------------------------------------ extra lines: fp16 storage
+    extras = {}
+    if not args.no_workloads:
+        for name in EXTRAS:
+            wl = extra_workload(name)
+            if wl.backward:
+                ms, km = time_fwdbwd(wl, inputs.make_inputs(wl), max(20, args.steps // 2), 10, dev, to_dev)
+                extras[name] = {"workload": name, "pass": "fwd+bwd", "us": round(ms * 1e3, 2),
+                                "tflops": round((wl.fwd_flops() + wl.bwd_flops()) / (ms * 1e-3) / 1e12, 1),
+                                "kernels_us": {n: round(t * 1e3, 2) for n, t in km.items()}}
+            else:
+                extras[name] = time_forward(name, None, 10, dev, to_dev, wl=wl)
         torch.cuda.empty_cache()
 
     # ------------------------------------------------------------------ CPU oracle baseline
@@ -250,6 +287,7 @@ def main():
         "cpu_baseline": cpu,
         "kernels": kernels,
         "workloads": workloads,
+        "extras_fp16": extras,
         "device": {"name": props.name, "arch": getattr(props, "gcnArchName", ""), "cus": props.multi_processor_count},
     }
     print(json.dumps(out))

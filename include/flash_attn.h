@@ -37,6 +37,7 @@
  *   Errors     The library never aborts and never prints. Launch failures are
  *              reported as FA_ERR_HIP.
  *   Support    bf16: d in {64, 128}, forward and backward.
+ *              fp16 (IEEE binary16): d in {64, 128}, forward and backward.
  *              fp32: d in {64, 128}, forward only.
  *              B, H, N >= 1, B*H*N*d < 2^31 elements per tensor and
  *              N*d < 2^29 (one head is addressed with 32-bit byte offsets).
@@ -61,16 +62,19 @@ typedef enum {
   FA_ERR_HIP = 7           /* the HIP runtime reported an error at launch */
 } fa_status_t;
 
-typedef enum { FA_DTYPE_FP32 = 0, FA_DTYPE_BF16 = 1 } fa_dtype_t;
+typedef enum { FA_DTYPE_FP32 = 0, FA_DTYPE_BF16 = 1, FA_DTYPE_FP16 = 2 } fa_dtype_t;
 
 /*
  * Forward: O = softmax(scale * Q K^T [+ causal mask]) V and LSE.
  *   q, k, v  [B,H,N,d] of `dtype`, read only.
- *   o        [B,H,N,d] of `dtype`, written (rounded to nearest even for bf16).
+ *   o        [B,H,N,d] of `dtype`, written (rounded to nearest even for bf16 and fp16).
  *   lse      [B,H,N] float32, written; may be NULL when not wanted.
  * Arithmetic: products on the matrix cores with float32 accumulation,
- * softmax in float32. Deterministic: the same inputs give bitwise-identical
- * outputs.
+ * softmax in float32; for the 16-bit types the probabilities that multiply V
+ * are rounded to that type. fp16 shares bf16's algorithm; its narrower range
+ * means scores whose dot products, or gradients, exceed 65504 in magnitude
+ * overflow where bf16 would not. Deterministic: the same inputs give
+ * bitwise-identical outputs.
  */
 fa_status_t flash_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                            int B, int H, int N, int d, float scale, int causal,
@@ -96,7 +100,7 @@ size_t flash_attn_bwd_workspace_size(int B, int H, int N, int d, int dtype);
  *                      flash_attn_bwd_workspace_size(); its contents on entry
  *                      are ignored; on return it holds delta (float32 [B,H,N]).
  * Runs flash_attn_bwd_dq and then flash_attn_bwd_dkdv (below) on `stream`.
- * Deterministic (no atomics). bf16 only.
+ * Deterministic (no atomics). bf16 and fp16 only.
  */
 fa_status_t flash_attn_bwd(const void* q, const void* k, const void* v, const void* o,
                            const float* lse, const void* dout,
@@ -107,7 +111,7 @@ fa_status_t flash_attn_bwd(const void* q, const void* k, const void* v, const vo
 
 /*
  * Backward stages, exposed so a caller can run (or time) them separately. Same
- * conventions and validation as flash_attn_bwd; bf16 only; deterministic.
+ * conventions and validation as flash_attn_bwd; bf16 and fp16; deterministic.
  * flash_attn_bwd runs flash_attn_bwd_dq and then flash_attn_bwd_dkdv.
  *
  * flash_attn_bwd_delta: delta[b,h,i] = sum_c dout[b,h,i,c] * o[b,h,i,c]

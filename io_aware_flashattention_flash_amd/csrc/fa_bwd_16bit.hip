@@ -1,4 +1,4 @@
-// Recompute-based attention backward for gfx950 (bf16 storage, fp32 math).
+// Recompute-based attention backward for gfx950 (16-bit storage: bf16 or fp16; fp32 math).
 //
 // The forward saves only O and the per-row LSE; the backward recomputes the
 // probabilities tile by tile from them instead of reading a stored N x N
@@ -16,7 +16,7 @@
 //     them and keeps K^T / V^T operands and the dK^T / dV^T accumulators in
 //     registers while Q, dO, LSE and delta tiles stream through LDS. It uses
 //     the untransposed score block S = Q K^T, so a lane holds one key and the
-//     registers run over queries: P and dS, rounded to bf16, are directly the
+//     registers run over queries: P and dS, rounded to the 16-bit type, are directly the
 //     B operands of dV^T += dO^T P and dK^T += Q^T dS, whose A operands
 //     (dO^T, Q^T) come from the LDS transpose read.
 //  3. dQ kernel (query-outer): the forward's layout (S^T = K Q^T, a lane holds
@@ -30,17 +30,18 @@
 
 namespace fa {
 
+template <typename E>
 struct BwdParams {
-  const bf16* q;
-  const bf16* k;
-  const bf16* v;
-  const bf16* o;
-  const bf16* dout;
+  const E* q;
+  const E* k;
+  const E* v;
+  const E* o;
+  const E* dout;
   const float* lse;
   float* delta;
-  bf16* dq;
-  bf16* dk;
-  bf16* dv;
+  E* dq;
+  E* dk;
+  E* dv;
   int N;
   int nh;
   int n_tiles;
@@ -52,8 +53,9 @@ struct BwdParams {
 // ---------------------------------------------------------------------------------------------
 // 1. delta = rowsum(dO * O)
 // ---------------------------------------------------------------------------------------------
-template <int D>
-__global__ __launch_bounds__(256) void bwd_delta_kernel(BwdParams p) {
+template <typename E, int D>
+__global__ __launch_bounds__(256) void bwd_delta_kernel(BwdParams<E> p) {
+  using e16x8 = typename Half16<E>::x8;
   constexpr int TPR = D / 8;               // threads per row, one 16-byte chunk each
   constexpr int RPI = 256 / TPR;           // rows per block per step
   constexpr int STEPS = 4;                 // rows per thread (independent loads in flight)
@@ -74,7 +76,7 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdParams p) {
   }
 #pragma unroll
   for (int i = 0; i < STEPS; ++i) {
-    const bf16x8 av = __builtin_bit_cast(bf16x8, a[i]), bv = __builtin_bit_cast(bf16x8, b[i]);
+    const e16x8 av = __builtin_bit_cast(e16x8, a[i]), bv = __builtin_bit_cast(e16x8, b[i]);
     float acc = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc += (float)av[e] * (float)bv[e];
@@ -88,8 +90,10 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdParams p) {
 // ---------------------------------------------------------------------------------------------
 // 2. dK, dV (key-outer)
 // ---------------------------------------------------------------------------------------------
-template <int D, int NW, int BQ, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64, (D > 64 ? 1 : 2)) void bwd_dkdv_kernel(BwdParams p) {
+template <typename E, int D, int NW, int BQ, bool CAUSAL>
+__global__ __launch_bounds__(NW * 64, (D > 64 ? 1 : 2)) void bwd_dkdv_kernel(BwdParams<E> p) {
+  using H = Half16<E>;
+  using e16x8 = typename H::x8;
   constexpr int BKV = 32 * NW;
   constexpr int NCH = D / 8;
   constexpr int TILE_BYTES = BQ * D * 2;
@@ -120,15 +124,15 @@ __global__ __launch_bounds__(NW * 64, (D > 64 ? 1 : 2)) void bwd_dkdv_kernel(Bwd
   const int key = key_w0 + lq;
 
   // K^T and V^T operands (B side of S = Q K^T and dP = dO V^T): lane (key, hf); keys >= N read 0.
-  bf16x8 kreg[NKK], vreg[NKK];
+  e16x8 kreg[NKK], vreg[NKK];
   {
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k + base, head_bytes);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + base, head_bytes);
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
       const int off = key * (D * 2) + (16 * kk + 8 * hf) * 2;
-      kreg[kk] = __builtin_bit_cast(bf16x8, buf_load16(rk, off));
-      vreg[kk] = __builtin_bit_cast(bf16x8, buf_load16(rv, off));
+      kreg[kk] = __builtin_bit_cast(e16x8, buf_load16(rk, off));
+      vreg[kk] = __builtin_bit_cast(e16x8, buf_load16(rv, off));
     }
   }
 
@@ -192,12 +196,12 @@ __global__ __launch_bounds__(NW * 64, (D > 64 ? 1 : 2)) void bwd_dkdv_kernel(Bwd
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
         const int off = T::chunk_off(32 * qb + lq, 2 * kk + hf);
-        s = mfma_bf16_32x32x16(lds_read16(qbuf, off), kreg[kk], s);
-        dp = mfma_bf16_32x32x16(lds_read16(obuf, off), vreg[kk], dp);
+        s = H::mfma(lds_read16<E>(qbuf, off), kreg[kk], s);
+        dp = H::mfma(lds_read16<E>(obuf, off), vreg[kk], dp);
       }
       // Register r holds query q0 + 8*(r/4) + 4*hf + r%4 against this lane's key.
       const int kmin = key - q0 - 4 * hf;  // (DIAG) query offsets below this are masked
-      bf16x8 pb[2], dsb[2];
+      e16x8 pb[2], dsb[2];
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const f32x4 lse4 = *reinterpret_cast<const f32x4*>(sr + 32 * qb + 8 * g + 4 * hf);
@@ -207,8 +211,8 @@ __global__ __launch_bounds__(NW * 64, (D > 64 ? 1 : 2)) void bwd_dkdv_kernel(Bwd
           const int r = 4 * g + e;
           float pr = fast_exp2(fmaf(s[r], c, -lse4[e]));
           if constexpr (DIAG) pr = (8 * g + e < kmin) ? 0.f : pr;
-          pb[r >> 3][r & 7] = (bf16)pr;
-          dsb[r >> 3][r & 7] = (bf16)(pr * (dp[r] - dl4[e]));
+          pb[r >> 3][r & 7] = (E)pr;
+          dsb[r >> 3][r & 7] = (E)(pr * (dp[r] - dl4[e]));
         }
       }
       // dV^T += dO^T P and dK^T += Q^T dS; k-step ks covers queries
@@ -220,8 +224,8 @@ __global__ __launch_bounds__(NW * 64, (D > 64 ? 1 : 2)) void bwd_dkdv_kernel(Bwd
         for (int ks = 0; ks < 2; ++ks) {
           const int r0 = 32 * qb + 16 * ks + tr_row_lane;
           const int o0 = T::elem_off(r0, col), o1 = T::elem_off(r0 + 8, col);
-          dv[db] = mfma_bf16_32x32x16(cat4(lds_read_tr16(obuf, o0), lds_read_tr16(obuf, o1)), pb[ks], dv[db]);
-          dk[db] = mfma_bf16_32x32x16(cat4(lds_read_tr16(qbuf, o0), lds_read_tr16(qbuf, o1)), dsb[ks], dk[db]);
+          dv[db] = H::mfma(cat4<E>(lds_read_tr16<E>(obuf, o0), lds_read_tr16<E>(obuf, o1)), pb[ks], dv[db]);
+          dk[db] = H::mfma(cat4<E>(lds_read_tr16<E>(qbuf, o0), lds_read_tr16<E>(qbuf, o1)), dsb[ks], dk[db]);
         }
       }
     }
@@ -260,15 +264,18 @@ __global__ __launch_bounds__(NW * 64, (D > 64 ? 1 : 2)) void bwd_dkdv_kernel(Bwd
   // dK = scale * dK^T^T and dV, written as whole rows through this wave's idle tile buffer.
   __syncthreads();  // every wave is done reading the last Q / dO tile
   char* stage = w == 0 ? sq0 : (w == 1 ? so0 : (w == 2 ? sq1 : so1));
-  store_rows_via_lds<D, TILE_BYTES>(stage, dk, p.scale, make_rsrc(p.dk + base, head_bytes), key_w0, l);
-  store_rows_via_lds<D, TILE_BYTES>(stage, dv, 1.0f, make_rsrc(p.dv + base, head_bytes), key_w0, l);
+  store_rows_via_lds<E, D, TILE_BYTES>(stage, dk, p.scale, make_rsrc(p.dk + base, head_bytes), key_w0, l);
+  store_rows_via_lds<E, D, TILE_BYTES>(stage, dv, 1.0f, make_rsrc(p.dv + base, head_bytes), key_w0, l);
 }
 
 // ---------------------------------------------------------------------------------------------
 // 3. dQ (query-outer)
 // ---------------------------------------------------------------------------------------------
-template <int D, int BC, int NW, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdParams p) {
+template <typename E, int D, int BC, int NW, bool CAUSAL>
+__global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdParams<E> p) {
+  using H = Half16<E>;
+  using e16x8 = typename H::x8;
+  using e16x4 = typename H::x4;
   constexpr int BR = 32 * NW;
   constexpr int NCH = D / 8;
   constexpr int TILE_BYTES = BC * D * 2;
@@ -309,7 +316,7 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdParams p) {
   // lanes load the matching half of O's row, so delta = rowsum(dO * O) for this row is a dot
   // product over the lane's 8*NKK columns plus one exchange with the lane 32 apart; it is
   // written to the delta buffer for the dK/dV kernel, which runs after this one.
-  bf16x8 qreg[NKK], oreg[NKK];
+  e16x8 qreg[NKK], oreg[NKK];
   float lse2, dlt;
   {
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + base, head_bytes);
@@ -319,9 +326,9 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
       const int off = q * (D * 2) + (16 * kk + 8 * hf) * 2;
-      qreg[kk] = __builtin_bit_cast(bf16x8, buf_load16(rq, off));
-      oreg[kk] = __builtin_bit_cast(bf16x8, buf_load16(rdo, off));
-      const bf16x8 ov = __builtin_bit_cast(bf16x8, buf_load16(rof, off));
+      qreg[kk] = __builtin_bit_cast(e16x8, buf_load16(rq, off));
+      oreg[kk] = __builtin_bit_cast(e16x8, buf_load16(rdo, off));
+      const e16x8 ov = __builtin_bit_cast(e16x8, buf_load16(rof, off));
 #pragma unroll
       for (int e = 0; e < 8; ++e) part = fmaf((float)oreg[kk][e], (float)ov[e], part);
     }
@@ -375,14 +382,14 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
         const int off = T::chunk_off(32 * kb + lq, 2 * kk + hf);
-        s[kb] = mfma_bf16_32x32x16(lds_read16(kbuf, off), qreg[kk], s[kb]);
-        dp[kb] = mfma_bf16_32x32x16(lds_read16(vbuf, off), oreg[kk], dp[kb]);
+        s[kb] = H::mfma(lds_read16<E>(kbuf, off), qreg[kk], s[kb]);
+        dp[kb] = H::mfma(lds_read16<E>(vbuf, off), oreg[kk], dp[kb]);
       }
     }
     const int lim = key_lim - key0 - 4 * hf;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      bf16x8 dsb;
+      e16x8 dsb;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int r = (ks & 1) * 8 + e;
@@ -391,15 +398,15 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdParams p) {
           const int krel = 32 * (ks >> 1) + (r >> 2) * 8 + (r & 3);
           pr = krel <= lim ? pr : 0.f;
         }
-        dsb[e] = (bf16)(pr * (dp[ks >> 1][r] - dlt));
+        dsb[e] = (E)(pr * (dp[ks >> 1][r] - dlt));
       }
       // dQ^T += K^T dS^T; k-step ks covers keys 16ks + {4hf..4hf+3, 8+4hf..8+4hf+3}.
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
         const int col = 32 * db + tr_col_lane;
-        const bf16x4 a0 = lds_read_tr16(kbuf, T::elem_off(16 * ks + tr_row_lane, col));
-        const bf16x4 a1 = lds_read_tr16(kbuf, T::elem_off(16 * ks + 8 + tr_row_lane, col));
-        dq[db] = mfma_bf16_32x32x16(cat4(a0, a1), dsb, dq[db]);
+        const e16x4 a0 = lds_read_tr16<E>(kbuf, T::elem_off(16 * ks + tr_row_lane, col));
+        const e16x4 a1 = lds_read_tr16<E>(kbuf, T::elem_off(16 * ks + 8 + tr_row_lane, col));
+        dq[db] = H::mfma(cat4<E>(a0, a1), dsb, dq[db]);
       }
     }
   };
@@ -433,7 +440,7 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdParams p) {
 
   __syncthreads();  // every wave is done reading the last K / V tile
   char* stage = w == 0 ? sk0 : (w == 1 ? sv0 : (w == 2 ? sk1 : sv1));
-  store_rows_via_lds<D, TILE_BYTES>(stage, dq, p.scale, make_rsrc(p.dq + base, head_bytes), q_w0, l);
+  store_rows_via_lds<E, D, TILE_BYTES>(stage, dq, p.scale, make_rsrc(p.dq + base, head_bytes), q_w0, l);
   }  // item
 }
 
@@ -448,20 +455,21 @@ constexpr int kDqNW = 4, kKvNW = 4, kKvBQ = 64;
 template <int D>
 constexpr int dq_bc() { return D == 128 ? 32 : 64; }
 
-BwdParams make_params(const void* q, const void* k, const void* v, const void* o, const float* lse,
-                      const void* dout, const float* delta, void* dq, void* dk, void* dv, int BH, int N,
-                      float scale) {
-  BwdParams prm;
-  prm.q = static_cast<const bf16*>(q);
-  prm.k = static_cast<const bf16*>(k);
-  prm.v = static_cast<const bf16*>(v);
-  prm.o = static_cast<const bf16*>(o);
-  prm.dout = static_cast<const bf16*>(dout);
+template <typename E>
+BwdParams<E> make_params(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                         const void* dout, const float* delta, void* dq, void* dk, void* dv, int BH, int N,
+                         float scale) {
+  BwdParams<E> prm;
+  prm.q = static_cast<const E*>(q);
+  prm.k = static_cast<const E*>(k);
+  prm.v = static_cast<const E*>(v);
+  prm.o = static_cast<const E*>(o);
+  prm.dout = static_cast<const E*>(dout);
   prm.lse = lse;
   prm.delta = const_cast<float*>(delta);
-  prm.dq = static_cast<bf16*>(dq);
-  prm.dk = static_cast<bf16*>(dk);
-  prm.dv = static_cast<bf16*>(dv);
+  prm.dq = static_cast<E*>(dq);
+  prm.dk = static_cast<E*>(dk);
+  prm.dv = static_cast<E*>(dv);
   prm.N = N;
   prm.nh = BH;
   prm.n_tiles = 0;
@@ -484,58 +492,80 @@ static int num_cus() {
   return cache[dev];
 }
 
-template <int D>
-hipError_t delta_d(BwdParams prm, hipStream_t stream) {
+template <typename E, int D>
+hipError_t delta_d(BwdParams<E> prm, hipStream_t stream) {
   constexpr int RPB = 256 / (D / 8) * 4;  // rows per block (4 per thread group)
   const long rows = (long)prm.nh * prm.N;
-  hipLaunchKernelGGL((bwd_delta_kernel<D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, stream, prm);
+  hipLaunchKernelGGL((bwd_delta_kernel<E, D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, stream, prm);
   return hipGetLastError();
 }
 
-template <int D, bool CAUSAL>
-hipError_t dkdv_d(BwdParams prm, hipStream_t stream) {
+template <typename E, int D, bool CAUSAL>
+hipError_t dkdv_d(BwdParams<E> prm, hipStream_t stream) {
   prm.n_tiles = (prm.N + 32 * kKvNW - 1) / (32 * kKvNW);
-  hipLaunchKernelGGL((bwd_dkdv_kernel<D, kKvNW, kKvBQ, CAUSAL>), dim3(prm.n_tiles * prm.nh), dim3(kKvNW * 64), 0,
+  hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, kKvNW, kKvBQ, CAUSAL>), dim3(prm.n_tiles * prm.nh), dim3(kKvNW * 64), 0,
                      stream, prm);
   return hipGetLastError();
 }
 
-template <int D, bool CAUSAL>
-hipError_t dq_d(BwdParams prm, hipStream_t stream) {
+template <typename E, int D, bool CAUSAL>
+hipError_t dq_d(BwdParams<E> prm, hipStream_t stream) {
   prm.n_tiles = (prm.N + 32 * kDqNW - 1) / (32 * kDqNW);
   // Pair causal tiles when there are at least four workgroups per CU to begin with.
   prm.n_units = (CAUSAL && (long)prm.n_tiles * prm.nh >= 4L * num_cus()) ? (prm.n_tiles + 1) / 2 : prm.n_tiles;
-  hipLaunchKernelGGL((bwd_dq_kernel<D, dq_bc<D>(), kDqNW, CAUSAL>), dim3(prm.n_units * prm.nh), dim3(kDqNW * 64), 0,
+  hipLaunchKernelGGL((bwd_dq_kernel<E, D, dq_bc<D>(), kDqNW, CAUSAL>), dim3(prm.n_units * prm.nh), dim3(kDqNW * 64), 0,
                      stream, prm);
   return hipGetLastError();
 }
 }  // namespace
 
-hipError_t launch_bwd_delta(const void* o, const void* dout, float* delta, int BH, int N, int d,
-                            hipStream_t stream) {
-  BwdParams prm = make_params(nullptr, nullptr, nullptr, o, nullptr, dout, delta, nullptr, nullptr, nullptr, BH, N,
-                              1.f);
-  if (d == 64) return delta_d<64>(prm, stream);
-  if (d == 128) return delta_d<128>(prm, stream);
+namespace {
+template <typename E>
+hipError_t delta_typed(const void* o, const void* dout, float* delta, int BH, int N, int d, hipStream_t stream) {
+  BwdParams<E> prm = make_params<E>(nullptr, nullptr, nullptr, o, nullptr, dout, delta, nullptr, nullptr, nullptr, BH,
+                                    N, 1.f);
+  if (d == 64) return delta_d<E, 64>(prm, stream);
+  if (d == 128) return delta_d<E, 128>(prm, stream);
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse, const void* dout,
+template <typename E>
+hipError_t dkdv_typed(const void* q, const void* k, const void* v, const float* lse, const void* dout,
+                      const float* delta, void* dk, void* dv, int BH, int N, int d, float scale, bool causal,
+                      hipStream_t stream) {
+  BwdParams<E> prm = make_params<E>(q, k, v, nullptr, lse, dout, delta, nullptr, dk, dv, BH, N, scale);
+  if (d == 64) return causal ? dkdv_d<E, 64, true>(prm, stream) : dkdv_d<E, 64, false>(prm, stream);
+  if (d == 128) return causal ? dkdv_d<E, 128, true>(prm, stream) : dkdv_d<E, 128, false>(prm, stream);
+  return hipErrorInvalidValue;
+}
+
+template <typename E>
+hipError_t dq_typed(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                    float* delta, void* dq, int BH, int N, int d, float scale, bool causal, hipStream_t stream) {
+  BwdParams<E> prm = make_params<E>(q, k, v, o, lse, dout, delta, dq, nullptr, nullptr, BH, N, scale);
+  if (d == 64) return causal ? dq_d<E, 64, true>(prm, stream) : dq_d<E, 64, false>(prm, stream);
+  if (d == 128) return causal ? dq_d<E, 128, true>(prm, stream) : dq_d<E, 128, false>(prm, stream);
+  return hipErrorInvalidValue;
+}
+}  // namespace
+
+hipError_t launch_bwd_delta(bool fp16, const void* o, const void* dout, float* delta, int BH, int N, int d,
+                            hipStream_t stream) {
+  return fp16 ? delta_typed<f16>(o, dout, delta, BH, N, d, stream) : delta_typed<bf16>(o, dout, delta, BH, N, d, stream);
+}
+
+hipError_t launch_bwd_dkdv(bool fp16, const void* q, const void* k, const void* v, const float* lse, const void* dout,
                            const float* delta, void* dk, void* dv, int BH, int N, int d, float scale, bool causal,
                            hipStream_t stream) {
-  BwdParams prm = make_params(q, k, v, nullptr, lse, dout, delta, nullptr, dk, dv, BH, N, scale);
-  if (d == 64) return causal ? dkdv_d<64, true>(prm, stream) : dkdv_d<64, false>(prm, stream);
-  if (d == 128) return causal ? dkdv_d<128, true>(prm, stream) : dkdv_d<128, false>(prm, stream);
-  return hipErrorInvalidValue;
+  return fp16 ? dkdv_typed<f16>(q, k, v, lse, dout, delta, dk, dv, BH, N, d, scale, causal, stream)
+              : dkdv_typed<bf16>(q, k, v, lse, dout, delta, dk, dv, BH, N, d, scale, causal, stream);
 }
 
-hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void* o, const float* lse,
+hipError_t launch_bwd_dq(bool fp16, const void* q, const void* k, const void* v, const void* o, const float* lse,
                          const void* dout, float* delta, void* dq, int BH, int N, int d, float scale, bool causal,
                          hipStream_t stream) {
-  BwdParams prm = make_params(q, k, v, o, lse, dout, delta, dq, nullptr, nullptr, BH, N, scale);
-  if (d == 64) return causal ? dq_d<64, true>(prm, stream) : dq_d<64, false>(prm, stream);
-  if (d == 128) return causal ? dq_d<128, true>(prm, stream) : dq_d<128, false>(prm, stream);
-  return hipErrorInvalidValue;
+  return fp16 ? dq_typed<f16>(q, k, v, o, lse, dout, delta, dq, BH, N, d, scale, causal, stream)
+              : dq_typed<bf16>(q, k, v, o, lse, dout, delta, dq, BH, N, d, scale, causal, stream);
 }
 
 }  // namespace fa

@@ -3,7 +3,7 @@
 // Lane layouts below were measured on gfx950 with a probe kernel and are the
 // contract every kernel in this library relies on:
 //
-//   v_mfma_f32_32x32x16_bf16   C[32x32] += A[32x16] * B[16x32]
+//   v_mfma_f32_32x32x16_bf16 / _f16   C[32x32] += A[32x16] * B[16x32]
 //     A: lane l holds row  (l % 32), 8 consecutive k of group (l / 32)
 //     B: lane l holds col  (l % 32), 8 consecutive k of group (l / 32)
 //     C: lane l holds col  (l % 32); accumulator register r holds
@@ -26,19 +26,61 @@ typedef __bf16 bf16;
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16;
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef __fp16 fp16x4_lds __attribute__((ext_vector_type(4)));  // the transpose-read builtin's type
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+typedef __attribute__((address_space(3))) fp16x4_lds lds_f16x4;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 
-__device__ __forceinline__ f32x16 mfma_bf16_32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
+// The 16-bit storage element of the matrix path: bf16 or IEEE fp16. Both are two bytes, so tiles,
+// swizzles and transpose reads are shared; they differ in the matrix instruction, the LDS
+// transpose-read builtin, the float -> 16-bit conversion (a plain cast, round to nearest even) and
+// the two-element dot product.
+template <typename E>
+struct Half16;
+template <>
+struct Half16<bf16> {
+  using x8 = bf16x8;
+  using x4 = bf16x4;
+  using x2 = bf16x2;
+  static __device__ __forceinline__ f32x16 mfma(x8 a, x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ x4 read_tr(const char* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)p);
+  }
+  // p[0] + p[1] accumulated in fp32
+  static __device__ __forceinline__ float dot2_ones(x2 p, float acc) {
+    const x2 ones = {(bf16)1.0f, (bf16)1.0f};
+    return __builtin_amdgcn_fdot2_f32_bf16(p, ones, acc, false);
+  }
+};
+template <>
+struct Half16<f16> {
+  using x8 = f16x8;
+  using x4 = f16x4;
+  using x2 = f16x2;
+  static __device__ __forceinline__ f32x16 mfma(x8 a, x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ x4 read_tr(const char* p) {
+    return __builtin_bit_cast(x4, __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_f16x4*)p));
+  }
+  static __device__ __forceinline__ float dot2_ones(x2 p, float acc) {
+    const x2 ones = {(f16)1.0f, (f16)1.0f};
+    return __builtin_amdgcn_fdot2(p, ones, acc, false);
+  }
+};
 
 __device__ __forceinline__ f32x16 mfma_f32_32x32x2(float a, float b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
@@ -69,7 +111,7 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 __device__ __forceinline__ u32x4 ld_global16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void st_global16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 
-// Row-major bf16 tile of ROWS x D in LDS, stored as 16-byte chunks with an XOR swizzle so that
+// Row-major 16-bit tile of ROWS x D in LDS, stored as 16-byte chunks with an XOR swizzle so that
 // (a) 16 consecutive rows read at the same logical chunk, and (b) 4 consecutive rows times 4
 // consecutive chunks (the transpose-read pattern), both land on distinct 16-byte bank groups.
 template <int D>
@@ -121,27 +163,30 @@ __device__ __forceinline__ void buf_load16_to_lds(__amdgpu_buffer_rsrc_t r, char
 // Wait until this wave's outstanding vector-memory operations (including LDS DMA) have completed.
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-__device__ __forceinline__ bf16x8 lds_read16(const char* base, int off) {
-  return *reinterpret_cast<const bf16x8*>(base + off);
+template <typename E>
+__device__ __forceinline__ typename Half16<E>::x8 lds_read16(const char* base, int off) {
+  return *reinterpret_cast<const typename Half16<E>::x8*>(base + off);
 }
 __device__ __forceinline__ void lds_write16(char* base, int off, u32x4 v) {
   *reinterpret_cast<u32x4*>(base + off) = v;
 }
-__device__ __forceinline__ bf16x4 lds_read_tr16(const char* base, int off) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(base + off));
+template <typename E>
+__device__ __forceinline__ typename Half16<E>::x4 lds_read_tr16(const char* base, int off) {
+  return Half16<E>::read_tr(base + off);
 }
 
-__device__ __forceinline__ bf16x8 cat4(bf16x4 a, bf16x4 b) {
-  return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+template <typename E>
+__device__ __forceinline__ typename Half16<E>::x8 cat4(typename Half16<E>::x4 a, typename Half16<E>::x4 b) {
+  return typename Half16<E>::x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
 
 // Write a wave's 32 x D block from the MFMA accumulator layout (lane l holds row l % 32, and
 // register r of block db holds column 32*db + 8*(r/4) + 4*(l/32) + r%4) to rows row0..row0+31 of a
-// row-major bf16 [rows, D] tensor, scaled by `mul`. The block is staged through `stage` (LDS
+// row-major 16-bit [rows, D] tensor (element E, rounded to nearest even), scaled by `mul`. The block is staged through `stage` (LDS
 // owned by this wave, STAGE_BYTES long; rows padded by 16 bytes against bank conflicts; two
 // passes of 16 rows when 32 rows do not fit) so global stores are whole rows of 16-byte chunks.
 // Rows beyond the descriptor's range are dropped.
-template <int D, int STAGE_BYTES>
+template <typename E, int D, int STAGE_BYTES>
 __device__ __forceinline__ void store_rows_via_lds(char* stage, const f32x16 (&acc)[D / 32], float mul,
                                                    __amdgpu_buffer_rsrc_t r, int row0, int lane) {
   constexpr int PITCH = D * 2 + 16, NCH = D / 8;
@@ -156,10 +201,10 @@ __device__ __forceinline__ void store_rows_via_lds(char* stage, const f32x16 (&a
       for (int db = 0; db < D / 32; ++db) {
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          bf16x4 t;
+          typename Half16<E>::x4 t;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) t[e] = (bf16)(acc[db][4 * g + e] * mul);
-          *reinterpret_cast<bf16x4*>(stage + srow * PITCH + (32 * db + 8 * g + 4 * hf) * 2) = t;
+          for (int e = 0; e < 4; ++e) t[e] = (E)(acc[db][4 * g + e] * mul);
+          *reinterpret_cast<typename Half16<E>::x4*>(stage + srow * PITCH + (32 * db + 8 * g + 4 * hf) * 2) = t;
         }
       }
     }
@@ -176,10 +221,5 @@ __device__ __forceinline__ void store_rows_via_lds(char* stage, const f32x16 (&a
   }
 }
 
-// Sum of the two bf16 values of a packed pair, accumulated in fp32.
-__device__ __forceinline__ float dot2_ones(bf16x2 p, float acc) {
-  const bf16x2 ones = {(bf16)1.0f, (bf16)1.0f};
-  return __builtin_amdgcn_fdot2_f32_bf16(p, ones, acc, false);
-}
 
 }  // namespace fa

@@ -1,4 +1,4 @@
-// Fused bf16 attention forward for gfx950.
+// Fused attention forward for gfx950, 16-bit storage (bf16 or fp16).
 //
 // What it computes (52jiny.com FlashAttention explainer, "key ideas" parts 1-3;
 // codechina.net CUDA/FlashAttention article, sections 4.1-4.2 and 5.1): one
@@ -13,10 +13,10 @@
 //
 // gfx950 mapping:
 //  * a wave owns 32 query rows and computes the transposed score block
-//    S^T = K Q^T with v_mfma_f32_32x32x16_bf16, so each lane holds the scores
+//    S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (or _f16), so each lane holds the scores
 //    of ONE query (its column) for 16 of every 32 keys; the other 16 sit in
 //    the lane 32 apart.
-//  * the same accumulator registers, rounded to bf16, are the B operand of
+//  * the same accumulator registers, rounded to the 16-bit type, are the B operand of
 //    O^T += V^T P^T; V^T comes from the row-major V tile in LDS through the
 //    gfx950 LDS transpose read (ds_read_b64_tr_b16), with the key order chosen
 //    to match the accumulator's row order.
@@ -33,13 +33,13 @@
 //      B(j): S(j+1, keys 0-31) and O += P(j, keys 0-31) V on the matrix cores,
 //            probabilities of S(j, keys 32-63) on the VALU.
 //    Inside a phase every matrix instruction is followed by a slice of the
-//    element work (exponent argument, exp2, sums, bf16 packing) of different
+//    element work (exponent argument, exp2, sums, 16-bit packing) of different
 //    scores, each stage a step after the previous one, and LDS fragments are
 //    fetched four instructions ahead; scheduling barriers keep this order.
 //    One barrier per tile: K(j+2) and V(j+1) are issued right after the barrier
 //    that follows A(j), the last reader of the buffers they overwrite.
 //  * softmax in the log2 domain: p = exp2(s*c - m) with c = |scale| * log2(e)
-//    (a negative scale is applied by negating Q, which is exact in bf16). There
+//    (a negative scale is applied by negating Q, which is exact in 16 bits). There
 //    is no per-tile row maximum: any reference m gives the same O = sum p V /
 //    sum p and LSE = m + log l, so m is only moved when it has to be. The
 //    per-lane sum of a half's 16 probabilities (needed anyway for l) bounds each
@@ -47,12 +47,12 @@
 //    still a placeholder, and later only if the scores climb by more than ~16
 //    log2 units) the half takes a slow path that raises m to the half's max,
 //    rescales O and the sums, and recomputes. Probabilities therefore stay
-//    below 2^16, far inside fp32/bf16 range, and the maximum reduction leaves
+//    below 2^16 (2^15 for fp16, whose largest value is 65504), and the maximum reduction leaves
 //    the common path.
 //  * two row sums are kept: l over the fp32 probabilities (for LSE: summing the
 //    rounded values would put up to ~2e-3 of error into LSE on rows dominated
-//    by a few keys), and l~ over the bf16-rounded probabilities that actually
-//    multiply V (v_dot2_f32_bf16, half an instruction per score). O is divided
+//    by a few keys), and l~ over the 16-bit-rounded probabilities that actually
+//    multiply V (v_dot2_f32_bf16 / _f16, half an instruction per score). O is divided
 //    by l~, so the weights applied to V sum to one exactly; with a reference
 //    max that is not the row max the dominant probability is not exactly 1, and
 //    dividing by l would leave its rounding error (up to 2^-9 |V|) in O.
@@ -67,27 +67,34 @@
 
 namespace fa {
 
-struct FwdBf16Params {
-  const bf16* q;
-  const bf16* k;
-  const bf16* v;
-  bf16* o;
+template <typename E>
+struct Fwd16Params {
+  const E* q;
+  const E* k;
+  const E* v;
+  E* o;
   float* lse;
   int N;
   int nh;
   int n_qt;
   float c;        // |scale| * log2(e) (a tiny positive value when scale == 0)
-  uint32_t qsign;  // 0x80008000 to negate Q (negative scale), else 0
+  uint32_t qsign;  // 0x80008000 to negate Q (negative scale; the sign bit of both 16-bit types), else 0
 };
 
 // A block's per-lane probability sum above this bound means some probability may have left the
 // safe range (or the running max is still the initial placeholder): the block then takes the
 // slow path, which raises the running max to the block's max and recomputes.
-constexpr float kOverflowSum = 65536.0f;
+// (fp16 tops out at 65504, so its probabilities are held below 2^15.)
+template <typename E>
+constexpr float kOverflowSum = std::is_same<E, f16>::value ? 32768.0f : 65536.0f;
 constexpr float kInitMax = -1e30f;
 
-template <int D, int BC, int NW, bool CAUSAL>
-__global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdBf16Params p) {
+template <typename E, int D, int BC, int NW, bool CAUSAL>
+__global__ __launch_bounds__(NW * 64, 2) void fwd16_kernel(Fwd16Params<E> p) {
+  using H = Half16<E>;
+  using e16x8 = typename H::x8;
+  using e16x4 = typename H::x4;
+  using e16x2 = typename H::x2;
   static_assert(BC == 64, "two 32-key halves per tile");
   constexpr int BR = 32 * NW;
   constexpr int NCH = D / 8;
@@ -111,21 +118,21 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdBf16Params p) {
   int head, qt;
   map_workgroup(blockIdx.x, p.n_qt, p.nh, CAUSAL ? Order::kLongestFirst : Order::kHeadMajor, true, head, qt);
   const size_t base = (size_t)head * N * D;
-  const bf16* Kh = p.k + base;
-  const bf16* Vh = p.v + base;
+  const E* Kh = p.k + base;
+  const E* Vh = p.v + base;
   const int head_bytes = N * D * 2;
   const int q_w0 = qt * BR + 32 * w;
   const int q = q_w0 + lq;
 
   // Q^T operand: lane (q, hf) holds Q[q][16*kk + 8*hf .. +7]; rows >= N read as zero.
-  bf16x8 qreg[NKK];
+  e16x8 qreg[NKK];
   {
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + base, head_bytes);
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
       u32x4 t = buf_load16(rq, q * (D * 2) + (16 * kk + 8 * hf) * 2);
       t ^= p.qsign;
-      qreg[kk] = __builtin_bit_cast(bf16x8, t);
+      qreg[kk] = __builtin_bit_cast(e16x8, t);
     }
   }
   int n_kv = (N + BC - 1) / BC;
@@ -141,7 +148,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdBf16Params p) {
     const int row = pos / NCH, pc = pos % NCH;
     goff[i] = row * (D * 2) + ((pc ^ T::swz(row)) * 16);
   }
-  auto dma = [&](const bf16* src, int j, char* dst) __attribute__((always_inline)) {
+  auto dma = [&](const E* src, int j, char* dst) __attribute__((always_inline)) {
     const int key0 = j * BC;
     const int rows = __builtin_amdgcn_readfirstlane(max(0, min(BC, N - key0)));
     const __amdgpu_buffer_rsrc_t r = make_rsrc(src + (size_t)min(key0, N) * D, rows * (D * 2));
@@ -166,7 +173,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdBf16Params p) {
     s = f32x16{};
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk)
-      s = mfma_bf16_32x32x16(lds_read16(kbuf, T::chunk_off(32 * h + lq, 2 * kk + hf)), qreg[kk], s);
+      s = H::mfma(lds_read16<E>(kbuf, T::chunk_off(32 * h + lq, 2 * kk + hf)), qreg[kk], s);
   };
   // Causal / ragged mask of the 32-key half `h` of tile j (only where it can bite).
   auto mask_half = [&](f32x16& s, int j, int h) __attribute__((always_inline)) {
@@ -181,29 +188,29 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdBf16Params p) {
     }
   };
   f32x16 s0, s1;
-  bf16x8 p0[2], p1[2];
+  e16x8 p0[2], p1[2];
   float rs, rr;
   // One pipeline phase: NS = NKK MFMAs of S^T for K half `hs` (into s_out), NPV = 2 * NDB MFMAs of
   // O^T += V^T P^T for V half `hv` (from p_in), and the probabilities of s_in (into p_out), with
-  // their fp32 sum in rs and the sum of their bf16 roundings in rr. The work is issued in a fixed
+  // their fp32 sum in rs and the sum of their 16-bit roundings in rr. The work is issued in a fixed
   // interleave, fenced by scheduling barriers.
-  auto phase = [&](auto with_pv, f32x16& s_out, const char* kbuf, int hs, const bf16x8 (&p_in)[2],
-                   const char* vbuf, int hv, const f32x16& s_in, bf16x8 (&p_out)[2]) __attribute__((always_inline)) {
+  auto phase = [&](auto with_pv, f32x16& s_out, const char* kbuf, int hs, const e16x8 (&p_in)[2],
+                   const char* vbuf, int hv, const f32x16& s_in, e16x8 (&p_out)[2]) __attribute__((always_inline)) {
     constexpr bool PV = decltype(with_pv)::value;
     constexpr int NS = NKK, NPV = PV ? 2 * NDB : 0, NM = NS + NPV;
-    auto frag = [&](int i) __attribute__((always_inline)) -> bf16x8 {
-      if (i < NS) return lds_read16(kbuf, T::chunk_off(32 * hs + lq, 2 * i + hf));
+    auto frag = [&](int i) __attribute__((always_inline)) -> e16x8 {
+      if (i < NS) return lds_read16<E>(kbuf, T::chunk_off(32 * hs + lq, 2 * i + hf));
       const int t = (i - NS) / NDB, db = (i - NS) % NDB, ks = 2 * hv + t;
       const int col = 32 * db + v_col_lane;
-      const bf16x4 a0 = lds_read_tr16(vbuf, T::elem_off(16 * ks + v_row_lane, col));
-      const bf16x4 a1 = lds_read_tr16(vbuf, T::elem_off(16 * ks + 8 + v_row_lane, col));
-      return cat4(a0, a1);
+      const e16x4 a0 = lds_read_tr16<E>(vbuf, T::elem_off(16 * ks + v_row_lane, col));
+      const e16x4 a1 = lds_read_tr16<E>(vbuf, T::elem_off(16 * ks + 8 + v_row_lane, col));
+      return cat4<E>(a0, a1);
     };
     const float neg_m = -m_run;
     float a0 = 0.f, a1 = 0.f, r0 = 0.f;
     // Element k of the 16 probabilities goes through three stages, each in a later matrix step
     // than the previous so no stage waits on the latency of the one before: x = s*c - m,
-    // p = exp2(x), then the sums and (odd k) the bf16 pair.
+    // p = exp2(x), then the sums and (odd k) the 16-bit pair.
     float xv[16], pv[16];
     auto st_fma = [&](int k) __attribute__((always_inline)) {
       xv[k] = fmaf(s_in[k], c, neg_m);
@@ -220,8 +227,8 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdBf16Params p) {
         asm volatile("" ::"v"(a0));
       } else {
         a1 += pv[k];
-        const bf16x2 pr = {(bf16)pv[k - 1], (bf16)pv[k]};
-        r0 = dot2_ones(pr, r0);
+        const e16x2 pr = {(E)pv[k - 1], (E)pv[k]};
+        r0 = H::dot2_ones(pr, r0);
         p_out[t][e - 1] = pr[0];
         p_out[t][e] = pr[1];
         asm volatile("" ::"v"(a1), "v"(r0), "v"(pr));
@@ -229,17 +236,17 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdBf16Params p) {
     };
     constexpr int PF = 4;          // LDS fragment prefetch distance (matrix steps)
     constexpr int NSTEP = NM + 2;  // two extra steps drain the element pipeline
-    bf16x8 fr[NM];
+    e16x8 fr[NM];
 #pragma unroll
     for (int i = 0; i < PF && i < NM; ++i) fr[i] = frag(i);
 #pragma unroll
     for (int i = 0; i < NSTEP; ++i) {
       if (i + PF < NM) fr[i + PF] = frag(i + PF);
       if (i < NS) {
-        s_out = mfma_bf16_32x32x16(fr[i], qreg[i], i == 0 ? f32x16{} : s_out);
+        s_out = H::mfma(fr[i], qreg[i], i == 0 ? f32x16{} : s_out);
       } else if (i < NM) {
         const int t = (i - NS) / NDB, db = (i - NS) % NDB;
-        acc_o[db] = mfma_bf16_32x32x16(fr[i], p_in[t], acc_o[db]);
+        acc_o[db] = H::mfma(fr[i], p_in[t], acc_o[db]);
       }
       // element work per step: stage f of element k runs at step (k * NM / 16) + f
       // (stages: 0 fma, 1 exp, 2 sums)
@@ -258,7 +265,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdBf16Params p) {
     asm volatile("" : "+v"(p_out[0]), "+v"(p_out[1]), "+v"(rs), "+v"(rr));
   };
   // Slow-path recomputation of one half's probabilities against the current m.
-  auto probs = [&](const f32x16& s, bf16x8 (&pk)[2], float& rs_, float& rr_) __attribute__((always_inline)) {
+  auto probs = [&](const f32x16& s, e16x8 (&pk)[2], float& rs_, float& rr_) __attribute__((always_inline)) {
     const float neg_m = -m_run;
     float a0 = 0.f, a1 = 0.f, r0 = 0.f;
 #pragma unroll
@@ -269,20 +276,20 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdBf16Params p) {
         const float pb = fast_exp2(fmaf(s[8 * t + e + 1], c, neg_m));
         a0 += pa;
         a1 += pb;
-        const bf16x2 pr = {(bf16)pa, (bf16)pb};
-        r0 = dot2_ones(pr, r0);
+        const e16x2 pr = {(E)pa, (E)pb};
+        r0 = H::dot2_ones(pr, r0);
         pk[t][e] = pr[0];
         pk[t][e + 1] = pr[1];
       }
     rs_ = a0 + a1;
     rr_ = r0;
   };
-  // Accept a half's probabilities, or (some lane's sum above kOverflowSum) raise m to the half's
+  // Accept a half's probabilities, or (some lane's sum above kOverflowSum<E>) raise m to the half's
   // max for the affected rows (both lanes of a row decide together), rescale O, l and l~, and
   // recompute the half.
-  auto settle = [&](const f32x16& s, bf16x8 (&pk)[2]) __attribute__((always_inline)) {
-    if (__builtin_amdgcn_ballot_w64(rs > kOverflowSum)) {
-      const float trig = half_swap_max(rs > kOverflowSum ? 1.f : 0.f);
+  auto settle = [&](const f32x16& s, e16x8 (&pk)[2]) __attribute__((always_inline)) {
+    if (__builtin_amdgcn_ballot_w64(rs > kOverflowSum<E>)) {
+      const float trig = half_swap_max(rs > kOverflowSum<E> ? 1.f : 0.f);
       float mx0 = -INFINITY, mx1 = -INFINITY;
 #pragma unroll
       for (int r = 0; r < 16; r += 4) {
@@ -350,28 +357,29 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd_bf16_kernel(FwdBf16Params p) {
   const float inv = 1.0f / half_swap_sum(lr_run);
   __syncthreads();  // every wave is done reading the last K/V tiles
   char* ostage = w == 0 ? sk0 : (w == 1 ? sv0 : (w == 2 ? sk1 : sv1));
-  store_rows_via_lds<D, TILE_BYTES>(ostage, acc_o, inv, make_rsrc(p.o + base, head_bytes), q_w0, l);
+  store_rows_via_lds<E, D, TILE_BYTES>(ostage, acc_o, inv, make_rsrc(p.o + base, head_bytes), q_w0, l);
   if (p.lse && hf == 0) {
     const __amdgpu_buffer_rsrc_t rl = make_rsrc(p.lse + (size_t)head * N, N * 4);
     buf_store4(rl, q * 4, (m_run + __log2f(l_tot)) * kLn2);
   }
 }
 
-template <int D, int BC, int NW, bool CAUSAL>
-static hipError_t launch_cfg(const FwdBf16Params& prm, hipStream_t stream) {
+template <typename E, int D, int BC, int NW, bool CAUSAL>
+static hipError_t launch_cfg(const Fwd16Params<E>& prm, hipStream_t stream) {
   const int grid = prm.n_qt * prm.nh;
-  hipLaunchKernelGGL((fwd_bf16_kernel<D, BC, NW, CAUSAL>), dim3(grid), dim3(NW * 64), 0, stream, prm);
+  hipLaunchKernelGGL((fwd16_kernel<E, D, BC, NW, CAUSAL>), dim3(grid), dim3(NW * 64), 0, stream, prm);
   return hipGetLastError();
 }
 
-hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int N,
-                           int d, float scale, bool causal, hipStream_t stream) {
+template <typename E>
+static hipError_t launch_typed(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int N,
+                               int d, float scale, bool causal, hipStream_t stream) {
   constexpr int NW = 4, BR = 32 * NW;
-  FwdBf16Params prm;
-  prm.q = static_cast<const bf16*>(q);
-  prm.k = static_cast<const bf16*>(k);
-  prm.v = static_cast<const bf16*>(v);
-  prm.o = static_cast<bf16*>(o);
+  Fwd16Params<E> prm;
+  prm.q = static_cast<const E*>(q);
+  prm.k = static_cast<const E*>(k);
+  prm.v = static_cast<const E*>(v);
+  prm.o = static_cast<E*>(o);
   prm.lse = lse;
   prm.N = N;
   prm.nh = BH;
@@ -381,9 +389,15 @@ hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o,
   // exactly the uniform softmax a zero scale means, and masked scores still map to -inf.
   prm.c = scale == 0.f ? 1e-30f : fabsf(scale) * kLog2e;
   prm.qsign = scale < 0.f ? 0x80008000u : 0u;
-  if (d == 64) return causal ? launch_cfg<64, 64, NW, true>(prm, stream) : launch_cfg<64, 64, NW, false>(prm, stream);
-  if (d == 128) return causal ? launch_cfg<128, 64, NW, true>(prm, stream) : launch_cfg<128, 64, NW, false>(prm, stream);
+  if (d == 64) return causal ? launch_cfg<E, 64, 64, NW, true>(prm, stream) : launch_cfg<E, 64, 64, NW, false>(prm, stream);
+  if (d == 128) return causal ? launch_cfg<E, 128, 64, NW, true>(prm, stream) : launch_cfg<E, 128, 64, NW, false>(prm, stream);
   return hipErrorInvalidValue;
+}
+
+hipError_t launch_fwd_16(bool fp16, const void* q, const void* k, const void* v, void* o, float* lse, int BH, int N,
+                         int d, float scale, bool causal, hipStream_t stream) {
+  return fp16 ? launch_typed<f16>(q, k, v, o, lse, BH, N, d, scale, causal, stream)
+              : launch_typed<bf16>(q, k, v, o, lse, BH, N, d, scale, causal, stream);
 }
 
 }  // namespace fa

@@ -5,21 +5,21 @@
 
 namespace fa {
 
-// Forward, bf16 storage. BH = B*H. d in {64, 128}. c = scale * log2(e).
-hipError_t launch_fwd_bf16(const void* q, const void* k, const void* v, void* o, float* lse,
-                           int BH, int N, int d, float scale, bool causal, hipStream_t stream);
+// Forward, 16-bit storage: bf16 (fp16 = false) or IEEE fp16 (fp16 = true). BH = B*H. d in {64, 128}.
+hipError_t launch_fwd_16(bool fp16, const void* q, const void* k, const void* v, void* o, float* lse,
+                         int BH, int N, int d, float scale, bool causal, hipStream_t stream);
 
 // Forward, fp32 storage. d in {64, 128}.
 hipError_t launch_fwd_fp32(const void* q, const void* k, const void* v, void* o, float* lse,
                            int BH, int N, int d, float scale, bool causal, hipStream_t stream);
 
-// Backward stages, bf16 storage, d in {64, 128}. delta: float32 [BH, N].
-hipError_t launch_bwd_delta(const void* o, const void* dout, float* delta, int BH, int N, int d,
+// Backward stages, 16-bit storage (bf16 or fp16), d in {64, 128}. delta: float32 [BH, N].
+hipError_t launch_bwd_delta(bool fp16, const void* o, const void* dout, float* delta, int BH, int N, int d,
                             hipStream_t stream);
-hipError_t launch_bwd_dkdv(const void* q, const void* k, const void* v, const float* lse,
+hipError_t launch_bwd_dkdv(bool fp16, const void* q, const void* k, const void* v, const float* lse,
                            const void* dout, const float* delta, void* dk, void* dv, int BH, int N,
                            int d, float scale, bool causal, hipStream_t stream);
-hipError_t launch_bwd_dq(const void* q, const void* k, const void* v, const void* o,
+hipError_t launch_bwd_dq(bool fp16, const void* q, const void* k, const void* v, const void* o,
                          const float* lse, const void* dout, float* delta, void* dq, int BH, int N,
                          int d, float scale, bool causal, hipStream_t stream);
 

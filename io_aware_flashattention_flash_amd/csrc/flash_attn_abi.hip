@@ -22,6 +22,7 @@ fa_status_t check_shape(int B, int H, int N, int d) {
 }
 
 bool supported_d(int d) { return d == 64 || d == 128; }
+bool is_16bit(int dtype) { return dtype == FA_DTYPE_BF16 || dtype == FA_DTYPE_FP16; }
 
 }  // namespace
 
@@ -32,13 +33,14 @@ fa_status_t flash_attn_fwd(const void* q, const void* k, const void* v, void* o,
   if (!q || !k || !v || !o) return FA_ERR_NULL_POINTER;
   fa_status_t st = check_shape(B, H, N, d);
   if (st != FA_OK) return st;
-  if ((dtype != FA_DTYPE_BF16 && dtype != FA_DTYPE_FP32) || !supported_d(d)) return FA_ERR_UNSUPPORTED;
+  if ((!is_16bit(dtype) && dtype != FA_DTYPE_FP32) || !supported_d(d)) return FA_ERR_UNSUPPORTED;
   if (!isfinite(scale)) return FA_ERR_BAD_SCALE;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || (lse && !aligned4(lse)))
     return FA_ERR_MISALIGNED;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = dtype == FA_DTYPE_BF16 ? fa::launch_fwd_bf16(q, k, v, o, lse, B * H, N, d, scale, causal != 0, s)
-                                        : fa::launch_fwd_fp32(q, k, v, o, lse, B * H, N, d, scale, causal != 0, s);
+  hipError_t e = is_16bit(dtype)
+                     ? fa::launch_fwd_16(dtype == FA_DTYPE_FP16, q, k, v, o, lse, B * H, N, d, scale, causal != 0, s)
+                     : fa::launch_fwd_fp32(q, k, v, o, lse, B * H, N, d, scale, causal != 0, s);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
@@ -50,11 +52,11 @@ size_t flash_attn_bwd_workspace_size(int B, int H, int N, int d, int dtype) {
 }
 
 namespace {
-// Checks shared by the backward entry points (bf16 only).
+// Checks shared by the backward entry points (16-bit types only).
 fa_status_t check_bwd_common(int B, int H, int N, int d, float scale, int dtype) {
   fa_status_t st = check_shape(B, H, N, d);
   if (st != FA_OK) return st;
-  if (dtype != FA_DTYPE_BF16 || !supported_d(d)) return FA_ERR_UNSUPPORTED;
+  if (!is_16bit(dtype) || !supported_d(d)) return FA_ERR_UNSUPPORTED;
   if (!isfinite(scale)) return FA_ERR_BAD_SCALE;
   return FA_OK;
 }
@@ -66,7 +68,7 @@ fa_status_t flash_attn_bwd_delta(const void* o, const void* dout, float* delta, 
   fa_status_t st = check_bwd_common(B, H, N, d, 1.0f, dtype);
   if (st != FA_OK) return st;
   if (!aligned16(o) || !aligned16(dout) || !aligned4(delta)) return FA_ERR_MISALIGNED;
-  hipError_t e = fa::launch_bwd_delta(o, dout, delta, B * H, N, d, static_cast<hipStream_t>(stream));
+  hipError_t e = fa::launch_bwd_delta(dtype == FA_DTYPE_FP16, o, dout, delta, B * H, N, d, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
@@ -79,8 +81,8 @@ fa_status_t flash_attn_bwd_dkdv(const void* q, const void* k, const void* v, con
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(dout) || !aligned16(dk) || !aligned16(dv) ||
       !aligned4(lse) || !aligned4(delta))
     return FA_ERR_MISALIGNED;
-  hipError_t e = fa::launch_bwd_dkdv(q, k, v, lse, dout, delta, dk, dv, B * H, N, d, scale, causal != 0,
-                                     static_cast<hipStream_t>(stream));
+  hipError_t e = fa::launch_bwd_dkdv(dtype == FA_DTYPE_FP16, q, k, v, lse, dout, delta, dk, dv, B * H, N, d, scale,
+                                     causal != 0, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
@@ -93,8 +95,8 @@ fa_status_t flash_attn_bwd_dq(const void* q, const void* k, const void* v, const
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) || !aligned16(dq) ||
       !aligned4(lse) || !aligned4(delta))
     return FA_ERR_MISALIGNED;
-  hipError_t e = fa::launch_bwd_dq(q, k, v, o, lse, dout, delta, dq, B * H, N, d, scale, causal != 0,
-                                   static_cast<hipStream_t>(stream));
+  hipError_t e = fa::launch_bwd_dq(dtype == FA_DTYPE_FP16, q, k, v, o, lse, dout, delta, dq, B * H, N, d, scale,
+                                   causal != 0, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
@@ -111,8 +113,10 @@ fa_status_t flash_attn_bwd(const void* q, const void* k, const void* v, const vo
   if (!aligned16(workspace)) return FA_ERR_MISALIGNED;
   hipStream_t s = static_cast<hipStream_t>(stream);
   float* delta = static_cast<float*>(workspace);
-  hipError_t e = fa::launch_bwd_dq(q, k, v, o, lse, dout, delta, dq, B * H, N, d, scale, causal != 0, s);
-  if (e == hipSuccess) e = fa::launch_bwd_dkdv(q, k, v, lse, dout, delta, dk, dv, B * H, N, d, scale, causal != 0, s);
+  const bool fp16 = dtype == FA_DTYPE_FP16;
+  hipError_t e = fa::launch_bwd_dq(fp16, q, k, v, o, lse, dout, delta, dq, B * H, N, d, scale, causal != 0, s);
+  if (e == hipSuccess)
+    e = fa::launch_bwd_dkdv(fp16, q, k, v, lse, dout, delta, dk, dv, B * H, N, d, scale, causal != 0, s);
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

@@ -21,7 +21,8 @@ LIB_PATH = os.path.join(_HERE, "libflashattn.so")
 
 FA_DTYPE_FP32 = 0
 FA_DTYPE_BF16 = 1
-_DTYPES = {torch.float32: FA_DTYPE_FP32, torch.bfloat16: FA_DTYPE_BF16}
+FA_DTYPE_FP16 = 2
+_DTYPES = {torch.float32: FA_DTYPE_FP32, torch.bfloat16: FA_DTYPE_BF16, torch.float16: FA_DTYPE_FP16}
 
 # Names and C signatures of every exported entry point (mirrors include/flash_attn.h).
 _vp, _int, _float, _size = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
@@ -80,7 +81,7 @@ def _check_tensor(name: str, t: torch.Tensor, like: Optional[torch.Tensor] = Non
     if t.dim() != 4:
         raise ValueError(f"{name} must be 4-D [B, H, N, d], got {tuple(t.shape)}")
     if t.dtype not in _DTYPES:
-        raise ValueError(f"{name} must be bfloat16 or float32, got {t.dtype}")
+        raise ValueError(f"{name} must be bfloat16, float16 or float32, got {t.dtype}")
     if like is not None and (t.shape != like.shape or t.dtype != like.dtype or t.device != like.device):
         raise ValueError(f"{name} must match q in shape, dtype and device")
 

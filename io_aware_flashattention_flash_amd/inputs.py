@@ -28,7 +28,7 @@ import numpy as np
 @dataclasses.dataclass(frozen=True)
 class Workload:
     name: str
-    dtype: str          # "fp32" or "bf16": storage type of Q, K, V, O, dO
+    dtype: str          # "fp32", "bf16" or "fp16": storage type of Q, K, V, O, dO
     B: int
     H: int
     N: int
@@ -79,6 +79,21 @@ def round_to_bf16(x: np.ndarray) -> np.ndarray:
     return (r.astype(np.uint32) << 16).view(np.float32)
 
 
+def round_to_fp16(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to the nearest IEEE binary16 (ties to even, NumPy's cast); returned as
+    float32. Values beyond the binary16 range become infinite."""
+    return np.ascontiguousarray(x, dtype=np.float32).astype(np.float16).astype(np.float32)
+
+
+def round_to(x: np.ndarray, dtype: str) -> np.ndarray:
+    """Round float32 values to the storage type `dtype` ("fp32" leaves them unchanged)."""
+    if dtype == "bf16":
+        return round_to_bf16(x)
+    if dtype == "fp16":
+        return round_to_fp16(x)
+    return np.ascontiguousarray(x, dtype=np.float32)
+
+
 def make_inputs(w: Workload, seed: Optional[int] = None, shape=None) -> Dict[str, np.ndarray]:
     """Draw Q, K, V (and dO for a backward workload) for workload ``w``.
 
@@ -93,9 +108,7 @@ def make_inputs(w: Workload, seed: Optional[int] = None, shape=None) -> Dict[str
         t = rng.standard_normal(shape).astype(np.float32)
         if nm == "q" and w.q_mult != 1.0:
             t = t * np.float32(w.q_mult)
-        if w.dtype == "bf16":
-            t = round_to_bf16(t)
-        out[nm] = t
+        out[nm] = round_to(t, w.dtype)
     return out
 
 
@@ -103,4 +116,4 @@ def random_tensor(shape, seed: int, dtype: str = "bf16", mult: float = 1.0) -> n
     """One standard-normal tensor from its own seed (for edge-case tests)."""
     rng = np.random.default_rng(seed)
     t = (rng.standard_normal(shape) * mult).astype(np.float32)
-    return round_to_bf16(t) if dtype == "bf16" else t
+    return round_to(t, dtype)

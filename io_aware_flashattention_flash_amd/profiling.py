@@ -21,8 +21,8 @@ import os
 from collections import defaultdict
 
 CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
-KERNEL_SOURCES = {"fwd": "fa_fwd_bf16.hip", "bwd_dq": "fa_bwd_bf16.hip", "bwd_dkdv": "fa_bwd_bf16.hip"}
-KERNEL_PREFIX = {"fwd": "fa::fwd_bf16_kernel", "bwd_dq": "fa::bwd_dq_kernel", "bwd_dkdv": "fa::bwd_dkdv_kernel"}
+KERNEL_SOURCES = {"fwd": "fa_fwd_16bit.hip", "bwd_dq": "fa_bwd_16bit.hip", "bwd_dkdv": "fa_bwd_16bit.hip"}
+KERNEL_PREFIX = {"fwd": "fa::fwd16_kernel", "bwd_dq": "fa::bwd_dq_kernel", "bwd_dkdv": "fa::bwd_dkdv_kernel"}
 
 
 def source_digest(kernel: str) -> str:

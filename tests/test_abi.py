@@ -81,7 +81,7 @@ def test_fwd_bad_shape(lib, shape):
     assert _fwd(lib, B=B, H=H, N=N, d=d) == SHAPE
 
 
-@pytest.mark.parametrize("d,dtype", [(32, 1), (96, 1), (256, 1), (80, 0), (64, 2), (64, -1)])
+@pytest.mark.parametrize("d,dtype", [(32, 1), (96, 1), (256, 1), (80, 0), (96, 2), (64, 3), (64, -1)])
 def test_fwd_unsupported(lib, d, dtype):
     assert _fwd(lib, d=d, dtype=dtype) == UNSUP
 
@@ -162,6 +162,16 @@ def _dq(lib, **kw):
     a = _stage_args(**kw)
     return lib.flash_attn_bwd_dq(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["delta"], a["dq"], a["B"],
                                  a["H"], a["N"], a["d"], a["scale"], a["causal"], a["dtype"], None)
+
+
+def test_fp16_passes_the_dtype_check(lib):
+    """dtype 2 (fp16) is in the support matrix of every entry point: its calls get past the dtype
+    check to the later ones (these fake pointers never reach a launch)."""
+    assert _fwd(lib, dtype=2, q=A + 8) == ALIGN
+    assert _bwd(lib, dtype=2, scale=math.nan) == SCALE
+    assert _dq(lib, dtype=2, k=A + 8) == ALIGN
+    assert _dkdv(lib, dtype=2, lse=A + 1) == ALIGN
+    assert lib.flash_attn_bwd_delta(A, A, A + 2, 1, 1, 8, 64, 2, None) == ALIGN
 
 
 def test_bwd_stage_validation(lib):

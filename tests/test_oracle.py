@@ -69,6 +69,18 @@ def test_bf16_rounding_matches_torch():
     np.testing.assert_array_equal(ours, ref)
 
 
+def test_fp16_rounding_matches_torch():
+    """The fp16 input rounding (NumPy's cast) agrees with torch's float32 -> float16 conversion,
+    including ties and values near the binary16 subnormal boundary."""
+    import torch
+
+    x = np.random.default_rng(74).standard_normal(100000).astype(np.float32) * 3
+    x[:5] = [1.0 + 2 ** -11, 1.0 + 3 * 2 ** -11, -(1.0 + 2 ** -11), 0.0, 2 ** -15]  # exact ties both ways
+    ours = inputs.round_to_fp16(x)
+    ref = torch.tensor(x).to(torch.float16).to(torch.float32).numpy()
+    np.testing.assert_array_equal(ours, ref)
+
+
 def test_recipe_regression_golden():
     """Oracle output on the fp32 N=128 d=64 workload under the seeded recipe, stored by
     tests/golden/make_golden.py (which calls only the oracle and the input module)."""

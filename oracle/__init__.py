@@ -7,7 +7,8 @@ native library is missing instead of falling back to anything here.
 
 Contents:
   attention.py  plain definition: explicit S, mask, row softmax, P.V, LSE, and
-                the analytic backward (NumPy, float64).
+                the analytic backward (NumPy, float64); attn_fwd_kv is the same
+                forward for Nq queries against Nk >= Nq keys.
   brute.py      pure-Python triple loops with math.exp / math.fsum for tiny
                 shapes (an independent second statement of the forward).
   online.py     the blocked online-softmax recurrence, step by step, used only
@@ -17,8 +18,8 @@ Every function cites the passage of the pages it follows. Parity pins (closed
 forms, invariants, brute force, library special cases, finite differences)
 live in tests/test_oracle.py.
 """
-from .attention import attn_fwd, attn_fwd_rows, attn_bwd, softmax_rows
+from .attention import attn_bwd, attn_fwd, attn_fwd_kv, attn_fwd_rows, softmax_rows
 from .brute import brute_fwd
 from .online import online_fwd
 
-__all__ = ["attn_fwd", "attn_fwd_rows", "attn_bwd", "softmax_rows", "brute_fwd", "online_fwd"]
+__all__ = ["attn_fwd", "attn_fwd_kv", "attn_fwd_rows", "attn_bwd", "softmax_rows", "brute_fwd", "online_fwd"]

@@ -77,6 +77,30 @@ def attn_fwd(q, k, v, scale: float, causal: bool):
     return O, LSE
 
 
+def attn_fwd_kv(q, k, v, scale: float, causal: bool):
+    """Attention of Nq queries [B, H, Nq, d] against Nk >= Nq keys and values [B, H, Nk, d]
+    (decoding new positions against a key/value history) -> (O [B,H,Nq,d], LSE [B,H,Nq]).
+
+    Reading (the pages define only the square case): the queries are the last Nq positions of
+    the key sequence, so with the causal mask query i, at position Nk - Nq + i, sees keys
+    j <= Nk - Nq + i. Otherwise it is the same definition as attn_fwd: explicit scaled scores,
+    mask, row softmax, P V and LSE = m + ln l."""
+    q, k, v = _f64(q), _f64(k), _f64(v)
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    O = np.empty((B, H, Nq, d))
+    LSE = np.empty((B, H, Nq))
+    for b in range(B):
+        for h in range(H):
+            for r0 in range(0, Nq, _ROW_CHUNK):
+                rows = np.arange(r0, min(Nq, r0 + _ROW_CHUNK))
+                S = _scores(q[b, h, rows], k[b, h], scale, causal, rows + (Nk - Nq))
+                P, _, _, lse = softmax_rows(S)
+                O[b, h, rows] = P @ v[b, h]
+                LSE[b, h, rows] = lse
+    return O, LSE
+
+
 def attn_fwd_rows(q, k, v, scale: float, causal: bool, b: int, h: int, rows):
     """The same definition restricted to some query rows of one (b, h):
     returns (O_rows [len(rows), d], LSE_rows [len(rows)]). Each row of the plain

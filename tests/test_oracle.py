@@ -117,3 +117,63 @@ def test_lse_definition_on_causal_prefix():
     s = [[0.5], [-1.0, 0.0], [-0.5, 2.0, 0.0]]
     for i in range(3):
         assert abs(L[0, 0, i] - math.log(math.fsum(math.exp(t) for t in s[i]))) < 1e-14
+
+
+# ---------------------------------------------------------------------------------------------
+# Nq queries against Nk >= Nq keys (decode / chunked prefill)
+# ---------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("nq", [1, 5, 37])
+def test_kv_oracle_matches_torch_sdpa_with_bottom_right_mask(causal, nq):
+    """torch's float64 scaled_dot_product_attention with an explicit mask that lets query i see
+    keys j <= Nk - Nq + i (and the matching logsumexp) on non-square inputs."""
+    import torch
+
+    from oracle import attn_fwd_kv
+
+    rng = np.random.default_rng(80 + nq)
+    B, H, Nk, d = 2, 3, 37, 6
+    q = rng.standard_normal((B, H, nq, d))
+    k, v = rng.standard_normal((B, H, Nk, d)), rng.standard_normal((B, H, Nk, d))
+    scale = 0.7
+    tq, tk, tv = (torch.tensor(x, dtype=torch.float64) for x in (q, k, v))
+    visible = torch.ones(nq, Nk, dtype=torch.bool)
+    if causal:
+        visible = torch.arange(Nk)[None, :] <= (torch.arange(nq)[:, None] + Nk - nq)
+    tO = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=visible, scale=scale)
+    s = (scale * (tq @ tk.transpose(-1, -2))).masked_fill(~visible, float("-inf"))
+    O, L = attn_fwd_kv(q, k, v, scale, causal)
+    np.testing.assert_allclose(O, tO.numpy(), atol=1e-12)
+    np.testing.assert_allclose(L, torch.logsumexp(s, dim=-1).numpy(), atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_kv_oracle_is_the_tail_of_the_full_sequence(causal):
+    """Decoding property: the last Nq rows of the square problem over the whole sequence are the
+    non-square problem of those Nq queries against all keys (for every Nq, including Nq = Nk)."""
+    from oracle import attn_fwd_kv
+
+    rng = np.random.default_rng(81)
+    N, d = 29, 5
+    q, k, v = (rng.standard_normal((1, 2, N, d)) for _ in range(3))
+    O_full, L_full = attn_fwd(q, k, v, 0.8, causal)
+    for nq in (1, 2, 13, N):
+        O, L = attn_fwd_kv(q[:, :, N - nq:], k, v, 0.8, causal)
+        np.testing.assert_allclose(O, O_full[:, :, N - nq:], atol=1e-13)
+        np.testing.assert_allclose(L, L_full[:, :, N - nq:], atol=1e-13)
+
+
+def test_kv_oracle_equal_keys_give_the_mean_of_values():
+    """Closed form: with every key equal, every visible score is equal, so a single decoded query
+    (which sees all Nk keys, causal or not) returns the mean of V and LSE = scale*q.k + ln Nk."""
+    from oracle import attn_fwd_kv
+
+    rng = np.random.default_rng(82)
+    Nk, d = 23, 4
+    q = rng.standard_normal((1, 1, 1, d))
+    k = np.repeat(rng.standard_normal((1, 1, 1, d)), Nk, axis=2)
+    v = rng.standard_normal((1, 1, Nk, d))
+    for causal in (False, True):
+        O, L = attn_fwd_kv(q, k, v, 1.3, causal)
+        np.testing.assert_allclose(O[0, 0, 0], v[0, 0].mean(axis=0), atol=1e-13)
+        np.testing.assert_allclose(L[0, 0, 0], 1.3 * float(q[0, 0, 0] @ k[0, 0, 0]) + math.log(Nk), atol=1e-13)

@@ -13,7 +13,8 @@ Prints ONE JSON line. Besides the headline it carries:
                 committed rocprofv3 counter summary, or null if that kernel's source changed since
   cpu_baseline  the float64 CPU oracle timed on the host cores over a bounded sample of heads
   workloads     forward-only TFLOPS of the other bf16 workloads and the fp32 workload's latency
-  extras_fp16   the same kernels on fp16 storage: the long causal forward and the fwd+bwd step
+  extras        the same kernels on fp16 storage (the long causal forward and the fwd+bwd step) and
+                the key-split decoding step (one query against 8192 keys, HBM-bound: GB/s)
 """
 from __future__ import annotations
 
@@ -108,6 +109,35 @@ def time_forward(name, reps, warmup, dev, to_dev, wl=None):
     nbytes = wl.B * wl.H * (4 * wl.N * wl.d * (4 if wl.dtype == "fp32" else 2) + 4 * wl.N)
     return {"workload": name, "pass": "fwd", "reps": reps, "us": round(us, 2), "tflops": round(tf, 1),
             "pct_of_peak": round(100 * tf / peak, 2), "gbps_algorithmic": round(nbytes / (us * 1e-6) / 1e9, 1)}
+
+
+def time_decode(B, H, Nk, d, reps, dev):
+    """Key-split forward of one query per (batch, head) against Nk keys (auto split count): the
+    HBM-bound decoding step. Algorithmic bytes: K and V once, plus Q, O and LSE."""
+    import torch
+
+    from io_aware_flashattention_flash_amd import flash_attn_fwd_kvsplit, flash_attn_fwd_kvsplit_workspace_size, inputs
+
+    q = torch.from_numpy(inputs.random_tensor((B, H, 1, d), 31)).to(dev).to(torch.bfloat16)
+    k = torch.from_numpy(inputs.random_tensor((B, H, Nk, d), 32)).to(dev).to(torch.bfloat16)
+    v = torch.from_numpy(inputs.random_tensor((B, H, Nk, d), 33)).to(dev).to(torch.bfloat16)
+    o = torch.empty_like(q)
+    lse = torch.empty(B, H, 1, device=dev)
+    ws = torch.empty(flash_attn_fwd_kvsplit_workspace_size(B, H, 1, Nk, d, 0, 1), dtype=torch.uint8, device=dev)
+    for _ in range(10):
+        flash_attn_fwd_kvsplit(q, k, v, None, False, 0, out=o, lse=lse, workspace=ws)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(reps):
+        flash_attn_fwd_kvsplit(q, k, v, None, False, 0, out=o, lse=lse, workspace=ws)
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) / reps * 1e3
+    nbytes = B * H * (2 * Nk * d * 2 + 2 * d * 2 + 4)
+    return {"workload": f"decode_bf16_b{B}h{H}nq1nk{Nk}d{d}", "pass": "fwd (key-split + merge)", "reps": reps,
+            "us": round(us, 2), "gbps_algorithmic": round(nbytes / (us * 1e-6) / 1e9, 1),
+            "pct_of_hbm_peak": round(100 * nbytes / (us * 1e-6) / 8e12, 2)}
 
 
 def time_fwdbwd(w, x, steps, warmup, dev, to_dev):
@@ -238,6 +268,7 @@ def main():
                                 "kernels_us": {n: round(t * 1e3, 2) for n, t in km.items()}}
             else:
                 extras[name] = time_forward(name, None, 10, dev, to_dev, wl=wl)
+        extras["decode_bf16_b8h32nq1nk8192d128"] = time_decode(8, 32, 8192, 128, 200, dev)
         torch.cuda.empty_cache()
 
     # ------------------------------------------------------------------ CPU oracle baseline
@@ -287,7 +318,7 @@ def main():
         "cpu_baseline": cpu,
         "kernels": kernels,
         "workloads": workloads,
-        "extras_fp16": extras,
+        "extras": extras,
         "device": {"name": props.name, "arch": getattr(props, "gcnArchName", ""), "cus": props.multi_processor_count},
     }
     print(json.dumps(out))

@@ -36,8 +36,8 @@
  *              error status has launched nothing and written nothing.
  *   Errors     The library never aborts and never prints. Launch failures are
  *              reported as FA_ERR_HIP.
- *   Support    bf16: d in {64, 128}, forward and backward.
- *              fp16 (IEEE binary16): d in {64, 128}, forward and backward.
+ *   Support    bf16: d in {64, 128}, forward (also key-split) and backward.
+ *              fp16 (IEEE binary16): d in {64, 128}, forward (also key-split) and backward.
  *              fp32: d in {64, 128}, forward only.
  *              B, H, N >= 1, B*H*N*d < 2^31 elements per tensor and
  *              N*d < 2^29 (one head is addressed with 32-bit byte offsets).
@@ -54,7 +54,8 @@ extern "C" {
 typedef enum {
   FA_OK = 0,
   FA_ERR_NULL_POINTER = 1, /* a required pointer is NULL */
-  FA_ERR_BAD_SHAPE = 2,    /* B, H, N or d < 1, a tensor exceeds 2^31 elements, or N*d >= 2^29 */
+  FA_ERR_BAD_SHAPE = 2,    /* B, H, N or d < 1, a tensor exceeds 2^31 elements, N*d >= 2^29,
+                              or (key-split forward) Nq > Nk or num_splits outside 0..64 */
   FA_ERR_UNSUPPORTED = 3,  /* (dtype, d, pass) outside the support matrix */
   FA_ERR_BAD_SCALE = 4,    /* scale is NaN or infinite */
   FA_ERR_MISALIGNED = 5,   /* a pointer is not 16-byte aligned */
@@ -79,6 +80,32 @@ typedef enum { FA_DTYPE_FP32 = 0, FA_DTYPE_BF16 = 1, FA_DTYPE_FP16 = 2 } fa_dtyp
 fa_status_t flash_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
                            int B, int H, int N, int d, float scale, int causal,
                            int dtype, void* stream);
+
+/*
+ * Forward of Nq queries against Nk >= Nq keys (decoding one or a few new
+ * positions against a long key/value history, or a chunk of a longer
+ * sequence), with the key range split across workgroups.
+ *   q, o     [B,H,Nq,d] of `dtype` (bf16 or fp16); lse [B,H,Nq] float32 or NULL.
+ *   k, v     [B,H,Nk,d] of `dtype`.
+ *   causal   query i is position Nk - Nq + i of the key sequence and sees keys
+ *            j <= Nk - Nq + i (with Nq == Nk this is flash_attn_fwd's mask).
+ *   num_splits  0 = as many as give every compute unit two workgroups; else
+ *            1..64. Each split covers a contiguous run of 64-key tiles.
+ * Each split writes its rows' partial softmax (O_s normalised within the
+ * split, LSE_s) in float32 to the workspace; a second kernel merges them with
+ * the rule the online softmax uses for consecutive blocks (52jiny.com
+ * FlashAttention explainer, "key ideas" part 2; codechina.net article,
+ * section 4.2): LSE = ln sum_s exp(LSE_s), O = sum_s exp(LSE_s - LSE) O_s.
+ * O and LSE equal those of the plain softmax over all Nk keys.
+ * workspace: device scratch of at least flash_attn_fwd_kvsplit_workspace_size()
+ * bytes for the same shape and num_splits (16-byte aligned); its contents on
+ * entry are ignored. Deterministic.
+ */
+size_t flash_attn_fwd_kvsplit_workspace_size(int B, int H, int Nq, int Nk, int d, int num_splits, int dtype);
+fa_status_t flash_attn_fwd_kvsplit(const void* q, const void* k, const void* v, void* o, float* lse,
+                                   int B, int H, int Nq, int Nk, int d, float scale, int causal,
+                                   int num_splits, void* workspace, size_t workspace_bytes,
+                                   int dtype, void* stream);
 
 /*
  * Bytes of device workspace flash_attn_bwd needs for this shape (the per-row

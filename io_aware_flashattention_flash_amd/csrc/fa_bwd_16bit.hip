@@ -479,19 +479,6 @@ BwdParams<E> make_params(const void* q, const void* k, const void* v, const void
   return prm;
 }
 
-// Compute units of the current device (cached per device; a benign race writes the same value).
-static int num_cus() {
-  static int cache[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cache[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cache[dev] = n;
-  }
-  return cache[dev];
-}
-
 template <typename E, int D>
 hipError_t delta_d(BwdParams<E> prm, hipStream_t stream) {
   constexpr int RPB = 256 / (D / 8) * 4;  // rows per block (4 per thread group)
@@ -512,7 +499,7 @@ template <typename E, int D, bool CAUSAL>
 hipError_t dq_d(BwdParams<E> prm, hipStream_t stream) {
   prm.n_tiles = (prm.N + 32 * kDqNW - 1) / (32 * kDqNW);
   // Pair causal tiles when there are at least four workgroups per CU to begin with.
-  prm.n_units = (CAUSAL && (long)prm.n_tiles * prm.nh >= 4L * num_cus()) ? (prm.n_tiles + 1) / 2 : prm.n_tiles;
+  prm.n_units = (CAUSAL && (long)prm.n_tiles * prm.nh >= 4L * device_cu_count()) ? (prm.n_tiles + 1) / 2 : prm.n_tiles;
   hipLaunchKernelGGL((bwd_dq_kernel<E, D, dq_bc<D>(), kDqNW, CAUSAL>), dim3(prm.n_units * prm.nh), dim3(kDqNW * 64), 0,
                      stream, prm);
   return hipGetLastError();

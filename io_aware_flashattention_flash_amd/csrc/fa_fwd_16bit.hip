@@ -74,11 +74,19 @@ struct Fwd16Params {
   const E* v;
   E* o;
   float* lse;
-  int N;
+  int N;           // query rows (Q, O, LSE)
   int nh;
   int n_qt;
   float c;        // |scale| * log2(e) (a tiny positive value when scale == 0)
   uint32_t qsign;  // 0x80008000 to negate Q (negative scale; the sign bit of both 16-bit types), else 0
+  // Key-split launches only (KV_SPLIT): key rows, the causal offset of query row 0 (query i sees
+  // keys j <= i + key_offset), K/V tiles per split, and the fp32 partials
+  // opart [split][head][row][D] and lsepart [split][head][row].
+  int Nk;
+  int key_offset;
+  int tiles_per_split;
+  float* opart;
+  float* lsepart;
 };
 
 // A block's per-lane probability sum above this bound means some probability may have left the
@@ -89,7 +97,10 @@ template <typename E>
 constexpr float kOverflowSum = std::is_same<E, f16>::value ? 32768.0f : 65536.0f;
 constexpr float kInitMax = -1e30f;
 
-template <typename E, int D, int BC, int NW, bool CAUSAL>
+// KV_SPLIT: this workgroup covers only the K/V tiles of split blockIdx.y and writes its rows'
+// partial (O, LSE) in fp32 (rows with no visible key in the split: O = 0, LSE = -inf); a merge
+// kernel combines the splits. Otherwise Q and K/V have the same length and O, LSE are final.
+template <typename E, int D, int BC, int NW, bool CAUSAL, bool KV_SPLIT>
 __global__ __launch_bounds__(NW * 64, 2) void fwd16_kernel(Fwd16Params<E> p) {
   using H = Half16<E>;
   using e16x8 = typename H::x8;
@@ -113,13 +124,16 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd16_kernel(Fwd16Params<E> p) {
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l = tid & 63, lq = l & 31, hf = l >> 5;
-  const int N = p.N;
+  const int N = p.N;                         // query rows
+  const int Nk = KV_SPLIT ? p.Nk : p.N;      // key rows
+  const int koff = KV_SPLIT ? p.key_offset : 0;
 
   int head, qt;
   map_workgroup(blockIdx.x, p.n_qt, p.nh, CAUSAL ? Order::kLongestFirst : Order::kHeadMajor, true, head, qt);
   const size_t base = (size_t)head * N * D;
-  const E* Kh = p.k + base;
-  const E* Vh = p.v + base;
+  const size_t kbase = (size_t)head * Nk * D;
+  const E* Kh = p.k + kbase;
+  const E* Vh = p.v + kbase;
   const int head_bytes = N * D * 2;
   const int q_w0 = qt * BR + 32 * w;
   const int q = q_w0 + lq;
@@ -135,8 +149,23 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd16_kernel(Fwd16Params<E> p) {
       qreg[kk] = __builtin_bit_cast(e16x8, t);
     }
   }
-  int n_kv = (N + BC - 1) / BC;
-  if (CAUSAL) n_kv = min(n_kv, (min(N, (qt + 1) * BR) - 1) / BC + 1);
+  int n_kv = (Nk + BC - 1) / BC;
+  if (CAUSAL) n_kv = min(n_kv, (min(N, (qt + 1) * BR) - 1 + koff) / BC + 1);
+  // K/V tiles [jb, je) of this workgroup; keys at or beyond key_end are masked.
+  int jb = 0, je = n_kv;
+  if (KV_SPLIT) {
+    jb = blockIdx.y * p.tiles_per_split;
+    je = min(n_kv, jb + p.tiles_per_split);
+    if (jb >= je) {  // no visible key in this split: empty partials (uniform over the workgroup)
+      if (q < N) {
+        const size_t row = ((size_t)blockIdx.y * p.nh + head) * N + q;
+        if (hf == 0) p.lsepart[row] = -INFINITY;
+        for (int c4 = 4 * hf; c4 < D; c4 += 8) *reinterpret_cast<f32x4*>(p.opart + row * D + c4) = f32x4{};
+      }
+      return;
+    }
+  }
+  const int key_end = KV_SPLIT ? min(Nk, je * BC) : Nk;
 
   // Byte offsets (within a tile) of the 16-byte chunks this lane deposits: DMA instruction i of
   // wave w fills LDS chunk positions (w + NW*i)*64 + lane, i.e. swizzled (row, chunk) slots.
@@ -150,8 +179,8 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd16_kernel(Fwd16Params<E> p) {
   }
   auto dma = [&](const E* src, int j, char* dst) __attribute__((always_inline)) {
     const int key0 = j * BC;
-    const int rows = __builtin_amdgcn_readfirstlane(max(0, min(BC, N - key0)));
-    const __amdgpu_buffer_rsrc_t r = make_rsrc(src + (size_t)min(key0, N) * D, rows * (D * 2));
+    const int rows = __builtin_amdgcn_readfirstlane(max(0, min(BC, Nk - key0)));
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(src + (size_t)min(key0, Nk) * D, rows * (D * 2));
 #pragma unroll
     for (int i = 0; i < NLD; ++i) buf_load16_to_lds(r, dst + (w + NW * i) * 1024, goff[i]);
   };
@@ -160,7 +189,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd16_kernel(Fwd16Params<E> p) {
   const int g16 = l >> 4, j16 = l & 15;
   const int v_row_lane = 4 * hf + (j16 >> 2);
   const int v_col_lane = 16 * (g16 & 1) + 4 * (j16 & 3);
-  const int key_lim = CAUSAL ? min(q, N - 1) : N - 1;
+  const int key_lim = CAUSAL ? min(q + koff, key_end - 1) : key_end - 1;
 
   f32x16 acc_o[NDB];
 #pragma unroll
@@ -178,7 +207,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd16_kernel(Fwd16Params<E> p) {
   // Causal / ragged mask of the 32-key half `h` of tile j (only where it can bite).
   auto mask_half = [&](f32x16& s, int j, int h) __attribute__((always_inline)) {
     const int key0 = j * BC + 32 * h;
-    if ((key0 + 32 > N) || (CAUSAL && key0 + 31 > q_w0)) {
+    if ((key0 + 32 > key_end) || (CAUSAL && key0 + 31 > q_w0 + koff)) {
       const int lim = key_lim - key0 - 4 * hf;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -325,26 +354,28 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd16_kernel(Fwd16Params<E> p) {
   // follows phase A(j), the last reader of K(j) and V(j-1), and are awaited one tile later. The
   // tile count is padded to even; a padded tile is fully masked (its probabilities are zero) and
   // its V rows are real data or zeros, so it leaves O and l unchanged.
-  const int n_eff = (n_kv + 1) & ~1;
-  dma(Kh, 0, sk0);
-  dma(Vh, 0, sv0);
-  if (n_kv > 1) dma(Kh, 1, sk1);
+  const int n_t = je - jb;
+  const int n_eff = (n_t + 1) & ~1;
+  dma(Kh, jb, sk0);
+  dma(Vh, jb, sv0);
+  if (n_t > 1) dma(Kh, jb + 1, sk1);
   wait_vmem();
   __syncthreads();
   s_half(s0, sk0, 0);
-  phase_a(0, sk0, sv1, no{});
+  phase_a(jb, sk0, sv1, no{});
 #pragma unroll 1
-  for (int j = 0; j < n_eff; j += 2) {
+  for (int t = 0; t < n_eff; t += 2) {
+    const int j = jb + t;
     wait_vmem();
     __syncthreads();
-    if (j + 2 < n_kv) dma(Kh, j + 2, sk0);
+    if (t + 2 < n_t) dma(Kh, j + 2, sk0);
     dma(Vh, j + 1, sv1);
     phase_b(j, sk1, sv0);
     phase_a(j + 1, sk1, sv0, yes{});
     wait_vmem();
     __syncthreads();
-    if (j + 3 < n_kv) dma(Kh, j + 3, sk1);
-    if (j + 2 < n_eff) dma(Vh, j + 2, sv0);
+    if (t + 3 < n_t) dma(Kh, j + 3, sk1);
+    if (t + 2 < n_eff) dma(Vh, j + 2, sv0);
     phase_b(j + 1, sk0, sv1);
     phase_a(j + 2, sk0, sv1, yes{});
   }
@@ -354,6 +385,30 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd16_kernel(Fwd16Params<E> p) {
   // by 16 bytes) and written back as whole rows of 16-byte chunks. Rows >= N fall outside the
   // buffer descriptors and are dropped.
   const float l_tot = half_swap_sum(l_run);
+  if (KV_SPLIT) {
+    // fp32 partial: O_s = O_acc / l~ and LSE_s; a row with no visible key in this split (l~ = 0)
+    // gets O_s = 0, LSE_s = -inf, so the merge gives it no weight. Lane (q, hf) holds columns
+    // 32*db + 8*g + 4*hf .. +3 of row q.
+    const float lr = half_swap_sum(lr_run);
+    const bool empty = lr == 0.f;
+    const float inv = empty ? 0.f : 1.0f / lr;
+    const size_t row0 = ((size_t)blockIdx.y * p.nh + head) * N;
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(p.opart + row0 * D, N * D * 4);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        f32x4 t;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) t[e] = acc_o[db][4 * g + e] * inv;
+        buf_store16(ro, (q * D + 32 * db + 8 * g + 4 * hf) * 4, __builtin_bit_cast(u32x4, t));
+      }
+    if (hf == 0) {
+      const __amdgpu_buffer_rsrc_t rl = make_rsrc(p.lsepart + row0, N * 4);
+      buf_store4(rl, q * 4, empty ? -INFINITY : (m_run + __log2f(l_tot)) * kLn2);
+    }
+    return;
+  }
   const float inv = 1.0f / half_swap_sum(lr_run);
   __syncthreads();  // every wave is done reading the last K/V tiles
   char* ostage = w == 0 ? sk0 : (w == 1 ? sv0 : (w == 2 ? sk1 : sv1));
@@ -364,16 +419,17 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd16_kernel(Fwd16Params<E> p) {
   }
 }
 
-template <typename E, int D, int BC, int NW, bool CAUSAL>
-static hipError_t launch_cfg(const Fwd16Params<E>& prm, hipStream_t stream) {
-  const int grid = prm.n_qt * prm.nh;
-  hipLaunchKernelGGL((fwd16_kernel<E, D, BC, NW, CAUSAL>), dim3(grid), dim3(NW * 64), 0, stream, prm);
+template <typename E, int D, int BC, int NW, bool CAUSAL, bool KV_SPLIT>
+static hipError_t launch_cfg(const Fwd16Params<E>& prm, int n_splits, hipStream_t stream) {
+  hipLaunchKernelGGL((fwd16_kernel<E, D, BC, NW, CAUSAL, KV_SPLIT>), dim3(prm.n_qt * prm.nh, n_splits), dim3(NW * 64),
+                     0, stream, prm);
   return hipGetLastError();
 }
 
-template <typename E>
+template <typename E, bool KV_SPLIT>
 static hipError_t launch_typed(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int N,
-                               int d, float scale, bool causal, hipStream_t stream) {
+                               int Nk, int d, float scale, bool causal, int n_splits, int tiles_per_split,
+                               float* opart, float* lsepart, hipStream_t stream) {
   constexpr int NW = 4, BR = 32 * NW;
   Fwd16Params<E> prm;
   prm.q = static_cast<const E*>(q);
@@ -389,15 +445,87 @@ static hipError_t launch_typed(const void* q, const void* k, const void* v, void
   // exactly the uniform softmax a zero scale means, and masked scores still map to -inf.
   prm.c = scale == 0.f ? 1e-30f : fabsf(scale) * kLog2e;
   prm.qsign = scale < 0.f ? 0x80008000u : 0u;
-  if (d == 64) return causal ? launch_cfg<E, 64, 64, NW, true>(prm, stream) : launch_cfg<E, 64, 64, NW, false>(prm, stream);
-  if (d == 128) return causal ? launch_cfg<E, 128, 64, NW, true>(prm, stream) : launch_cfg<E, 128, 64, NW, false>(prm, stream);
+  prm.Nk = Nk;
+  prm.key_offset = Nk - N;
+  prm.tiles_per_split = tiles_per_split;
+  prm.opart = opart;
+  prm.lsepart = lsepart;
+  if (d == 64)
+    return causal ? launch_cfg<E, 64, 64, NW, true, KV_SPLIT>(prm, n_splits, stream)
+                  : launch_cfg<E, 64, 64, NW, false, KV_SPLIT>(prm, n_splits, stream);
+  if (d == 128)
+    return causal ? launch_cfg<E, 128, 64, NW, true, KV_SPLIT>(prm, n_splits, stream)
+                  : launch_cfg<E, 128, 64, NW, false, KV_SPLIT>(prm, n_splits, stream);
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_fwd_16(bool fp16, const void* q, const void* k, const void* v, void* o, float* lse, int BH, int N,
                          int d, float scale, bool causal, hipStream_t stream) {
-  return fp16 ? launch_typed<f16>(q, k, v, o, lse, BH, N, d, scale, causal, stream)
-              : launch_typed<bf16>(q, k, v, o, lse, BH, N, d, scale, causal, stream);
+  return fp16 ? launch_typed<f16, false>(q, k, v, o, lse, BH, N, N, d, scale, causal, 1, 0, nullptr, nullptr, stream)
+              : launch_typed<bf16, false>(q, k, v, o, lse, BH, N, N, d, scale, causal, 1, 0, nullptr, nullptr, stream);
+}
+
+// ---------------------------------------------------------------------------------------------
+// Key-split forward: partials per split, then a merge.
+// ---------------------------------------------------------------------------------------------
+// One wave per query row: LSE = ln sum_s exp(LSE_s), O = sum_s exp(LSE_s - LSE) O_s (the same
+// combination rule the online softmax applies to consecutive blocks, here across splits).
+template <typename E, int D>
+__global__ __launch_bounds__(256) void kvsplit_merge_kernel(const float* opart, const float* lsepart, E* o,
+                                                            float* lse, int rows, int n_splits) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int l = threadIdx.x & 63;
+  if (row >= rows) return;
+  const float ls = l < n_splits ? lsepart[(size_t)l * rows + row] : -INFINITY;
+  float mx = ls;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  // every row sees at least one key, so mx is finite (or NaN from NaN inputs, which propagates)
+  float wgt = l < n_splits ? __expf(ls - mx) : 0.f;
+  float sum = wgt;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off);
+  wgt /= sum;
+  constexpr int CPL = D / 64;  // columns per lane
+  float acc[CPL];
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) acc[c] = 0.f;
+  for (int sp = 0; sp < n_splits; ++sp) {
+    const float ws = __shfl(wgt, sp);
+    const float* src = opart + ((size_t)sp * rows + row) * D;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) acc[c] += ws * src[l + 64 * c];
+  }
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) o[(size_t)row * D + l + 64 * c] = (E)acc[c];
+  if (l == 0 && lse) lse[row] = mx + __logf(sum);
+}
+
+template <typename E>
+static hipError_t launch_split_typed(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int N,
+                                     int Nk, int d, float scale, bool causal, int n_splits, int tiles_per_split,
+                                     float* opart, float* lsepart, hipStream_t stream) {
+  hipError_t e = launch_typed<E, true>(q, k, v, o, lse, BH, N, Nk, d, scale, causal, n_splits, tiles_per_split, opart,
+                                       lsepart, stream);
+  if (e != hipSuccess) return e;
+  const int rows = BH * N;
+  const dim3 grid((rows + 3) / 4);
+  if (d == 64)
+    hipLaunchKernelGGL((kvsplit_merge_kernel<E, 64>), grid, dim3(256), 0, stream, opart, lsepart, static_cast<E*>(o),
+                       lse, rows, n_splits);
+  else
+    hipLaunchKernelGGL((kvsplit_merge_kernel<E, 128>), grid, dim3(256), 0, stream, opart, lsepart, static_cast<E*>(o),
+                       lse, rows, n_splits);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_16_kvsplit(bool fp16, const void* q, const void* k, const void* v, void* o, float* lse, int BH,
+                                 int N, int Nk, int d, float scale, bool causal, int n_splits, int tiles_per_split,
+                                 float* opart, float* lsepart, hipStream_t stream) {
+  return fp16 ? launch_split_typed<f16>(q, k, v, o, lse, BH, N, Nk, d, scale, causal, n_splits, tiles_per_split, opart,
+                                        lsepart, stream)
+              : launch_split_typed<bf16>(q, k, v, o, lse, BH, N, Nk, d, scale, causal, n_splits, tiles_per_split,
+                                         opart, lsepart, stream);
 }
 
 }  // namespace fa

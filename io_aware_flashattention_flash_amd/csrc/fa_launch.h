@@ -9,6 +9,17 @@ namespace fa {
 hipError_t launch_fwd_16(bool fp16, const void* q, const void* k, const void* v, void* o, float* lse,
                          int BH, int N, int d, float scale, bool causal, hipStream_t stream);
 
+// Key-split forward (Nq = N query rows against Nk >= N key rows; causal: query i sees keys
+// j <= i + Nk - N). The K/V tiles are dealt to n_splits groups of tiles_per_split tiles; each group's
+// fp32 partial (O, LSE) goes to opart [n_splits][BH][N][d] / lsepart [n_splits][BH][N], then a
+// merge kernel writes O and LSE.
+hipError_t launch_fwd_16_kvsplit(bool fp16, const void* q, const void* k, const void* v, void* o, float* lse,
+                                 int BH, int N, int Nk, int d, float scale, bool causal, int n_splits,
+                                 int tiles_per_split, float* opart, float* lsepart, hipStream_t stream);
+
+// Compute units of the current device (cached per device).
+int device_cu_count();
+
 // Forward, fp32 storage. d in {64, 128}.
 hipError_t launch_fwd_fp32(const void* q, const void* k, const void* v, void* o, float* lse,
                            int BH, int N, int d, float scale, bool causal, hipStream_t stream);

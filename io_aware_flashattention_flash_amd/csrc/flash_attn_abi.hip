@@ -26,6 +26,56 @@ bool is_16bit(int dtype) { return dtype == FA_DTYPE_BF16 || dtype == FA_DTYPE_FP
 
 }  // namespace
 
+namespace fa {
+// Compute units of the current device (cached per device; a benign race writes the same value).
+int device_cu_count() {
+  static int cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+}  // namespace fa
+
+namespace {
+constexpr int kMaxSplits = 64;
+constexpr int kQueryTile = 128;  // query rows per workgroup of the forward kernels
+constexpr int kKeyTile = 64;     // keys per K/V tile
+
+// Split plan of the key-split forward: `requested` splits (0 = enough to give every CU two
+// workgroups), each covering a whole number of K/V tiles. Returns the number of splits used.
+int kvsplit_plan(int BH, int Nq, int Nk, int requested, int* tiles_per_split) {
+  const int n_qt = (Nq + kQueryTile - 1) / kQueryTile;
+  const int n_tiles = (Nk + kKeyTile - 1) / kKeyTile;
+  int s = requested;
+  if (s == 0) {
+    const long want = 2L * fa::device_cu_count();
+    const long have = (long)n_qt * BH;
+    s = (int)((want + have - 1) / have);
+  }
+  s = s < 1 ? 1 : (s > kMaxSplits ? kMaxSplits : s);
+  if (s > n_tiles) s = n_tiles;
+  const int tps = (n_tiles + s - 1) / s;
+  *tiles_per_split = tps;
+  return (n_tiles + tps - 1) / tps;
+}
+
+size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+fa_status_t check_kvsplit_shape(int B, int H, int Nq, int Nk, int d, int num_splits) {
+  fa_status_t st = check_shape(B, H, Nq, d);
+  if (st != FA_OK) return st;
+  st = check_shape(B, H, Nk, d);
+  if (st != FA_OK) return st;
+  if (Nq > Nk || num_splits < 0 || num_splits > kMaxSplits) return FA_ERR_BAD_SHAPE;
+  return FA_OK;
+}
+}  // namespace
+
 extern "C" {
 
 fa_status_t flash_attn_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
@@ -41,6 +91,38 @@ fa_status_t flash_attn_fwd(const void* q, const void* k, const void* v, void* o,
   hipError_t e = is_16bit(dtype)
                      ? fa::launch_fwd_16(dtype == FA_DTYPE_FP16, q, k, v, o, lse, B * H, N, d, scale, causal != 0, s)
                      : fa::launch_fwd_fp32(q, k, v, o, lse, B * H, N, d, scale, causal != 0, s);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+size_t flash_attn_fwd_kvsplit_workspace_size(int B, int H, int Nq, int Nk, int d, int num_splits, int dtype) {
+  (void)dtype;
+  if (check_kvsplit_shape(B, H, Nq, Nk, d, num_splits) != FA_OK) return 0;
+  int tps = 0;
+  const int s = num_splits == 0 ? kvsplit_plan(B * H, Nq, Nk, 0, &tps) : num_splits;
+  const size_t rows = (size_t)s * B * H * Nq;
+  return round256(rows * d * sizeof(float)) + round256(rows * sizeof(float));
+}
+
+fa_status_t flash_attn_fwd_kvsplit(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                                   int Nq, int Nk, int d, float scale, int causal, int num_splits, void* workspace,
+                                   size_t workspace_bytes, int dtype, void* stream) {
+  if (!q || !k || !v || !o) return FA_ERR_NULL_POINTER;
+  fa_status_t st = check_kvsplit_shape(B, H, Nq, Nk, d, num_splits);
+  if (st != FA_OK) return st;
+  if (!is_16bit(dtype) || !supported_d(d)) return FA_ERR_UNSUPPORTED;
+  if (!isfinite(scale)) return FA_ERR_BAD_SCALE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || (lse && !aligned4(lse)))
+    return FA_ERR_MISALIGNED;
+  if (!workspace || workspace_bytes < flash_attn_fwd_kvsplit_workspace_size(B, H, Nq, Nk, d, num_splits, dtype))
+    return FA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return FA_ERR_MISALIGNED;
+  int tps = 0;
+  const int s = kvsplit_plan(B * H, Nq, Nk, num_splits, &tps);
+  const size_t rows = (size_t)s * B * H * Nq;
+  float* opart = static_cast<float*>(workspace);
+  float* lsepart = reinterpret_cast<float*>(static_cast<char*>(workspace) + round256(rows * d * sizeof(float)));
+  hipError_t e = fa::launch_fwd_16_kvsplit(dtype == FA_DTYPE_FP16, q, k, v, o, lse, B * H, Nq, Nk, d, scale,
+                                           causal != 0, s, tps, opart, lsepart, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

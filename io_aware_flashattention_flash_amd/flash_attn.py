@@ -36,6 +36,9 @@ SIGNATURES = {
                                    _int, _int, _int, _int, _float, _int, _int, _vp]),
     "flash_attn_bwd_dq": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                  _int, _int, _int, _int, _float, _int, _int, _vp]),
+    "flash_attn_fwd_kvsplit_workspace_size": (_size, [_int, _int, _int, _int, _int, _int, _int]),
+    "flash_attn_fwd_kvsplit": (_int, [_vp, _vp, _vp, _vp, _vp, _int, _int, _int, _int, _int, _float, _int, _int,
+                                      _vp, _size, _int, _vp]),
     "flash_attn_status_string": (ctypes.c_char_p, [_int]),
 }
 
@@ -111,6 +114,46 @@ def flash_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: Opt
         raise ValueError("lse must be a contiguous float32 [B, H, N] tensor on q's device")
     st = load_library().flash_attn_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, d, scale,
                                        int(bool(causal)), _DTYPES[q.dtype], _stream_handle(q))
+    _check(st)
+    return out, lse
+
+
+def flash_attn_fwd_kvsplit_workspace_size(B: int, H: int, Nq: int, Nk: int, d: int, num_splits: int = 0,
+                                          dtype: int = FA_DTYPE_BF16) -> int:
+    return int(load_library().flash_attn_fwd_kvsplit_workspace_size(B, H, Nq, Nk, d, num_splits, dtype))
+
+
+def flash_attn_fwd_kvsplit(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: Optional[float] = None,
+                           causal: bool = False, num_splits: int = 0, out: Optional[torch.Tensor] = None,
+                           lse: Optional[torch.Tensor] = None, want_lse: bool = True,
+                           workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Attention of q [B, H, Nq, d] against k, v [B, H, Nk, d] with Nq <= Nk (decode / chunked
+    prefill), the key range split across workgroups and the partial softmaxes merged. Causal
+    aligns the queries with the last Nq key positions."""
+    _check_tensor("q", q)
+    _check_tensor("k", k)
+    _check_tensor("v", v, k)
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    if k.shape[0] != B or k.shape[1] != H or k.shape[3] != d or k.dtype != q.dtype or k.device != q.device:
+        raise ValueError("k and v must be [B, H, Nk, d] with q's B, H, d, dtype and device")
+    scale = float(d) ** -0.5 if scale is None else float(scale)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check_tensor("out", out, q)
+    if lse is None and want_lse:
+        lse = torch.empty((B, H, Nq), dtype=torch.float32, device=q.device)
+    if lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, Nq) or not lse.is_contiguous()
+                            or lse.device != q.device):
+        raise ValueError("lse must be a contiguous float32 [B, H, Nq] tensor on q's device")
+    dt = _DTYPES[q.dtype]
+    need = flash_attn_fwd_kvsplit_workspace_size(B, H, Nq, Nk, d, num_splits, dt)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    st = load_library().flash_attn_fwd_kvsplit(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Nq, Nk, d,
+                                               scale, int(bool(causal)), int(num_splits), _ptr(workspace),
+                                               workspace.numel() * workspace.element_size(), dt, _stream_handle(q))
     _check(st)
     return out, lse
 

@@ -164,6 +164,36 @@ def _dq(lib, **kw):
                                  a["H"], a["N"], a["d"], a["scale"], a["causal"], a["dtype"], None)
 
 
+def _kvs(lib, q=A, k=A, v=A, o=A, lse=A, B=1, H=1, Nq=1, Nk=8, d=64, scale=0.125, causal=0, splits=0, ws=A,
+         ws_bytes=1 << 20, dtype=1):
+    return lib.flash_attn_fwd_kvsplit(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, splits, ws, ws_bytes, dtype,
+                                      None)
+
+
+def test_kvsplit_validation(lib):
+    assert _kvs(lib, q=None) == NULLP
+    assert _kvs(lib, Nq=9, Nk=8) == SHAPE          # more queries than keys
+    assert _kvs(lib, splits=65) == SHAPE
+    assert _kvs(lib, splits=-1) == SHAPE
+    assert _kvs(lib, Nq=0) == SHAPE
+    assert _kvs(lib, dtype=0) == UNSUP              # 16-bit types only
+    assert _kvs(lib, d=96) == UNSUP
+    assert _kvs(lib, scale=math.inf) == SCALE
+    assert _kvs(lib, k=A + 8) == ALIGN
+    assert _kvs(lib, ws=None) == WS
+    assert _kvs(lib, ws_bytes=16) == WS
+    assert _kvs(lib, ws=A + 4) == ALIGN
+    assert _kvs(lib, dtype=2, v=A + 2) == ALIGN      # fp16 gets past the dtype check
+
+
+def test_kvsplit_workspace_size(lib):
+    assert lib.flash_attn_fwd_kvsplit_workspace_size(1, 1, 9, 8, 64, 0, 1) == 0      # Nq > Nk
+    one = lib.flash_attn_fwd_kvsplit_workspace_size(2, 4, 3, 1000, 128, 1, 1)
+    four = lib.flash_attn_fwd_kvsplit_workspace_size(2, 4, 3, 1000, 128, 4, 1)
+    assert one >= 2 * 4 * 3 * 129 * 4 and four >= 4 * 2 * 4 * 3 * 129 * 4 and four > one
+    assert one < 2 * 4 * 3 * 1000 * 4  # linear in Nq, independent of Nk: no score matrix
+
+
 def test_fp16_passes_the_dtype_check(lib):
     """dtype 2 (fp16) is in the support matrix of every entry point: its calls get past the dtype
     check to the later ones (these fake pointers never reach a launch)."""

@@ -18,6 +18,7 @@ import glob
 import hashlib
 import json
 import os
+import re
 from collections import defaultdict
 
 CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
@@ -34,10 +35,36 @@ def source_digest(kernel: str) -> str:
     return h.hexdigest()[:16]
 
 
+_TEMPLATE_ARG = re.compile(r"DF16b|DF16_|Li(-?\d+)E|Lb([01])E")
+
+
+def readable_name(name: str) -> str:
+    """This library's kernel names as `fa::kernel<args>`. The profiler reports some template
+    instances undemangled (the bf16 / fp16 element types); their Itanium-mangled form
+    _ZN2fa<len><name>I<args>E... is rendered here for the handful of argument kinds the
+    kernels use (16-bit float types, int and bool constants)."""
+    short = name.replace("void ", "").split("(")[0]
+    m = re.match(r"_ZN2fa(\d+)", short)
+    if not m:
+        return short
+    n = int(m.group(1))
+    start = m.end()
+    fn = short[start:start + n]
+    rest = short[start + n:]
+    if not rest.startswith("I"):
+        return f"fa::{fn}"
+    args = []
+    for a in _TEMPLATE_ARG.finditer(rest[1:rest.index("EE") + 1] if "EE" in rest else rest[1:]):
+        tok = a.group(0)
+        args.append("bf16" if tok == "DF16b" else "f16" if tok == "DF16_" else
+                    a.group(1) if a.group(1) is not None else ("true" if a.group(2) == "1" else "false"))
+    return f"fa::{fn}<{', '.join(args)}>"
+
+
 def kernel_key(name: str):
-    short = name.replace("void ", "")
+    short = readable_name(name)
     for key, prefix in KERNEL_PREFIX.items():
-        if short.startswith(prefix):
+        if short.startswith(prefix + "<"):
             return key
     return None
 
@@ -64,9 +91,9 @@ def trace(stats_csv: str, out_md: str, command: str, title: str) -> str:
     lines = [f"# {title}", "", "Command (run from the repository root on one MI355X):", "", "```", command, "```", "",
              "| kernel | calls | avg µs | min µs | max µs | share of GPU time |", "|---|---|---|---|---|---|"]
     for r in rows:
-        if "fa::" not in r["Name"]:
+        short = readable_name(r["Name"])
+        if not short.startswith("fa::"):
             continue
-        short = r["Name"].replace("void ", "").split("(")[0]
         lines.append(f"| `{short}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
                      f"{float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.2f}% |")
     text = "\n".join(lines) + "\n"

@@ -1,0 +1,20 @@
+"""CPU tests of the profiler-output helpers (kernel naming and classification)."""
+from io_aware_flashattention_flash_amd.profiling import kernel_key, readable_name
+
+
+def test_mangled_and_demangled_names_classify_alike():
+    cases = {
+        "_ZN2fa12fwd16_kernelIDF16bLi128ELi64ELi4ELb1ELb0EEEvNS_11Fwd16ParamsIT_EE":
+            ("fa::fwd16_kernel<bf16, 128, 64, 4, true, false>", "fwd"),
+        "_ZN2fa13bwd_dq_kernelIDF16_Li64ELi64ELi4ELb1EEEvNS_9BwdParamsIT_EE":
+            ("fa::bwd_dq_kernel<f16, 64, 64, 4, true>", "bwd_dq"),
+        "_ZN2fa15bwd_dkdv_kernelIDF16bLi64ELi4ELi64ELb0EEEvNS_9BwdParamsIT_EE":
+            ("fa::bwd_dkdv_kernel<bf16, 64, 4, 64, false>", "bwd_dkdv"),
+        "void fa::fwd_fp32_kernel<64, false>(fa::FwdF32Params)": ("fa::fwd_fp32_kernel<64, false>", None),
+        "_ZN2fa20kvsplit_merge_kernelIDF16bLi128EEEvPKfS2_PT_Pfii": ("fa::kvsplit_merge_kernel<bf16, 128>", None),
+        "__amd_rocclr_copyBuffer": ("__amd_rocclr_copyBuffer", None),
+    }
+    for raw, (pretty, key) in cases.items():
+        assert readable_name(raw) == pretty
+        assert kernel_key(raw) == key
+    assert kernel_key("void fa::fwd16_kernel<__bf16, 64, 64, 4, true, false>(fa::Fwd16Params<__bf16>)") == "fwd"

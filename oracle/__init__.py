@@ -13,13 +13,18 @@ Contents:
                 shapes (an independent second statement of the forward).
   online.py     the blocked online-softmax recurrence, step by step, used only
                 to show that the recurrence the fused kernel runs is exact.
+  masked.py     the same definition under a general boolean visibility mask, with builders
+                for padded variable-length batches, per-sequence key/value cache lengths and
+                block-sparse maps (empty rows: O = 0, LSE = -inf).
 
 Every function cites the passage of the pages it follows. Parity pins (closed
 forms, invariants, brute force, library special cases, finite differences)
-live in tests/test_oracle.py.
+live in tests/test_oracle.py and tests/test_oracle_masked.py.
 """
 from .attention import attn_bwd, attn_fwd, attn_fwd_kv, attn_fwd_rows, softmax_rows
 from .brute import brute_fwd
+from .masked import attn_bwd_masked, attn_fwd_masked, kv_cache_visible, padded_batch_visible
 from .online import online_fwd
 
-__all__ = ["attn_fwd", "attn_fwd_kv", "attn_fwd_rows", "attn_bwd", "softmax_rows", "brute_fwd", "online_fwd"]
+__all__ = ["attn_fwd", "attn_fwd_kv", "attn_fwd_rows", "attn_bwd", "softmax_rows", "brute_fwd", "online_fwd",
+           "attn_fwd_masked", "attn_bwd_masked", "padded_batch_visible", "kv_cache_visible"]

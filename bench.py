@@ -140,6 +140,51 @@ def time_decode(B, H, Nk, d, reps, dev):
             "pct_of_hbm_peak": round(100 * nbytes / (us * 1e-6) / 8e12, 2)}
 
 
+def time_masked_forward(kind, B, H, N, d, dev, reps=100):
+    """Forward under a mask: "blocksparse" (causal; a seeded map enabling about half of the 128 x 128
+    blocks, diagonal blocks always on) or "varlen" (causal; seeded lengths uniform in [N/4, N]).
+    TFLOPS counts 4 d flops per visible (query, key) pair only."""
+    import numpy as np
+    import torch
+
+    from io_aware_flashattention_flash_amd import flash_attn_fwd_masked, inputs
+
+    q, k, v = (torch.from_numpy(inputs.random_tensor((B, H, N, d), 41 + i)).to(dev).to(torch.bfloat16)
+               for i in range(3))
+    rng = np.random.default_rng(43)
+    nb = -(-N // 128)
+    sl = bm = None
+    if kind == "blocksparse":
+        bmap = (rng.random((B, H, nb, nb)) < 0.5).astype(np.uint8)
+        bmap[:, :, np.arange(nb), np.arange(nb)] = 1
+        # visible pairs: enabled blocks on or below the diagonal, causal inside diagonal blocks
+        rows = np.minimum(128, N - 128 * np.arange(nb))  # rows (= keys) per block
+        diag = np.array([r * (r + 1) // 2 for r in rows])
+        below = np.tril(np.ones((nb, nb), dtype=bool), -1)
+        pairs = int(np.einsum("bhrc,r,c->", ((bmap != 0) & below).astype(np.int64), rows, rows) + B * H * diag.sum())
+        bm = torch.from_numpy(bmap).to(dev)
+    else:
+        lens = rng.integers(N // 4, N + 1, size=B).astype(np.int32)
+        pairs = int(H * sum(int(L) * (int(L) + 1) // 2 for L in lens))
+        sl = torch.from_numpy(lens).to(dev)
+    o = torch.empty_like(q)
+    lse = torch.empty(B, H, N, device=dev)
+    for _ in range(10):
+        flash_attn_fwd_masked(q, k, v, None, True, seqlens=sl, block_mask=bm, out=o, lse=lse)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(reps):
+        flash_attn_fwd_masked(q, k, v, None, True, seqlens=sl, block_mask=bm, out=o, lse=lse)
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) / reps * 1e3
+    tf = 4.0 * d * pairs / (us * 1e-6) / 1e12
+    return {"workload": f"fwd_bf16_b{B}h{H}n{N}d{d}_causal_{kind}", "pass": "fwd (masked)", "reps": reps,
+            "us": round(us, 2), "visible_pairs": pairs, "tflops_visible": round(tf, 1),
+            "pct_of_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2)}
+
+
 def time_fwdbwd(w, x, steps, warmup, dev, to_dev):
     """One step = forward, dQ (with delta), dK/dV on resident inputs of a 16-bit workload. Returns
     (ms per step over `steps` timed steps, {stage: average ms}) from HIP events on the stream."""
@@ -269,6 +314,9 @@ def main():
             else:
                 extras[name] = time_forward(name, None, 10, dev, to_dev, wl=wl)
         extras["decode_bf16_b8h32nq1nk8192d128"] = time_decode(8, 32, 8192, 128, 200, dev)
+        for kind, shape in (("blocksparse", (2, 32, 4096, 128)), ("varlen", (8, 16, 4096, 128))):
+            r = time_masked_forward(kind, *shape, dev)
+            extras[r["workload"]] = r
         torch.cuda.empty_cache()
 
     # ------------------------------------------------------------------ CPU oracle baseline

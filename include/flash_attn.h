@@ -36,9 +36,10 @@
  *              error status has launched nothing and written nothing.
  *   Errors     The library never aborts and never prints. Launch failures are
  *              reported as FA_ERR_HIP.
- *   Support    bf16: d in {64, 128}, forward (also key-split) and backward.
- *              fp16 (IEEE binary16): d in {64, 128}, forward (also key-split) and backward.
- *              fp32: d in {64, 128}, forward only.
+ *   Support    bf16: d in {64, 128}, forward (also key-split and masked) and
+ *              backward (also masked).
+ *              fp16 (IEEE binary16): the same as bf16.
+ *              fp32: d in {64, 128}, forward only (no masks).
  *              B, H, N >= 1, B*H*N*d < 2^31 elements per tensor and
  *              N*d < 2^29 (one head is addressed with 32-bit byte offsets).
  */
@@ -46,6 +47,7 @@
 #define FLASH_ATTN_H_
 
 #include <stddef.h>
+#include <stdint.h>
 
 #ifdef __cplusplus
 extern "C" {
@@ -56,14 +58,20 @@ typedef enum {
   FA_ERR_NULL_POINTER = 1, /* a required pointer is NULL */
   FA_ERR_BAD_SHAPE = 2,    /* B, H, N or d < 1, a tensor exceeds 2^31 elements, N*d >= 2^29,
                               or (key-split forward) Nq > Nk or num_splits outside 0..64 */
-  FA_ERR_UNSUPPORTED = 3,  /* (dtype, d, pass) outside the support matrix */
+  FA_ERR_UNSUPPORTED = 3,  /* (dtype, d, pass) outside the support matrix, or a block map with
+                              more than FA_MAX_MASK_BLOCKS blocks per row */
   FA_ERR_BAD_SCALE = 4,    /* scale is NaN or infinite */
-  FA_ERR_MISALIGNED = 5,   /* a pointer is not 16-byte aligned */
+  FA_ERR_MISALIGNED = 5,   /* a pointer is not 16-byte aligned (lse, seqlens: 4-byte) */
   FA_ERR_WORKSPACE = 6,    /* workspace NULL or smaller than flash_attn_bwd_workspace_size() */
   FA_ERR_HIP = 7           /* the HIP runtime reported an error at launch */
 } fa_status_t;
 
 typedef enum { FA_DTYPE_FP32 = 0, FA_DTYPE_BF16 = 1, FA_DTYPE_FP16 = 2 } fa_dtype_t;
+
+/* Block-sparse maps: one byte per FA_MASK_BLOCK x FA_MASK_BLOCK block of scores, at most
+ * FA_MAX_MASK_BLOCKS blocks per row (N <= 131072 with a map). */
+#define FA_MASK_BLOCK 128
+#define FA_MAX_MASK_BLOCKS 1024
 
 /*
  * Forward: O = softmax(scale * Q K^T [+ causal mask]) V and LSE.
@@ -82,6 +90,24 @@ fa_status_t flash_attn_fwd(const void* q, const void* k, const void* v, void* o,
                            int dtype, void* stream);
 
 /*
+ * Forward under padding and block-sparse masks (the mask step of 52jiny.com FlashAttention
+ * explainer, "why standard attention is IO-bound"; sparse attention as named in yunthe.com
+ * "FlashAttention explained", section 5, and codechina.net article, section 7.2).
+ *   seqlens     int32 [B] on the device, or NULL: sequence b occupies rows 0 .. L_b - 1 of Q, K
+ *               and V; the rest is padding. Values are clamped to [0, N] (not checked on the host).
+ *   block_mask  uint8 [B,H,ceil(N/128),ceil(N/128)] on the device, or NULL: entry (r, c) == 0
+ *               removes scores of query rows 128r .. 128r+127 against keys 128c .. 128c+127;
+ *               whole blocks are skipped, never loaded.
+ * Query i sees key j iff i < L_b, j < L_b, (not causal or j <= i) and the block of (i, j) is
+ * enabled. A row that sees no key (padding rows included) gets O = 0 and LSE = -inf. bf16 and fp16;
+ * other arguments as flash_attn_fwd. Deterministic.
+ */
+fa_status_t flash_attn_fwd_masked(const void* q, const void* k, const void* v, void* o, float* lse,
+                                  int B, int H, int N, int d, float scale, int causal,
+                                  const int32_t* seqlens, const uint8_t* block_mask,
+                                  int dtype, void* stream);
+
+/*
  * Forward of Nq queries against Nk >= Nq keys (decoding one or a few new
  * positions against a long key/value history, or a chunk of a longer
  * sequence), with the key range split across workgroups.
@@ -89,6 +115,10 @@ fa_status_t flash_attn_fwd(const void* q, const void* k, const void* v, void* o,
  *   k, v     [B,H,Nk,d] of `dtype`.
  *   causal   query i is position Nk - Nq + i of the key sequence and sees keys
  *            j <= Nk - Nq + i (with Nq == Nk this is flash_attn_fwd's mask).
+ *   seqlens_k  int32 [B] on the device, or NULL: sequence b's cache holds L_b <= Nk valid
+ *            keys (rows L_b .. Nk-1 of K and V are ignored); its queries are positions
+ *            L_b - Nq .. L_b - 1, so with causal query i sees keys j <= L_b - Nq + i. A query
+ *            that sees no key gets O = 0 and LSE = -inf. Values are clamped to [0, Nk].
  *   num_splits  0 = as many as give every compute unit two workgroups; else
  *            1..64. Each split covers a contiguous run of 64-key tiles.
  * Each split writes its rows' partial softmax (O_s normalised within the
@@ -104,8 +134,8 @@ fa_status_t flash_attn_fwd(const void* q, const void* k, const void* v, void* o,
 size_t flash_attn_fwd_kvsplit_workspace_size(int B, int H, int Nq, int Nk, int d, int num_splits, int dtype);
 fa_status_t flash_attn_fwd_kvsplit(const void* q, const void* k, const void* v, void* o, float* lse,
                                    int B, int H, int Nq, int Nk, int d, float scale, int causal,
-                                   int num_splits, void* workspace, size_t workspace_bytes,
-                                   int dtype, void* stream);
+                                   const int32_t* seqlens_k, int num_splits, void* workspace,
+                                   size_t workspace_bytes, int dtype, void* stream);
 
 /*
  * Bytes of device workspace flash_attn_bwd needs for this shape (the per-row
@@ -135,6 +165,19 @@ fa_status_t flash_attn_bwd(const void* q, const void* k, const void* v, const vo
                            void* workspace, size_t workspace_bytes,
                            int B, int H, int N, int d, float scale, int causal,
                            int dtype, void* stream);
+
+/*
+ * Backward of flash_attn_fwd_masked (same seqlens and block_mask; o and lse from that call).
+ * Rows that see no key contribute nothing; dQ rows of such queries and dK, dV rows of keys that
+ * no query sees are 0 (padding rows included). Workspace and other arguments as flash_attn_bwd.
+ */
+fa_status_t flash_attn_bwd_masked(const void* q, const void* k, const void* v, const void* o,
+                                  const float* lse, const void* dout,
+                                  void* dq, void* dk, void* dv,
+                                  void* workspace, size_t workspace_bytes,
+                                  int B, int H, int N, int d, float scale, int causal,
+                                  const int32_t* seqlens, const uint8_t* block_mask,
+                                  int dtype, void* stream);
 
 /*
  * Backward stages, exposed so a caller can run (or time) them separately. Same

@@ -48,7 +48,36 @@ struct BwdParams {
   int n_units;  // workgroups per head (dQ: n_tiles, or (n_tiles + 1) / 2 when causal tiles are paired)
   float c;      // scale * log2(e)
   float scale;
+  // Masked launches only: per-sequence valid rows (sequence = head / heads; clamped to [0, N]) and
+  // the block-sparse map [head][n_mb][n_mb] (one byte per 128 x 128 block; zero = skipped), or null.
+  const int* seqlens;
+  const uint8_t* block_mask;
+  int heads;
+  int n_mb;
 };
+
+// Valid rows of this head's sequence.
+template <bool MASKED, typename P>
+__device__ __forceinline__ int valid_rows(const P& p, int head) {
+  return (MASKED && p.seqlens) ? min(max(p.seqlens[head / p.heads], 0), p.N) : p.N;
+}
+
+// Compacts the enabled entries among map[0], map[stride], ..., map[(n - 1) * stride] (n <= the list
+// size) into `list` in increasing order and returns their count (wave-uniform). Every wave counts;
+// wave 0 writes. The caller synchronises the workgroup before reading the list.
+__device__ __forceinline__ int build_block_list(const uint8_t* map, size_t stride, int n, short* list, int wave,
+                                                int lane) {
+  int cnt = 0;
+  for (int b0 = 0; b0 < n; b0 += 64) {
+    const int b = b0 + lane;
+    const bool on = b < n && map[(size_t)b * stride] != 0;
+    const uint64_t bal = __builtin_amdgcn_ballot_w64(on);
+    if (wave == 0 && on)
+      list[cnt + __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0))] = b;
+    cnt += __builtin_popcountll(bal);
+  }
+  return cnt;
+}
 
 // ---------------------------------------------------------------------------------------------
 // 1. delta = rowsum(dO * O)
@@ -90,7 +119,9 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdParams<E> p) {
 // ---------------------------------------------------------------------------------------------
 // 2. dK, dV (key-outer)
 // ---------------------------------------------------------------------------------------------
-template <typename E, int D, int NW, int BQ, bool CAUSAL>
+// MASKED: padding rows (>= the sequence's length) and, with a block-sparse map, only the query
+// blocks enabled in this key tile's map column; keys no query sees get dK = dV = 0.
+template <typename E, int D, int NW, int BQ, bool CAUSAL, bool MASKED>
 __global__ __launch_bounds__(NW * 64, (D > 64 ? 1 : 2)) void bwd_dkdv_kernel(BwdParams<E> p) {
   using H = Half16<E>;
   using e16x8 = typename H::x8;
@@ -101,6 +132,7 @@ __global__ __launch_bounds__(NW * 64, (D > 64 ? 1 : 2)) void bwd_dkdv_kernel(Bwd
   static_assert(NLD * 64 * NW == BQ * NCH, "tile must split evenly over the workgroup's waves");
   static_assert(BQ == 64, "wave 0 stages one LSE / delta row per lane");
   static_assert(BKV % BQ == 0, "key tiles start on query-tile boundaries");
+  static_assert(!MASKED || BKV == kMaskBlock, "a key tile is one column of the block map");
   constexpr int NKK = D / 16, NDB = D / 32, NQB = BQ / 32;
   using T = SwizzledTile<D>;
 
@@ -110,6 +142,7 @@ __global__ __launch_bounds__(NW * 64, (D > 64 ? 1 : 2)) void bwd_dkdv_kernel(Bwd
   __shared__ __attribute__((aligned(16))) char so1[TILE_BYTES];
   __shared__ __attribute__((aligned(16))) float sr0[2 * BQ];  // [lse * log2(e) | delta] of the tile's rows
   __shared__ __attribute__((aligned(16))) float sr1[2 * BQ];
+  __shared__ short blist[MASKED ? kMaxMaskBlocks : 1];  // enabled query blocks of this key tile
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -122,12 +155,13 @@ __global__ __launch_bounds__(NW * 64, (D > 64 ? 1 : 2)) void bwd_dkdv_kernel(Bwd
   const int head_bytes = N * D * 2;
   const int key_w0 = kt * BKV + 32 * w;
   const int key = key_w0 + lq;
+  const int Lb = valid_rows<MASKED>(p, head);  // rows >= Lb of every input read as zero
 
-  // K^T and V^T operands (B side of S = Q K^T and dP = dO V^T): lane (key, hf); keys >= N read 0.
+  // K^T and V^T operands (B side of S = Q K^T and dP = dO V^T): lane (key, hf); keys >= Lb read 0.
   e16x8 kreg[NKK], vreg[NKK];
   {
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k + base, head_bytes);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + base, head_bytes);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k + base, Lb * (D * 2));
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + base, Lb * (D * 2));
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
       const int off = key * (D * 2) + (16 * kk + 8 * hf) * 2;
@@ -143,8 +177,27 @@ __global__ __launch_bounds__(NW * 64, (D > 64 ? 1 : 2)) void bwd_dkdv_kernel(Bwd
     dv[db] = f32x16{};
   }
 
-  const int n_qt = (N + BQ - 1) / BQ;
+  const int n_qt = (Lb + BQ - 1) / BQ;
   const int qt0 = CAUSAL ? (kt * BKV) / BQ : 0;
+  // Loop positions u = 0 .. n_t - 1 map to query tiles tile(u): qt0 + u, or with a block map the
+  // tile pairs of the enabled 128-row blocks (causal: from the diagonal block on).
+  constexpr int TPB = kMaskBlock / BQ;
+  int n_t = n_qt - qt0;
+  if (MASKED && kt * BKV >= Lb) n_t = 0;  // padding keys only
+  const bool sparse = MASKED && p.block_mask != nullptr;
+  int n_diag = CAUSAL ? BKV / BQ : 0;     // leading positions that meet the diagonal
+  if (sparse && n_t > 0) {
+    const int cnt = build_block_list(p.block_mask + (size_t)head * p.n_mb * p.n_mb + (size_t)(CAUSAL ? kt : 0) * p.n_mb + kt,
+                                     p.n_mb, (n_qt + TPB - 1) / TPB - (CAUSAL ? kt : 0), blist, w, l);
+    __syncthreads();
+    n_t = TPB * cnt;
+    // list entries are relative to the first block scanned (the diagonal one when causal)
+    if (CAUSAL && (cnt == 0 || __builtin_amdgcn_readfirstlane(blist[0]) != 0)) n_diag = 0;
+  }
+  auto tile = [&](int u) __attribute__((always_inline)) -> int {
+    if (!sparse) return qt0 + u;
+    return qt0 + TPB * __builtin_amdgcn_readfirstlane(blist[u / TPB]) + u % TPB;
+  };
 
   int goff[NLD];
 #pragma unroll
@@ -153,14 +206,14 @@ __global__ __launch_bounds__(NW * 64, (D > 64 ? 1 : 2)) void bwd_dkdv_kernel(Bwd
     const int row = pos / NCH, pc = pos % NCH;
     goff[i] = row * (D * 2) + ((pc ^ T::swz(row)) * 16);
   }
-  const __amdgpu_buffer_rsrc_t rlse = make_rsrc(p.lse + rbase, N * 4);
-  const __amdgpu_buffer_rsrc_t rdel = make_rsrc(p.delta + rbase, N * 4);
+  const __amdgpu_buffer_rsrc_t rlse = make_rsrc(p.lse + rbase, Lb * 4);
+  const __amdgpu_buffer_rsrc_t rdel = make_rsrc(p.delta + rbase, Lb * 4);
   float st_l = 0.f, st_d = 0.f;  // wave 0: this tile's row statistics, staged in registers
   auto dma = [&](int i, char* qb, char* ob) __attribute__((always_inline)) {
     const int row0 = i * BQ;
-    const int bytes = min(BQ, N - row0) * (D * 2);
-    const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + base + (size_t)row0 * D, bytes);
-    const __amdgpu_buffer_rsrc_t ro = make_rsrc(p.dout + base + (size_t)row0 * D, bytes);
+    const int bytes = max(0, min(BQ, Lb - row0)) * (D * 2);
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + base + (size_t)min(row0, Lb) * D, bytes);
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(p.dout + base + (size_t)min(row0, Lb) * D, bytes);
 #pragma unroll
     for (int t = 0; t < NLD; ++t) {
       buf_load16_to_lds(rq, qb + (w + NW * t) * 1024, goff[t]);
@@ -233,32 +286,38 @@ __global__ __launch_bounds__(NW * 64, (D > 64 ? 1 : 2)) void bwd_dkdv_kernel(Bwd
   // Ping-pong over two LDS buffers: query tile i+1 streams in while tile i is computed. A causal
   // key tile's first BKV / BQ query tiles meet its diagonal; they run first, in their own loop, so
   // the steady-state loop body holds only the unmasked path.
-  constexpr int NDIAG = CAUSAL ? BKV / BQ : 0;
-  static_assert(NDIAG % 2 == 0, "the diagonal section must keep the buffer parity");
-  auto pair = [&](auto diag_tag, int i) __attribute__((always_inline)) {
-    if (i + 1 < n_qt) dma(i + 1, sq1, so1);
-    compute(diag_tag, i, sq0, so0, sr0);
+  static_assert((BKV / BQ) % 2 == 0, "the diagonal section must keep the buffer parity");
+  auto pair = [&](auto diag_tag, int u) __attribute__((always_inline)) {
+    if (u + 1 < n_t) dma(tile(u + 1), sq1, so1);
+    compute(diag_tag, tile(u), sq0, so0, sr0);
     wait_vmem();
     stage_rows(sr1);
     __syncthreads();
-    if (i + 1 < n_qt) {
-      if (i + 2 < n_qt) dma(i + 2, sq0, so0);
-      compute(diag_tag, i + 1, sq1, so1, sr1);
+    if (u + 1 < n_t) {
+      if (u + 2 < n_t) dma(tile(u + 2), sq0, so0);
+      compute(diag_tag, tile(u + 1), sq1, so1, sr1);
       wait_vmem();
       stage_rows(sr0);
       __syncthreads();
     }
   };
-  if (qt0 < n_qt) {
-    dma(qt0, sq0, so0);
+  if (n_t > 0) {
+    dma(tile(0), sq0, so0);
     stage_rows(sr0);
     wait_vmem();
     __syncthreads();
-    int i = qt0;
+    int u = 0;
 #pragma unroll 1
-    for (; i < qt0 + NDIAG && i < n_qt; i += 2) pair(std::true_type{}, i);
+    for (; u < n_diag && u < n_t; u += 2) pair(std::true_type{}, u);
 #pragma unroll 1
-    for (; i < n_qt; i += 2) pair(std::false_type{}, i);
+    for (; u < n_t; u += 2) pair(std::false_type{}, u);
+  }
+  if (MASKED && key >= Lb) {  // padding keys (their K, V read as zero but queries still saw them)
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      dk[db] = f32x16{};
+      dv[db] = f32x16{};
+    }
   }
 
   // dK = scale * dK^T^T and dV, written as whole rows through this wave's idle tile buffer.
@@ -271,7 +330,9 @@ __global__ __launch_bounds__(NW * 64, (D > 64 ? 1 : 2)) void bwd_dkdv_kernel(Bwd
 // ---------------------------------------------------------------------------------------------
 // 3. dQ (query-outer)
 // ---------------------------------------------------------------------------------------------
-template <typename E, int D, int BC, int NW, bool CAUSAL>
+// MASKED: padding rows and, with a block-sparse map, only the key blocks enabled in this query
+// tile's map row; every tile takes the masked path.
+template <typename E, int D, int BC, int NW, bool CAUSAL, bool MASKED>
 __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdParams<E> p) {
   using H = Half16<E>;
   using e16x8 = typename H::x8;
@@ -283,11 +344,13 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdParams<E> p) {
   static_assert(NLD * 64 * NW == BC * NCH, "tile must split evenly over the workgroup's waves");
   constexpr int NKB = BC / 32, NDB = D / 32, NKK = D / 16, NKS = BC / 16;
   using T = SwizzledTile<D>;
+  static_assert(!MASKED || BR == kMaskBlock, "a query tile is one row of the block map");
 
   __shared__ __attribute__((aligned(16))) char sk0[TILE_BYTES];
   __shared__ __attribute__((aligned(16))) char sv0[TILE_BYTES];
   __shared__ __attribute__((aligned(16))) char sk1[TILE_BYTES];
   __shared__ __attribute__((aligned(16))) char sv1[TILE_BYTES];
+  __shared__ short blist[MASKED ? kMaxMaskBlocks : 1];  // enabled key blocks of this query tile
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -302,6 +365,7 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdParams<E> p) {
   map_workgroup(blockIdx.x, p.n_units, p.nh, paired ? Order::kHeadMajor : (CAUSAL ? Order::kLongestFirst : Order::kHeadMajor),
                 !paired, head, unit);
   const int n_items = (paired && p.n_tiles - 1 - unit != unit) ? 2 : 1;
+  const int Lb = valid_rows<MASKED>(p, head);  // rows >= Lb of every input read as zero
 #pragma unroll 1
   for (int item = 0; item < n_items; ++item) {
   const int qt = (paired && item == 0) ? p.n_tiles - 1 - unit : unit;
@@ -319,9 +383,9 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdParams<E> p) {
   e16x8 qreg[NKK], oreg[NKK];
   float lse2, dlt;
   {
-    const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + base, head_bytes);
-    const __amdgpu_buffer_rsrc_t rdo = make_rsrc(p.dout + base, head_bytes);
-    const __amdgpu_buffer_rsrc_t rof = make_rsrc(p.o + base, head_bytes);
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + base, Lb * (D * 2));
+    const __amdgpu_buffer_rsrc_t rdo = make_rsrc(p.dout + base, Lb * (D * 2));
+    const __amdgpu_buffer_rsrc_t rof = make_rsrc(p.o + base, Lb * (D * 2));
     float part = 0.f;
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
@@ -333,12 +397,28 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdParams<E> p) {
       for (int e = 0; e < 8; ++e) part = fmaf((float)oreg[kk][e], (float)ov[e], part);
     }
     dlt = half_swap_sum(part);
-    lse2 = buf_load4f(make_rsrc(p.lse + rbase, N * 4), q * 4) * kLog2e;
+    lse2 = buf_load4f(make_rsrc(p.lse + rbase, Lb * 4), q * 4) * kLog2e;
     if (hf == 0) buf_store4(make_rsrc(p.delta + rbase, N * 4), q * 4, dlt);
   }
 
-  int n_kv = (N + BC - 1) / BC;
-  if (CAUSAL) n_kv = min(n_kv, (min(N, (qt + 1) * BR) - 1) / BC + 1);
+  int n_kv = (Lb + BC - 1) / BC;
+  if (CAUSAL) n_kv = min(n_kv, (min(Lb, (qt + 1) * BR) - 1) / BC + 1);
+  if (MASKED && qt * BR >= Lb) n_kv = 0;  // padding rows only: dQ = 0
+  // Loop positions u = 0 .. n_t - 1 map to key tiles tile(u): u, or with a block map the tiles of
+  // the enabled 128-key blocks.
+  constexpr int TPB = kMaskBlock / BC;
+  int n_t = n_kv;
+  const bool sparse = MASKED && p.block_mask != nullptr;
+  if (sparse && n_t > 0) {
+    const int cnt = build_block_list(p.block_mask + ((size_t)head * p.n_mb + qt) * p.n_mb, 1, (n_kv + TPB - 1) / TPB,
+                                     blist, w, l);
+    __syncthreads();
+    n_t = TPB * cnt;
+  }
+  auto tile = [&](int u) __attribute__((always_inline)) -> int {
+    if (!sparse) return u;
+    return TPB * __builtin_amdgcn_readfirstlane(blist[u / TPB]) + u % TPB;
+  };
 
   f32x16 dq[NDB];
 #pragma unroll
@@ -353,9 +433,9 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdParams<E> p) {
   }
   auto dma = [&](int j, char* kb, char* vb) __attribute__((always_inline)) {
     const int key0 = j * BC;
-    const int bytes = min(BC, N - key0) * (D * 2);
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k + base + (size_t)key0 * D, bytes);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + base + (size_t)key0 * D, bytes);
+    const int bytes = max(0, min(BC, Lb - key0)) * (D * 2);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k + base + (size_t)min(key0, Lb) * D, bytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + base + (size_t)min(key0, Lb) * D, bytes);
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
       buf_load16_to_lds(rk, kb + (w + NW * i) * 1024, goff[i]);
@@ -366,7 +446,7 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdParams<E> p) {
   const int g16 = l >> 4, j16 = l & 15;
   const int tr_row_lane = 4 * hf + (j16 >> 2);
   const int tr_col_lane = 16 * (g16 & 1) + 4 * (j16 & 3);
-  const int key_lim = CAUSAL ? min(q, N - 1) : N - 1;
+  const int key_lim = CAUSAL ? min(q, Lb - 1) : Lb - 1;
   const float c = p.c;
 
   // One key tile; MASK for diagonal and ragged tiles (compiled separately from the clean path).
@@ -415,28 +495,31 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdParams<E> p) {
   int j_mask = CAUSAL ? (qt * BR) / BC : n_kv;
   if (N % BC != 0) j_mask = min(j_mask, n_kv - 1);
   j_mask = min(j_mask, n_kv);
-  auto pair = [&](auto mask_tag, int j, int j_end) __attribute__((always_inline)) {
-    if (j + 1 < n_kv) dma(j + 1, sk1, sv1);
-    compute(mask_tag, j, sk0, sv0);
+  if (MASKED) j_mask = 0;
+  auto pair = [&](auto mask_tag, int u, int u_end) __attribute__((always_inline)) {
+    if (u + 1 < n_t) dma(tile(u + 1), sk1, sv1);
+    compute(mask_tag, tile(u), sk0, sv0);
     wait_vmem();
     __syncthreads();
-    if (j + 1 < j_end) {
-      if (j + 2 < n_kv) dma(j + 2, sk0, sv0);
-      compute(mask_tag, j + 1, sk1, sv1);
+    if (u + 1 < u_end) {
+      if (u + 2 < n_t) dma(tile(u + 2), sk0, sv0);
+      compute(mask_tag, tile(u + 1), sk1, sv1);
       wait_vmem();
       __syncthreads();
     }
   };
-  dma(0, sk0, sv0);
-  wait_vmem();
-  __syncthreads();
-  int j = 0;
+  if (!MASKED || n_t > 0) {
+    dma(tile(0), sk0, sv0);
+    wait_vmem();
+    __syncthreads();
+    int u = 0;
 #pragma unroll 1
-  for (; j + 1 < j_mask; j += 2) pair(std::false_type{}, j, j_mask);
-  // j is even here. A single clean tile may remain before the masked ones; it is run through the
-  // masked path (its mask is all-pass), which keeps the buffer parity simple.
+    for (; u + 1 < j_mask; u += 2) pair(std::false_type{}, u, j_mask);
+    // u is even here. A single clean tile may remain before the masked ones; it is run through the
+    // masked path (its mask is all-pass), which keeps the buffer parity simple.
 #pragma unroll 1
-  for (; j < n_kv; j += 2) pair(std::true_type{}, j, n_kv);
+    for (; u < n_t; u += 2) pair(std::true_type{}, u, n_t);
+  }
 
   __syncthreads();  // every wave is done reading the last K / V tile
   char* stage = w == 0 ? sk0 : (w == 1 ? sv0 : (w == 2 ? sk1 : sv1));
@@ -476,6 +559,10 @@ BwdParams<E> make_params(const void* q, const void* k, const void* v, const void
   prm.n_units = 0;
   prm.c = scale * kLog2e;
   prm.scale = scale;
+  prm.seqlens = nullptr;
+  prm.block_mask = nullptr;
+  prm.heads = 1;
+  prm.n_mb = (N + kMaskBlock - 1) / kMaskBlock;
   return prm;
 }
 
@@ -487,21 +574,21 @@ hipError_t delta_d(BwdParams<E> prm, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <typename E, int D, bool CAUSAL>
+template <typename E, int D, bool CAUSAL, bool MASKED = false>
 hipError_t dkdv_d(BwdParams<E> prm, hipStream_t stream) {
   prm.n_tiles = (prm.N + 32 * kKvNW - 1) / (32 * kKvNW);
-  hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, kKvNW, kKvBQ, CAUSAL>), dim3(prm.n_tiles * prm.nh), dim3(kKvNW * 64), 0,
-                     stream, prm);
+  hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, kKvNW, kKvBQ, CAUSAL, MASKED>), dim3(prm.n_tiles * prm.nh),
+                     dim3(kKvNW * 64), 0, stream, prm);
   return hipGetLastError();
 }
 
-template <typename E, int D, bool CAUSAL>
+template <typename E, int D, bool CAUSAL, bool MASKED = false>
 hipError_t dq_d(BwdParams<E> prm, hipStream_t stream) {
   prm.n_tiles = (prm.N + 32 * kDqNW - 1) / (32 * kDqNW);
   // Pair causal tiles when there are at least four workgroups per CU to begin with.
   prm.n_units = (CAUSAL && (long)prm.n_tiles * prm.nh >= 4L * device_cu_count()) ? (prm.n_tiles + 1) / 2 : prm.n_tiles;
-  hipLaunchKernelGGL((bwd_dq_kernel<E, D, dq_bc<D>(), kDqNW, CAUSAL>), dim3(prm.n_units * prm.nh), dim3(kDqNW * 64), 0,
-                     stream, prm);
+  hipLaunchKernelGGL((bwd_dq_kernel<E, D, dq_bc<D>(), kDqNW, CAUSAL, MASKED>), dim3(prm.n_units * prm.nh),
+                     dim3(kDqNW * 64), 0, stream, prm);
   return hipGetLastError();
 }
 }  // namespace
@@ -534,7 +621,36 @@ hipError_t dq_typed(const void* q, const void* k, const void* v, const void* o, 
   if (d == 128) return causal ? dq_d<E, 128, true>(prm, stream) : dq_d<E, 128, false>(prm, stream);
   return hipErrorInvalidValue;
 }
+template <typename E>
+hipError_t masked_typed(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
+                        float* delta, void* dq, void* dk, void* dv, int BH, int N, int d, float scale, bool causal,
+                        const Masks& m, hipStream_t stream) {
+  BwdParams<E> prm = make_params<E>(q, k, v, o, lse, dout, delta, dq, dk, dv, BH, N, scale);
+  prm.seqlens = m.seqlens;
+  prm.block_mask = m.block_mask;
+  prm.heads = m.heads;
+  hipError_t e;
+  if (d == 64) {
+    e = causal ? dq_d<E, 64, true, true>(prm, stream) : dq_d<E, 64, false, true>(prm, stream);
+    if (e == hipSuccess) e = causal ? dkdv_d<E, 64, true, true>(prm, stream) : dkdv_d<E, 64, false, true>(prm, stream);
+    return e;
+  }
+  if (d == 128) {
+    e = causal ? dq_d<E, 128, true, true>(prm, stream) : dq_d<E, 128, false, true>(prm, stream);
+    if (e == hipSuccess)
+      e = causal ? dkdv_d<E, 128, true, true>(prm, stream) : dkdv_d<E, 128, false, true>(prm, stream);
+    return e;
+  }
+  return hipErrorInvalidValue;
+}
 }  // namespace
+
+hipError_t launch_bwd_masked(bool fp16, const void* q, const void* k, const void* v, const void* o, const float* lse,
+                             const void* dout, float* delta, void* dq, void* dk, void* dv, int BH, int N, int d,
+                             float scale, bool causal, const Masks& masks, hipStream_t stream) {
+  return fp16 ? masked_typed<f16>(q, k, v, o, lse, dout, delta, dq, dk, dv, BH, N, d, scale, causal, masks, stream)
+              : masked_typed<bf16>(q, k, v, o, lse, dout, delta, dq, dk, dv, BH, N, d, scale, causal, masks, stream);
+}
 
 hipError_t launch_bwd_delta(bool fp16, const void* o, const void* dout, float* delta, int BH, int N, int d,
                             hipStream_t stream) {

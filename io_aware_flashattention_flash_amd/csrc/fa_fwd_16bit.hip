@@ -87,6 +87,14 @@ struct Fwd16Params {
   int tiles_per_split;
   float* opart;
   float* lsepart;
+  // Per-sequence lengths (sequence = head / heads), or null: kMasked, the valid rows of Q and K/V;
+  // kSplit, the valid keys of the cache. Values are clamped to [0, N] (kSplit: [0, Nk]).
+  const int* seqlens;
+  // kMasked only: block-sparse map [head][n_qt][n_kb], one byte per 128 x 128 block of scores
+  // (zero: skipped), or null.
+  const uint8_t* block_mask;
+  int heads;
+  int n_kb;
 };
 
 // A block's per-lane probability sum above this bound means some probability may have left the
@@ -97,11 +105,19 @@ template <typename E>
 constexpr float kOverflowSum = std::is_same<E, f16>::value ? 32768.0f : 65536.0f;
 constexpr float kInitMax = -1e30f;
 
-// KV_SPLIT: this workgroup covers only the K/V tiles of split blockIdx.y and writes its rows'
-// partial (O, LSE) in fp32 (rows with no visible key in the split: O = 0, LSE = -inf); a merge
-// kernel combines the splits. Otherwise Q and K/V have the same length and O, LSE are final.
-template <typename E, int D, int BC, int NW, bool CAUSAL, bool KV_SPLIT>
+// Launch modes.
+//  kDense:  Q and K/V have the same length N; O, LSE are final.
+//  kSplit:  this workgroup covers only the K/V tiles of split blockIdx.y and writes its rows'
+//           partial (O, LSE) in fp32 (rows with no visible key in the split: O = 0, LSE = -inf); a
+//           merge kernel combines the splits. Optional per-sequence cache lengths.
+//  kMasked: square, with optional per-sequence lengths (rows >= L of Q and K/V are padding) and
+//           an optional block-sparse map; the workgroup walks only the key blocks its map row
+//           enables. Rows that see no key get O = 0, LSE = -inf.
+enum FwdMode : int { kDense = 0, kSplit = 1, kMasked = 2 };
+
+template <typename E, int D, int BC, int NW, bool CAUSAL, int MODE>
 __global__ __launch_bounds__(NW * 64, 2) void fwd16_kernel(Fwd16Params<E> p) {
+  constexpr bool KV_SPLIT = MODE == kSplit, MASKED = MODE == kMasked;
   using H = Half16<E>;
   using e16x8 = typename H::x8;
   using e16x4 = typename H::x4;
@@ -115,21 +131,29 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd16_kernel(Fwd16Params<E> p) {
   constexpr int NDB = D / 32;
   constexpr int NKK = D / 16;
   using T = SwizzledTile<D>;
+  static_assert(!MASKED || BR == kMaskBlock, "a query tile is one row of the block map");
 
   __shared__ __attribute__((aligned(16))) char sk0[TILE_BYTES];
   __shared__ __attribute__((aligned(16))) char sv0[TILE_BYTES];
   __shared__ __attribute__((aligned(16))) char sk1[TILE_BYTES];
   __shared__ __attribute__((aligned(16))) char sv1[TILE_BYTES];
+  __shared__ short blist[MASKED ? kMaxMaskBlocks : 1];  // enabled key blocks of this query tile
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l = tid & 63, lq = l & 31, hf = l >> 5;
   const int N = p.N;                         // query rows
   const int Nk = KV_SPLIT ? p.Nk : p.N;      // key rows
-  const int koff = KV_SPLIT ? p.key_offset : 0;
 
   int head, qt;
   map_workgroup(blockIdx.x, p.n_qt, p.nh, CAUSAL ? Order::kLongestFirst : Order::kHeadMajor, true, head, qt);
+  // Valid query rows Lq and keys Lk of this head's sequence.
+  int Lq = N, Lk = Nk;
+  if ((KV_SPLIT || MASKED) && p.seqlens) {
+    Lk = min(max(p.seqlens[head / p.heads], 0), Nk);
+    if (MASKED) Lq = Lk;
+  }
+  const int koff = KV_SPLIT ? Lk - N : 0;  // causal: query i sees keys j <= i + koff
   const size_t base = (size_t)head * N * D;
   const size_t kbase = (size_t)head * Nk * D;
   const E* Kh = p.k + kbase;
@@ -138,10 +162,24 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd16_kernel(Fwd16Params<E> p) {
   const int q_w0 = qt * BR + 32 * w;
   const int q = q_w0 + lq;
 
-  // Q^T operand: lane (q, hf) holds Q[q][16*kk + 8*hf .. +7]; rows >= N read as zero.
+  // Rows of this tile that see no key at all (padding rows, empty map rows): O = 0, LSE = -inf.
+  auto write_empty_rows = [&]() __attribute__((always_inline)) {
+    if (q < N) {
+      const __amdgpu_buffer_rsrc_t ro = make_rsrc(p.o + base, head_bytes);
+#pragma unroll
+      for (int c8 = hf; c8 < D / 8; c8 += 2) buf_store16(ro, (q * D + 8 * c8) * 2, u32x4{0, 0, 0, 0});
+      if (p.lse && hf == 0) p.lse[(size_t)head * N + q] = -INFINITY;
+    }
+  };
+  if (MASKED && qt * BR >= Lq) {  // a tile of padding rows only (uniform over the workgroup)
+    write_empty_rows();
+    return;
+  }
+
+  // Q^T operand: lane (q, hf) holds Q[q][16*kk + 8*hf .. +7]; rows >= Lq read as zero.
   e16x8 qreg[NKK];
   {
-    const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + base, head_bytes);
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + base, Lq * (D * 2));
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
       u32x4 t = buf_load16(rq, q * (D * 2) + (16 * kk + 8 * hf) * 2);
@@ -149,8 +187,11 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd16_kernel(Fwd16Params<E> p) {
       qreg[kk] = __builtin_bit_cast(e16x8, t);
     }
   }
-  int n_kv = (Nk + BC - 1) / BC;
-  if (CAUSAL) n_kv = min(n_kv, (min(N, (qt + 1) * BR) - 1 + koff) / BC + 1);
+  int n_kv = (Lk + BC - 1) / BC;
+  if (CAUSAL) {
+    const int last_key = min(Lq, (qt + 1) * BR) - 1 + koff;  // the last key any row here sees
+    n_kv = min(n_kv, last_key < 0 ? 0 : last_key / BC + 1);
+  }
   // K/V tiles [jb, je) of this workgroup; keys at or beyond key_end are masked.
   int jb = 0, je = n_kv;
   if (KV_SPLIT) {
@@ -165,7 +206,38 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd16_kernel(Fwd16Params<E> p) {
       return;
     }
   }
-  const int key_end = KV_SPLIT ? min(Nk, je * BC) : Nk;
+  const int key_end = KV_SPLIT ? min(Lk, je * BC) : Lk;
+
+  // Block-sparse: compact the enabled 128-key blocks of this tile's map row into blist (the
+  // tile pair of block b is 2b, 2b + 1). Every wave counts; wave 0 writes the list.
+  int n_t = je - jb;
+  const bool sparse = MASKED && p.block_mask != nullptr;
+  if (sparse) {
+    const int nblk = (n_kv + 1) / 2;
+    const uint8_t* mrow = p.block_mask + ((size_t)head * p.n_qt + qt) * p.n_kb;
+    int cnt = 0;
+    for (int b0 = 0; b0 < nblk; b0 += 64) {
+      const int b = b0 + l;
+      const bool on = b < nblk && mrow[b] != 0;
+      const uint64_t bal = __builtin_amdgcn_ballot_w64(on);
+      if (w == 0 && on)
+        blist[cnt + __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0))] = b;
+      cnt += __builtin_popcountll(bal);
+    }
+    __syncthreads();
+    if (cnt == 0) {
+      write_empty_rows();
+      return;
+    }
+    n_t = 2 * cnt;
+  }
+  // Tile index of loop position u. Positions past the end (the pipeline's look-ahead) map to a
+  // tile beyond every key this workgroup can see: fully masked and never loaded.
+  auto tile = [&](int u) __attribute__((always_inline)) -> int {
+    if (!sparse) return jb + u;
+    if (u >= n_t) return n_kv + 2;
+    return 2 * __builtin_amdgcn_readfirstlane(blist[u >> 1]) + (u & 1);
+  };
 
   // Byte offsets (within a tile) of the 16-byte chunks this lane deposits: DMA instruction i of
   // wave w fills LDS chunk positions (w + NW*i)*64 + lane, i.e. swizzled (row, chunk) slots.
@@ -179,8 +251,8 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd16_kernel(Fwd16Params<E> p) {
   }
   auto dma = [&](const E* src, int j, char* dst) __attribute__((always_inline)) {
     const int key0 = j * BC;
-    const int rows = __builtin_amdgcn_readfirstlane(max(0, min(BC, Nk - key0)));
-    const __amdgpu_buffer_rsrc_t r = make_rsrc(src + (size_t)min(key0, Nk) * D, rows * (D * 2));
+    const int rows = __builtin_amdgcn_readfirstlane(max(0, min(BC, Lk - key0)));
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(src + (size_t)min(key0, Lk) * D, rows * (D * 2));
 #pragma unroll
     for (int i = 0; i < NLD; ++i) buf_load16_to_lds(r, dst + (w + NW * i) * 1024, goff[i]);
   };
@@ -354,30 +426,30 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd16_kernel(Fwd16Params<E> p) {
   // follows phase A(j), the last reader of K(j) and V(j-1), and are awaited one tile later. The
   // tile count is padded to even; a padded tile is fully masked (its probabilities are zero) and
   // its V rows are real data or zeros, so it leaves O and l unchanged.
-  const int n_t = je - jb;
   const int n_eff = (n_t + 1) & ~1;
-  dma(Kh, jb, sk0);
-  dma(Vh, jb, sv0);
-  if (n_t > 1) dma(Kh, jb + 1, sk1);
+  const int j_first = tile(0);
+  dma(Kh, j_first, sk0);
+  dma(Vh, j_first, sv0);
+  if (n_t > 1) dma(Kh, tile(1), sk1);
   wait_vmem();
   __syncthreads();
   s_half(s0, sk0, 0);
-  phase_a(jb, sk0, sv1, no{});
+  phase_a(j_first, sk0, sv1, no{});
 #pragma unroll 1
   for (int t = 0; t < n_eff; t += 2) {
-    const int j = jb + t;
+    const int j0 = tile(t), j1 = tile(t + 1), j2 = tile(t + 2);
     wait_vmem();
     __syncthreads();
-    if (t + 2 < n_t) dma(Kh, j + 2, sk0);
-    dma(Vh, j + 1, sv1);
-    phase_b(j, sk1, sv0);
-    phase_a(j + 1, sk1, sv0, yes{});
+    if (t + 2 < n_t) dma(Kh, j2, sk0);
+    dma(Vh, j1, sv1);
+    phase_b(j0, sk1, sv0);
+    phase_a(j1, sk1, sv0, yes{});
     wait_vmem();
     __syncthreads();
-    if (t + 3 < n_t) dma(Kh, j + 3, sk1);
-    if (t + 2 < n_eff) dma(Vh, j + 2, sv0);
-    phase_b(j + 1, sk0, sv1);
-    phase_a(j + 2, sk0, sv1, yes{});
+    if (t + 3 < n_t) dma(Kh, tile(t + 3), sk1);
+    if (t + 2 < n_eff) dma(Vh, j2, sv0);
+    phase_b(j1, sk0, sv1);
+    phase_a(j2, sk0, sv1, yes{});
   }
 
   // Epilogue: O = O_acc / l~, LSE = ln2 * (m + log2 l). The accumulator holds one query row per
@@ -409,27 +481,47 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd16_kernel(Fwd16Params<E> p) {
     }
     return;
   }
-  const float inv = 1.0f / half_swap_sum(lr_run);
+  float inv = 1.0f / half_swap_sum(lr_run);
+  float lse_row = (m_run + __log2f(l_tot)) * kLn2;
+  if (MASKED) {
+    // padding rows, and rows whose visible keys all fell in disabled blocks or the causal mask
+    const bool empty = q >= Lq || half_swap_sum(lr_run) == 0.f;
+    inv = empty ? 0.f : inv;
+    lse_row = empty ? -INFINITY : lse_row;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc_o[db][r] = empty ? 0.f : acc_o[db][r];
+  }
   __syncthreads();  // every wave is done reading the last K/V tiles
   char* ostage = w == 0 ? sk0 : (w == 1 ? sv0 : (w == 2 ? sk1 : sv1));
   store_rows_via_lds<E, D, TILE_BYTES>(ostage, acc_o, inv, make_rsrc(p.o + base, head_bytes), q_w0, l);
   if (p.lse && hf == 0) {
     const __amdgpu_buffer_rsrc_t rl = make_rsrc(p.lse + (size_t)head * N, N * 4);
-    buf_store4(rl, q * 4, (m_run + __log2f(l_tot)) * kLn2);
+    buf_store4(rl, q * 4, lse_row);
   }
 }
 
-template <typename E, int D, int BC, int NW, bool CAUSAL, bool KV_SPLIT>
+template <typename E, int D, int BC, int NW, bool CAUSAL, int MODE>
 static hipError_t launch_cfg(const Fwd16Params<E>& prm, int n_splits, hipStream_t stream) {
-  hipLaunchKernelGGL((fwd16_kernel<E, D, BC, NW, CAUSAL, KV_SPLIT>), dim3(prm.n_qt * prm.nh, n_splits), dim3(NW * 64),
-                     0, stream, prm);
+  hipLaunchKernelGGL((fwd16_kernel<E, D, BC, NW, CAUSAL, MODE>), dim3(prm.n_qt * prm.nh, n_splits), dim3(NW * 64), 0,
+                     stream, prm);
   return hipGetLastError();
 }
 
-template <typename E, bool KV_SPLIT>
-static hipError_t launch_typed(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int N,
-                               int Nk, int d, float scale, bool causal, int n_splits, int tiles_per_split,
-                               float* opart, float* lsepart, hipStream_t stream) {
+// Launch arguments beyond the dense forward's (key-split partials, masks).
+struct FwdExtra {
+  int Nk;
+  int n_splits = 1;
+  int tiles_per_split = 0;
+  float* opart = nullptr;
+  float* lsepart = nullptr;
+  Masks masks;
+};
+
+template <typename E, int MODE>
+static hipError_t launch_typed(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int N, int d,
+                               float scale, bool causal, const FwdExtra& x, hipStream_t stream) {
   constexpr int NW = 4, BR = 32 * NW;
   Fwd16Params<E> prm;
   prm.q = static_cast<const E*>(q);
@@ -445,24 +537,39 @@ static hipError_t launch_typed(const void* q, const void* k, const void* v, void
   // exactly the uniform softmax a zero scale means, and masked scores still map to -inf.
   prm.c = scale == 0.f ? 1e-30f : fabsf(scale) * kLog2e;
   prm.qsign = scale < 0.f ? 0x80008000u : 0u;
-  prm.Nk = Nk;
-  prm.key_offset = Nk - N;
-  prm.tiles_per_split = tiles_per_split;
-  prm.opart = opart;
-  prm.lsepart = lsepart;
+  prm.Nk = x.Nk;
+  prm.key_offset = x.Nk - N;
+  prm.tiles_per_split = x.tiles_per_split;
+  prm.opart = x.opart;
+  prm.lsepart = x.lsepart;
+  prm.seqlens = x.masks.seqlens;
+  prm.block_mask = x.masks.block_mask;
+  prm.heads = x.masks.heads;
+  prm.n_kb = (N + kMaskBlock - 1) / kMaskBlock;
   if (d == 64)
-    return causal ? launch_cfg<E, 64, 64, NW, true, KV_SPLIT>(prm, n_splits, stream)
-                  : launch_cfg<E, 64, 64, NW, false, KV_SPLIT>(prm, n_splits, stream);
+    return causal ? launch_cfg<E, 64, 64, NW, true, MODE>(prm, x.n_splits, stream)
+                  : launch_cfg<E, 64, 64, NW, false, MODE>(prm, x.n_splits, stream);
   if (d == 128)
-    return causal ? launch_cfg<E, 128, 64, NW, true, KV_SPLIT>(prm, n_splits, stream)
-                  : launch_cfg<E, 128, 64, NW, false, KV_SPLIT>(prm, n_splits, stream);
+    return causal ? launch_cfg<E, 128, 64, NW, true, MODE>(prm, x.n_splits, stream)
+                  : launch_cfg<E, 128, 64, NW, false, MODE>(prm, x.n_splits, stream);
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_fwd_16(bool fp16, const void* q, const void* k, const void* v, void* o, float* lse, int BH, int N,
                          int d, float scale, bool causal, hipStream_t stream) {
-  return fp16 ? launch_typed<f16, false>(q, k, v, o, lse, BH, N, N, d, scale, causal, 1, 0, nullptr, nullptr, stream)
-              : launch_typed<bf16, false>(q, k, v, o, lse, BH, N, N, d, scale, causal, 1, 0, nullptr, nullptr, stream);
+  FwdExtra x;
+  x.Nk = N;
+  return fp16 ? launch_typed<f16, kDense>(q, k, v, o, lse, BH, N, d, scale, causal, x, stream)
+              : launch_typed<bf16, kDense>(q, k, v, o, lse, BH, N, d, scale, causal, x, stream);
+}
+
+hipError_t launch_fwd_16_masked(bool fp16, const void* q, const void* k, const void* v, void* o, float* lse, int BH,
+                                int N, int d, float scale, bool causal, const Masks& masks, hipStream_t stream) {
+  FwdExtra x;
+  x.Nk = N;
+  x.masks = masks;
+  return fp16 ? launch_typed<f16, kMasked>(q, k, v, o, lse, BH, N, d, scale, causal, x, stream)
+              : launch_typed<bf16, kMasked>(q, k, v, o, lse, BH, N, d, scale, causal, x, stream);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -480,7 +587,13 @@ __global__ __launch_bounds__(256) void kvsplit_merge_kernel(const float* opart, 
   float mx = ls;
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-  // every row sees at least one key, so mx is finite (or NaN from NaN inputs, which propagates)
+  if (mx == -INFINITY) {  // the row sees no key in any split (cache shorter than its position)
+#pragma unroll
+    for (int c = 0; c < D / 64; ++c) o[(size_t)row * D + l + 64 * c] = (E)0.f;
+    if (l == 0 && lse) lse[row] = -INFINITY;
+    return;
+  }
+  // mx is finite here, or NaN from NaN inputs, which propagates
   float wgt = l < n_splits ? __expf(ls - mx) : 0.f;
   float sum = wgt;
 #pragma unroll
@@ -503,11 +616,12 @@ __global__ __launch_bounds__(256) void kvsplit_merge_kernel(const float* opart, 
 
 template <typename E>
 static hipError_t launch_split_typed(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int N,
-                                     int Nk, int d, float scale, bool causal, int n_splits, int tiles_per_split,
-                                     float* opart, float* lsepart, hipStream_t stream) {
-  hipError_t e = launch_typed<E, true>(q, k, v, o, lse, BH, N, Nk, d, scale, causal, n_splits, tiles_per_split, opart,
-                                       lsepart, stream);
+                                     int d, float scale, bool causal, const FwdExtra& x, hipStream_t stream) {
+  hipError_t e = launch_typed<E, kSplit>(q, k, v, o, lse, BH, N, d, scale, causal, x, stream);
   if (e != hipSuccess) return e;
+  const int n_splits = x.n_splits;
+  float* opart = x.opart;
+  float* lsepart = x.lsepart;
   const int rows = BH * N;
   const dim3 grid((rows + 3) / 4);
   if (d == 64)
@@ -521,11 +635,17 @@ static hipError_t launch_split_typed(const void* q, const void* k, const void* v
 
 hipError_t launch_fwd_16_kvsplit(bool fp16, const void* q, const void* k, const void* v, void* o, float* lse, int BH,
                                  int N, int Nk, int d, float scale, bool causal, int n_splits, int tiles_per_split,
-                                 float* opart, float* lsepart, hipStream_t stream) {
-  return fp16 ? launch_split_typed<f16>(q, k, v, o, lse, BH, N, Nk, d, scale, causal, n_splits, tiles_per_split, opart,
-                                        lsepart, stream)
-              : launch_split_typed<bf16>(q, k, v, o, lse, BH, N, Nk, d, scale, causal, n_splits, tiles_per_split,
-                                         opart, lsepart, stream);
+                                 float* opart, float* lsepart, const int* seqlens_k, int heads, hipStream_t stream) {
+  FwdExtra x;
+  x.Nk = Nk;
+  x.n_splits = n_splits;
+  x.tiles_per_split = tiles_per_split;
+  x.opart = opart;
+  x.lsepart = lsepart;
+  x.masks.seqlens = seqlens_k;
+  x.masks.heads = heads;
+  return fp16 ? launch_split_typed<f16>(q, k, v, o, lse, BH, N, d, scale, causal, x, stream)
+              : launch_split_typed<bf16>(q, k, v, o, lse, BH, N, d, scale, causal, x, stream);
 }
 
 }  // namespace fa

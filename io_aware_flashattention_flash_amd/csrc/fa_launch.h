@@ -2,20 +2,41 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <stdint.h>
 
 namespace fa {
+
+// Block-sparse maps hold one byte per kMaskBlock x kMaskBlock block of scores; a workgroup keeps the
+// list of its enabled blocks in LDS, which bounds the blocks per map row.
+constexpr int kMaskBlock = 128;
+constexpr int kMaxMaskBlocks = 1024;
+
+// Optional masks (device pointers, or null). seqlens: [B] valid length of each sequence
+// (sequence = head / heads). block_mask: [B*H][ceil(N/128)][ceil(N/128)] bytes, zero = skipped.
+struct Masks {
+  const int* seqlens = nullptr;
+  const uint8_t* block_mask = nullptr;
+  int heads = 1;
+};
 
 // Forward, 16-bit storage: bf16 (fp16 = false) or IEEE fp16 (fp16 = true). BH = B*H. d in {64, 128}.
 hipError_t launch_fwd_16(bool fp16, const void* q, const void* k, const void* v, void* o, float* lse,
                          int BH, int N, int d, float scale, bool causal, hipStream_t stream);
 
+// Forward with padding / block-sparse masks (16-bit storage; rows that see no key: O = 0,
+// LSE = -inf).
+hipError_t launch_fwd_16_masked(bool fp16, const void* q, const void* k, const void* v, void* o, float* lse,
+                                int BH, int N, int d, float scale, bool causal, const Masks& masks,
+                                hipStream_t stream);
+
 // Key-split forward (Nq = N query rows against Nk >= N key rows; causal: query i sees keys
-// j <= i + Nk - N). The K/V tiles are dealt to n_splits groups of tiles_per_split tiles; each group's
-// fp32 partial (O, LSE) goes to opart [n_splits][BH][N][d] / lsepart [n_splits][BH][N], then a
-// merge kernel writes O and LSE.
+// j <= i + L - N, L = the sequence's cache length, Nk without seqlens_k). The K/V tiles are dealt to
+// n_splits groups of tiles_per_split tiles; each group's fp32 partial (O, LSE) goes to
+// opart [n_splits][BH][N][d] / lsepart [n_splits][BH][N], then a merge kernel writes O and LSE.
 hipError_t launch_fwd_16_kvsplit(bool fp16, const void* q, const void* k, const void* v, void* o, float* lse,
                                  int BH, int N, int Nk, int d, float scale, bool causal, int n_splits,
-                                 int tiles_per_split, float* opart, float* lsepart, hipStream_t stream);
+                                 int tiles_per_split, float* opart, float* lsepart, const int* seqlens_k,
+                                 int heads, hipStream_t stream);
 
 // Compute units of the current device (cached per device).
 int device_cu_count();
@@ -33,6 +54,12 @@ hipError_t launch_bwd_dkdv(bool fp16, const void* q, const void* k, const void* 
 hipError_t launch_bwd_dq(bool fp16, const void* q, const void* k, const void* v, const void* o,
                          const float* lse, const void* dout, float* delta, void* dq, int BH, int N,
                          int d, float scale, bool causal, hipStream_t stream);
+
+// Full backward (dQ with delta, then dK/dV) under padding / block-sparse masks.
+hipError_t launch_bwd_masked(bool fp16, const void* q, const void* k, const void* v, const void* o,
+                             const float* lse, const void* dout, float* delta, void* dq, void* dk, void* dv,
+                             int BH, int N, int d, float scale, bool causal, const Masks& masks,
+                             hipStream_t stream);
 
 // Work decomposition shared by the kernels: workgroup id -> (head, tile).
 // The hardware hands consecutive workgroup ids to the 8 XCDs round-robin, each with its own L2.

@@ -66,6 +66,13 @@ int kvsplit_plan(int BH, int Nq, int Nk, int requested, int* tiles_per_split) {
 
 size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// Block-sparse maps: the map row of a query tile must fit the kernels' LDS block list.
+fa_status_t check_masks(int N, const int32_t* seqlens, const uint8_t* block_mask) {
+  if (seqlens && !aligned4(seqlens)) return FA_ERR_MISALIGNED;
+  if (block_mask && (N + fa::kMaskBlock - 1) / fa::kMaskBlock > fa::kMaxMaskBlocks) return FA_ERR_UNSUPPORTED;
+  return FA_OK;
+}
+
 fa_status_t check_kvsplit_shape(int B, int H, int Nq, int Nk, int d, int num_splits) {
   fa_status_t st = check_shape(B, H, Nq, d);
   if (st != FA_OK) return st;
@@ -103,9 +110,30 @@ size_t flash_attn_fwd_kvsplit_workspace_size(int B, int H, int Nq, int Nk, int d
   return round256(rows * d * sizeof(float)) + round256(rows * sizeof(float));
 }
 
+fa_status_t flash_attn_fwd_masked(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                                  int N, int d, float scale, int causal, const int32_t* seqlens,
+                                  const uint8_t* block_mask, int dtype, void* stream) {
+  if (!q || !k || !v || !o) return FA_ERR_NULL_POINTER;
+  fa_status_t st = check_shape(B, H, N, d);
+  if (st != FA_OK) return st;
+  if (!is_16bit(dtype) || !supported_d(d)) return FA_ERR_UNSUPPORTED;
+  if (!isfinite(scale)) return FA_ERR_BAD_SCALE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || (lse && !aligned4(lse)))
+    return FA_ERR_MISALIGNED;
+  st = check_masks(N, seqlens, block_mask);
+  if (st != FA_OK) return st;
+  fa::Masks m;
+  m.seqlens = seqlens;
+  m.block_mask = block_mask;
+  m.heads = H;
+  hipError_t e = fa::launch_fwd_16_masked(dtype == FA_DTYPE_FP16, q, k, v, o, lse, B * H, N, d, scale, causal != 0, m,
+                                          static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 fa_status_t flash_attn_fwd_kvsplit(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
-                                   int Nq, int Nk, int d, float scale, int causal, int num_splits, void* workspace,
-                                   size_t workspace_bytes, int dtype, void* stream) {
+                                   int Nq, int Nk, int d, float scale, int causal, const int32_t* seqlens_k,
+                                   int num_splits, void* workspace, size_t workspace_bytes, int dtype, void* stream) {
   if (!q || !k || !v || !o) return FA_ERR_NULL_POINTER;
   fa_status_t st = check_kvsplit_shape(B, H, Nq, Nk, d, num_splits);
   if (st != FA_OK) return st;
@@ -115,14 +143,15 @@ fa_status_t flash_attn_fwd_kvsplit(const void* q, const void* k, const void* v, 
     return FA_ERR_MISALIGNED;
   if (!workspace || workspace_bytes < flash_attn_fwd_kvsplit_workspace_size(B, H, Nq, Nk, d, num_splits, dtype))
     return FA_ERR_WORKSPACE;
-  if (!aligned16(workspace)) return FA_ERR_MISALIGNED;
+  if (!aligned16(workspace) || (seqlens_k && !aligned4(seqlens_k))) return FA_ERR_MISALIGNED;
   int tps = 0;
   const int s = kvsplit_plan(B * H, Nq, Nk, num_splits, &tps);
   const size_t rows = (size_t)s * B * H * Nq;
   float* opart = static_cast<float*>(workspace);
   float* lsepart = reinterpret_cast<float*>(static_cast<char*>(workspace) + round256(rows * d * sizeof(float)));
   hipError_t e = fa::launch_fwd_16_kvsplit(dtype == FA_DTYPE_FP16, q, k, v, o, lse, B * H, Nq, Nk, d, scale,
-                                           causal != 0, s, tps, opart, lsepart, static_cast<hipStream_t>(stream));
+                                           causal != 0, s, tps, opart, lsepart, seqlens_k, H,
+                                           static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
@@ -199,6 +228,29 @@ fa_status_t flash_attn_bwd(const void* q, const void* k, const void* v, const vo
   hipError_t e = fa::launch_bwd_dq(fp16, q, k, v, o, lse, dout, delta, dq, B * H, N, d, scale, causal != 0, s);
   if (e == hipSuccess)
     e = fa::launch_bwd_dkdv(fp16, q, k, v, lse, dout, delta, dk, dv, B * H, N, d, scale, causal != 0, s);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+fa_status_t flash_attn_bwd_masked(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                                  const void* dout, void* dq, void* dk, void* dv, void* workspace,
+                                  size_t workspace_bytes, int B, int H, int N, int d, float scale, int causal,
+                                  const int32_t* seqlens, const uint8_t* block_mask, int dtype, void* stream) {
+  if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FA_ERR_NULL_POINTER;
+  fa_status_t st = check_bwd_common(B, H, N, d, scale, dtype);
+  if (st != FA_OK) return st;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) || !aligned16(dq) ||
+      !aligned16(dk) || !aligned16(dv) || !aligned4(lse))
+    return FA_ERR_MISALIGNED;
+  st = check_masks(N, seqlens, block_mask);
+  if (st != FA_OK) return st;
+  if (!workspace || workspace_bytes < flash_attn_bwd_workspace_size(B, H, N, d, dtype)) return FA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return FA_ERR_MISALIGNED;
+  fa::Masks m;
+  m.seqlens = seqlens;
+  m.block_mask = block_mask;
+  m.heads = H;
+  hipError_t e = fa::launch_bwd_masked(dtype == FA_DTYPE_FP16, q, k, v, o, lse, dout, static_cast<float*>(workspace),
+                                       dq, dk, dv, B * H, N, d, scale, causal != 0, m, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 

@@ -22,6 +22,7 @@ LIB_PATH = os.path.join(_HERE, "libflashattn.so")
 FA_DTYPE_FP32 = 0
 FA_DTYPE_BF16 = 1
 FA_DTYPE_FP16 = 2
+FA_MASK_BLOCK = 128  # rows and keys per block-sparse map entry
 _DTYPES = {torch.float32: FA_DTYPE_FP32, torch.bfloat16: FA_DTYPE_BF16, torch.float16: FA_DTYPE_FP16}
 
 # Names and C signatures of every exported entry point (mirrors include/flash_attn.h).
@@ -37,8 +38,12 @@ SIGNATURES = {
     "flash_attn_bwd_dq": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                  _int, _int, _int, _int, _float, _int, _int, _vp]),
     "flash_attn_fwd_kvsplit_workspace_size": (_size, [_int, _int, _int, _int, _int, _int, _int]),
-    "flash_attn_fwd_kvsplit": (_int, [_vp, _vp, _vp, _vp, _vp, _int, _int, _int, _int, _int, _float, _int, _int,
-                                      _vp, _size, _int, _vp]),
+    "flash_attn_fwd_kvsplit": (_int, [_vp, _vp, _vp, _vp, _vp, _int, _int, _int, _int, _int, _float, _int, _vp,
+                                      _int, _vp, _size, _int, _vp]),
+    "flash_attn_fwd_masked": (_int, [_vp, _vp, _vp, _vp, _vp, _int, _int, _int, _int, _float, _int, _vp, _vp,
+                                     _int, _vp]),
+    "flash_attn_bwd_masked": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _size,
+                                     _int, _int, _int, _int, _float, _int, _vp, _vp, _int, _vp]),
     "flash_attn_status_string": (ctypes.c_char_p, [_int]),
 }
 
@@ -123,13 +128,96 @@ def flash_attn_fwd_kvsplit_workspace_size(B: int, H: int, Nq: int, Nk: int, d: i
     return int(load_library().flash_attn_fwd_kvsplit_workspace_size(B, H, Nq, Nk, d, num_splits, dtype))
 
 
+def _check_seqlens(name: str, t: Optional[torch.Tensor], B: int, ref: torch.Tensor) -> None:
+    if t is None:
+        return
+    if t.dtype != torch.int32 or tuple(t.shape) != (B,) or not t.is_contiguous() or t.device != ref.device:
+        raise ValueError(f"{name} must be a contiguous int32 [B] tensor on q's device")
+
+
+def _check_block_mask(t: Optional[torch.Tensor], B: int, H: int, N: int, ref: torch.Tensor) -> None:
+    if t is None:
+        return
+    nb = (N + FA_MASK_BLOCK - 1) // FA_MASK_BLOCK
+    if t.dtype not in (torch.uint8, torch.bool) or tuple(t.shape) != (B, H, nb, nb) or not t.is_contiguous() \
+            or t.device != ref.device:
+        raise ValueError(f"block_mask must be a contiguous uint8 or bool [B, H, {nb}, {nb}] tensor on q's device")
+
+
+def flash_attn_fwd_masked(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: Optional[float] = None,
+                          causal: bool = False, seqlens: Optional[torch.Tensor] = None,
+                          block_mask: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                          lse: Optional[torch.Tensor] = None, want_lse: bool = True
+                          ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Forward with per-sequence lengths (int32 [B]: rows >= L_b of Q, K, V are padding) and/or a
+    block-sparse map (uint8 / bool [B, H, ceil(N/128), ceil(N/128)], zero = block skipped). Rows
+    that see no key get O = 0, LSE = -inf."""
+    _check_tensor("q", q)
+    _check_tensor("k", k, q)
+    _check_tensor("v", v, q)
+    B, H, N, d = q.shape
+    _check_seqlens("seqlens", seqlens, B, q)
+    _check_block_mask(block_mask, B, H, N, q)
+    scale = float(d) ** -0.5 if scale is None else float(scale)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check_tensor("out", out, q)
+    if lse is None and want_lse:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    if lse is not None:
+        _check_rows("lse", lse, q)
+    st = load_library().flash_attn_fwd_masked(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, d, scale,
+                                              int(bool(causal)), _ptr(seqlens), _ptr(block_mask), _DTYPES[q.dtype],
+                                              _stream_handle(q))
+    _check(st)
+    return out, lse
+
+
+def flash_attn_bwd_masked(dout: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor,
+                          lse: torch.Tensor, scale: Optional[float] = None, causal: bool = False,
+                          seqlens: Optional[torch.Tensor] = None, block_mask: Optional[torch.Tensor] = None,
+                          dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
+                          dv: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None
+                          ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """Backward of flash_attn_fwd_masked (same seqlens and block_mask)."""
+    _check_tensor("q", q)
+    for name, t in (("k", k), ("v", v), ("o", o), ("dout", dout)):
+        _check_tensor(name, t, q)
+    B, H, N, d = q.shape
+    _check_rows("lse", lse, q)
+    _check_seqlens("seqlens", seqlens, B, q)
+    _check_block_mask(block_mask, B, H, N, q)
+    scale = float(d) ** -0.5 if scale is None else float(scale)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        _check_tensor(name, t, q)
+    dt = _DTYPES[q.dtype]
+    need = flash_attn_bwd_workspace_size(B, H, N, d, dt)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    if workspace.device != q.device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on q's device")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    st = load_library().flash_attn_bwd_masked(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
+                                              _ptr(dk), _ptr(dv), _ptr(workspace), ws_bytes, B, H, N, d, scale,
+                                              int(bool(causal)), _ptr(seqlens), _ptr(block_mask), dt,
+                                              _stream_handle(q))
+    _check(st)
+    return dq, dk, dv
+
+
 def flash_attn_fwd_kvsplit(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: Optional[float] = None,
                            causal: bool = False, num_splits: int = 0, out: Optional[torch.Tensor] = None,
                            lse: Optional[torch.Tensor] = None, want_lse: bool = True,
-                           workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+                           workspace: Optional[torch.Tensor] = None, seqlens_k: Optional[torch.Tensor] = None
+                           ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Attention of q [B, H, Nq, d] against k, v [B, H, Nk, d] with Nq <= Nk (decode / chunked
     prefill), the key range split across workgroups and the partial softmaxes merged. Causal
-    aligns the queries with the last Nq key positions."""
+    aligns the queries with the last Nq key positions. seqlens_k (int32 [B]) gives each
+    sequence's valid cache length L_b <= Nk; its queries are then positions L_b - Nq .. L_b - 1."""
     _check_tensor("q", q)
     _check_tensor("k", k)
     _check_tensor("v", v, k)
@@ -147,12 +235,14 @@ def flash_attn_fwd_kvsplit(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, sc
     if lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, Nq) or not lse.is_contiguous()
                             or lse.device != q.device):
         raise ValueError("lse must be a contiguous float32 [B, H, Nq] tensor on q's device")
+    _check_seqlens("seqlens_k", seqlens_k, B, q)
     dt = _DTYPES[q.dtype]
     need = flash_attn_fwd_kvsplit_workspace_size(B, H, Nq, Nk, d, num_splits, dt)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     st = load_library().flash_attn_fwd_kvsplit(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Nq, Nk, d,
-                                               scale, int(bool(causal)), int(num_splits), _ptr(workspace),
+                                               scale, int(bool(causal)), _ptr(seqlens_k), int(num_splits),
+                                               _ptr(workspace),
                                                workspace.numel() * workspace.element_size(), dt, _stream_handle(q))
     _check(st)
     return out, lse

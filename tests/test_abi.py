@@ -165,9 +165,9 @@ def _dq(lib, **kw):
 
 
 def _kvs(lib, q=A, k=A, v=A, o=A, lse=A, B=1, H=1, Nq=1, Nk=8, d=64, scale=0.125, causal=0, splits=0, ws=A,
-         ws_bytes=1 << 20, dtype=1):
-    return lib.flash_attn_fwd_kvsplit(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, splits, ws, ws_bytes, dtype,
-                                      None)
+         ws_bytes=1 << 20, dtype=1, seqlens_k=None):
+    return lib.flash_attn_fwd_kvsplit(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, seqlens_k, splits, ws, ws_bytes,
+                                      dtype, None)
 
 
 def test_kvsplit_validation(lib):
@@ -184,6 +184,35 @@ def test_kvsplit_validation(lib):
     assert _kvs(lib, ws_bytes=16) == WS
     assert _kvs(lib, ws=A + 4) == ALIGN
     assert _kvs(lib, dtype=2, v=A + 2) == ALIGN      # fp16 gets past the dtype check
+    assert _kvs(lib, seqlens_k=A + 2) == ALIGN       # int32 lengths: 4-byte aligned
+
+
+def _fm(lib, q=A, k=A, v=A, o=A, lse=A, B=1, H=1, N=8, d=64, scale=0.125, causal=0, seqlens=None, bm=None, dtype=1):
+    return lib.flash_attn_fwd_masked(q, k, v, o, lse, B, H, N, d, scale, causal, seqlens, bm, dtype, None)
+
+
+def _bm(lib, q=A, k=A, v=A, o=A, lse=A, do=A, dq=A, dk=A, dv=A, ws=A, ws_bytes=1 << 20, B=1, H=1, N=8, d=64,
+        scale=0.125, causal=0, seqlens=None, bmask=None, dtype=1):
+    return lib.flash_attn_bwd_masked(q, k, v, o, lse, do, dq, dk, dv, ws, ws_bytes, B, H, N, d, scale, causal, seqlens,
+                                     bmask, dtype, None)
+
+
+def test_masked_validation(lib):
+    for call in (_fm, _bm):
+        assert call(lib, q=None) == NULLP
+        assert call(lib, N=0) == SHAPE
+        assert call(lib, dtype=0) == UNSUP            # 16-bit types only
+        assert call(lib, d=96) == UNSUP
+        assert call(lib, scale=math.nan) == SCALE
+        assert call(lib, k=A + 8) == ALIGN
+        assert call(lib, seqlens=A + 2) == ALIGN
+        assert call(lib, dtype=2, q=A + 8) == ALIGN   # fp16 gets past the dtype check
+    # a block map row may hold at most FA_MAX_MASK_BLOCKS = 1024 blocks of 128 keys
+    assert _fm(lib, N=1024 * 128 + 1, B=1, H=1, bm=A) == UNSUP
+    assert _bm(lib, N=1024 * 128 + 1, bmask=A) == UNSUP
+    assert _fm(lib, N=1024 * 128 + 1, q=A + 8) == ALIGN  # without a map the length is fine
+    assert _bm(lib, ws=None) == WS
+    assert _bm(lib, lse=None) == NULLP
 
 
 def test_kvsplit_workspace_size(lib):

@@ -1,0 +1,197 @@
+"""GPU parity of the masked paths (padding / variable length, block-sparse maps, per-sequence cache
+lengths) against the float64 masked oracle, through the C ABI.
+
+Gates are the dense path's (O <= 1e-2, LSE <= 1e-3 max-abs on rows that see a key; gradients
+<= 5e-2 relative to their norm). Rows that see no key must be exactly O = 0, LSE = -inf, and
+their gradients exactly 0. With every block enabled and full lengths the masked kernels walk the
+same tiles in the same order as the dense ones, so their results must be bitwise identical.
+"""
+import numpy as np
+import pytest
+import torch
+
+from io_aware_flashattention_flash_amd import (flash_attn_bwd, flash_attn_bwd_masked, flash_attn_fwd,
+                                               flash_attn_fwd_kvsplit, flash_attn_fwd_masked, inputs)
+from oracle import attn_bwd_masked, attn_fwd_masked, kv_cache_visible, padded_batch_visible
+from tests.test_parity_gpu import BF16_LSE, BF16_O, DEV, GRAD, dev, grad_errors, host
+
+pytestmark = pytest.mark.gpu
+
+BLK = 128
+
+
+def _inputs(B, H, N, d, seed, dtype="bf16", with_do=False):
+    names = ("q", "k", "v", "do") if with_do else ("q", "k", "v")
+    return {n: inputs.random_tensor((B, H, N, d), seed + i, dtype) for i, n in enumerate(names)}
+
+
+def _random_map(B, H, N, seed, density):
+    nb = -(-N // BLK)
+    return (np.random.default_rng(seed).random((B, H, nb, nb)) < density).astype(np.uint8)
+
+
+def _fwd(x, scale, causal, seqlens, bmap, tdt=torch.bfloat16):
+    q, k, v = (dev(x[n], tdt) for n in ("q", "k", "v"))
+    sl = None if seqlens is None else torch.tensor(seqlens, dtype=torch.int32, device=DEV)
+    bm = None if bmap is None else torch.from_numpy(bmap).to(DEV)
+    o = torch.full_like(q, float("nan"))
+    lse = torch.full(q.shape[:3], float("nan"), device=DEV)
+    o, lse = flash_attn_fwd_masked(q, k, v, scale, causal, seqlens=sl, block_mask=bm, out=o, lse=lse)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+def _check_fwd(o, lse, O, L):
+    o, lse = host(o), host(lse)
+    full = np.isfinite(L)
+    assert np.isfinite(o).all()
+    assert (o[~full] == 0).all() and np.isneginf(lse[~full]).all()
+    assert np.abs(o[full] - O[full]).max(initial=0) <= BF16_O
+    assert np.abs(lse[full] - L[full]).max(initial=0) <= BF16_LSE
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N,seqlens", [(300, [300, 1, 0, 129]), (1000, [999, 640, 128, 257]), (77, [77, 50, 5, 0])])
+def test_fwd_padded(N, seqlens, causal, d):
+    B, H = len(seqlens), 2
+    x = _inputs(B, H, N, d, seed=N + d)
+    o, lse = _fwd(x, d ** -0.5, causal, seqlens, None)
+    O, L = attn_fwd_masked(x["q"], x["k"], x["v"], d ** -0.5, padded_batch_visible(B, H, N, causal, seqlens))
+    _check_fwd(o, lse, O, L)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N,density", [(700, 0.5), (1100, 0.3), (256, 0.0), (513, 0.8)])
+def test_fwd_block_sparse(N, density, causal, d):
+    B, H = 2, 2
+    x = _inputs(B, H, N, d, seed=2 * N + d)
+    bmap = _random_map(B, H, N, seed=N, density=density)
+    if density > 0:
+        bmap[0, 0, -1, :] = 0  # one query block with no enabled block at all
+    seqlens = [N, N - 130] if N > 200 else None
+    o, lse = _fwd(x, d ** -0.5, causal, seqlens, bmap)
+    O, L = attn_fwd_masked(x["q"], x["k"], x["v"], d ** -0.5,
+                           padded_batch_visible(B, H, N, causal, seqlens, bmap, BLK))
+    _check_fwd(o, lse, O, L)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_masked_forward_without_masks_is_the_dense_forward(causal, d):
+    """All blocks enabled and full lengths: the same tiles in the same order, bitwise."""
+    B, H, N = 2, 3, 900
+    x = _inputs(B, H, N, d, seed=5)
+    q, k, v = (dev(x[n], torch.bfloat16) for n in ("q", "k", "v"))
+    ref = flash_attn_fwd(q, k, v, 0.1, causal)
+    nb = -(-N // BLK)
+    ones = torch.ones((B, H, nb, nb), dtype=torch.uint8, device=DEV)
+    full = torch.full((B,), N, dtype=torch.int32, device=DEV)
+    for sl, bm in ((None, None), (full, None), (None, ones), (full, ones)):
+        got = flash_attn_fwd_masked(q, k, v, 0.1, causal, seqlens=sl, block_mask=bm)
+        torch.cuda.synchronize()
+        assert torch.equal(got[0], ref[0]) and torch.equal(got[1], ref[1])
+
+
+def _bwd_case(B, H, N, d, causal, seqlens, bmap, seed, tdt=torch.bfloat16, dtype="bf16"):
+    x = _inputs(B, H, N, d, seed=seed, dtype=dtype, with_do=True)
+    q, k, v, do = (dev(x[n], tdt) for n in ("q", "k", "v", "do"))
+    sl = None if seqlens is None else torch.tensor(seqlens, dtype=torch.int32, device=DEV)
+    bm = None if bmap is None else torch.from_numpy(bmap).to(DEV)
+    scale = d ** -0.5
+    o, lse = flash_attn_fwd_masked(q, k, v, scale, causal, seqlens=sl, block_mask=bm)
+    dq, dk, dv = (torch.full_like(q, float("nan")) for _ in range(3))
+    flash_attn_bwd_masked(do, q, k, v, o, lse, scale, causal, seqlens=sl, block_mask=bm, dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    vis = padded_batch_visible(B, H, N, causal, seqlens, bmap, BLK)
+    dQ, dK, dV, _ = attn_bwd_masked(x["q"], x["k"], x["v"], x["do"], scale, vis)
+    rows_seen = vis.any(axis=-1)   # queries that see a key
+    keys_seen = vis.any(axis=-2)   # keys some query sees
+    for name, g, r, live in (("dQ", dq, dQ, rows_seen), ("dK", dk, dK, keys_seen), ("dV", dv, dV, keys_seen)):
+        g = host(g)
+        assert np.isfinite(g).all(), name
+        assert (g[~live] == 0).all(), name
+        e_inf, e_fro = grad_errors(g, r)
+        assert e_inf <= GRAD and e_fro <= GRAD, (name, e_inf, e_fro)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N,seqlens", [(300, [300, 1, 0, 129]), (640, [500, 640, 64, 200])])
+def test_bwd_padded(N, seqlens, causal, d):
+    _bwd_case(len(seqlens), 2, N, d, causal, seqlens, None, seed=7 * N + d)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N,density,padded", [(700, 0.5, False), (1000, 0.4, True), (300, 0.0, False)])
+def test_bwd_block_sparse(N, density, padded, causal, d):
+    B, H = 2, 2
+    bmap = _random_map(B, H, N, seed=N + 1, density=density)
+    if density > 0:
+        bmap[1, 0, 1, :] = 0  # a query block with nothing enabled
+        bmap[0, 1, :, 2] = 0  # a key block no query sees
+    _bwd_case(B, H, N, d, causal, [N - 37, N - 300] if padded else None, bmap, seed=N + d)
+
+
+def test_bwd_masked_fp16():
+    bmap = _random_map(2, 2, 600, seed=3, density=0.6)
+    _bwd_case(2, 2, 600, 128, True, [600, 333], bmap, seed=11, tdt=torch.float16, dtype="fp16")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_masked_backward_without_masks_is_the_dense_backward(causal, d):
+    B, H, N = 2, 2, 700
+    x = _inputs(B, H, N, d, seed=9, with_do=True)
+    q, k, v, do = (dev(x[n], torch.bfloat16) for n in ("q", "k", "v", "do"))
+    o, lse = flash_attn_fwd(q, k, v, 0.1, causal)
+    ref = flash_attn_bwd(do, q, k, v, o, lse, 0.1, causal)
+    nb = -(-N // BLK)
+    ones = torch.ones((B, H, nb, nb), dtype=torch.uint8, device=DEV)
+    full = torch.full((B,), N, dtype=torch.int32, device=DEV)
+    got = flash_attn_bwd_masked(do, q, k, v, o, lse, 0.1, causal, seqlens=full, block_mask=ones)
+    torch.cuda.synchronize()
+    for g, r in zip(got, ref):
+        assert torch.equal(g, r)
+
+
+def test_masked_deterministic():
+    B, H, N = 2, 4, 1500
+    x = _inputs(B, H, N, 128, seed=12, with_do=True)
+    q, k, v, do = (dev(x[n], torch.bfloat16) for n in ("q", "k", "v", "do"))
+    sl = torch.tensor([1500, 777], dtype=torch.int32, device=DEV)
+    bm = torch.from_numpy(_random_map(B, H, N, seed=4, density=0.5)).to(DEV)
+    first = None
+    for _ in range(3):
+        o, lse = flash_attn_fwd_masked(q, k, v, 0.09, True, seqlens=sl, block_mask=bm)
+        g = flash_attn_bwd_masked(do, q, k, v, o, lse, 0.09, True, seqlens=sl, block_mask=bm)
+        torch.cuda.synchronize()
+        cur = (o, lse) + tuple(g)
+        if first is None:
+            first = cur
+        else:
+            assert all(torch.equal(a, b) for a, b in zip(cur, first))
+
+
+# ---------------------------------------------------------------------------------------------
+# key-split forward with per-sequence cache lengths
+# ---------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("Nq,Nk,lens,splits", [(1, 4097, [4097, 1, 0, 2000], 0), (1, 1000, [999, 64, 65, 500], 3),
+                                               (200, 1000, [1000, 150, 200, 901], 0), (64, 640, [640, 0, 10, 300], 4)])
+def test_kvsplit_cache_lengths(Nq, Nk, lens, splits, causal, d):
+    B, H = len(lens), 2
+    x = {"q": inputs.random_tensor((B, H, Nq, d), Nq + d, "bf16"),
+         "k": inputs.random_tensor((B, H, Nk, d), Nk + d, "bf16"),
+         "v": inputs.random_tensor((B, H, Nk, d), Nk + d + 1, "bf16")}
+    q, k, v = (dev(x[n], torch.bfloat16) for n in ("q", "k", "v"))
+    o = torch.full_like(q, float("nan"))
+    lse = torch.full(q.shape[:3], float("nan"), device=DEV)
+    sl = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    o, lse = flash_attn_fwd_kvsplit(q, k, v, d ** -0.5, causal, splits, out=o, lse=lse, seqlens_k=sl)
+    torch.cuda.synchronize()
+    O, L = attn_fwd_masked(x["q"], x["k"], x["v"], d ** -0.5, kv_cache_visible(B, H, Nq, Nk, causal, lens))
+    _check_fwd(o, lse, O, L)

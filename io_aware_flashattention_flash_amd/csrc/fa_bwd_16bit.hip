@@ -210,10 +210,12 @@ __global__ __launch_bounds__(NW * 64, (D > 64 ? 1 : 2)) void bwd_dkdv_kernel(Bwd
   const __amdgpu_buffer_rsrc_t rdel = make_rsrc(p.delta + rbase, Lb * 4);
   float st_l = 0.f, st_d = 0.f;  // wave 0: this tile's row statistics, staged in registers
   auto dma = [&](int i, char* qb, char* ob) __attribute__((always_inline)) {
+    // (wave-uniform by construction; readfirstlane keeps the descriptors in scalar registers)
     const int row0 = i * BQ;
-    const int bytes = max(0, min(BQ, Lb - row0)) * (D * 2);
-    const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + base + (size_t)min(row0, Lb) * D, bytes);
-    const __amdgpu_buffer_rsrc_t ro = make_rsrc(p.dout + base + (size_t)min(row0, Lb) * D, bytes);
+    const int bytes = __builtin_amdgcn_readfirstlane(max(0, min(BQ, Lb - row0)) * (D * 2));
+    const int first = __builtin_amdgcn_readfirstlane(min(row0, Lb));
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + base + (size_t)first * D, bytes);
+    const __amdgpu_buffer_rsrc_t ro = make_rsrc(p.dout + base + (size_t)first * D, bytes);
 #pragma unroll
     for (int t = 0; t < NLD; ++t) {
       buf_load16_to_lds(rq, qb + (w + NW * t) * 1024, goff[t]);
@@ -432,10 +434,12 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdParams<E> p) {
     goff[i] = row * (D * 2) + ((pc ^ T::swz(row)) * 16);
   }
   auto dma = [&](int j, char* kb, char* vb) __attribute__((always_inline)) {
+    // (wave-uniform by construction; readfirstlane keeps the descriptors in scalar registers)
     const int key0 = j * BC;
-    const int bytes = max(0, min(BC, Lb - key0)) * (D * 2);
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k + base + (size_t)min(key0, Lb) * D, bytes);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + base + (size_t)min(key0, Lb) * D, bytes);
+    const int bytes = __builtin_amdgcn_readfirstlane(max(0, min(BC, Lb - key0)) * (D * 2));
+    const int first = __builtin_amdgcn_readfirstlane(min(key0, Lb));
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k + base + (size_t)first * D, bytes);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + base + (size_t)first * D, bytes);
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
       buf_load16_to_lds(rk, kb + (w + NW * i) * 1024, goff[i]);

@@ -185,6 +185,40 @@ def time_masked_forward(kind, B, H, N, d, dev, reps=100):
             "pct_of_peak": round(100 * tf / PEAK_BF16_TFLOPS, 2)}
 
 
+def time_dropout_step(B, H, N, d, p, dev, reps=50):
+    """Forward + backward (dQ, then dK/dV) of causal attention with dropout probability p, through
+    the masked entry points; flops counted as for the dense step (dropout adds none)."""
+    import torch
+
+    from io_aware_flashattention_flash_amd import flash_attn_bwd_masked, flash_attn_fwd_masked, inputs
+
+    q, k, v, do = (torch.from_numpy(inputs.random_tensor((B, H, N, d), 51 + i)).to(dev).to(torch.bfloat16)
+                   for i in range(4))
+    o = torch.empty_like(q)
+    lse = torch.empty(B, H, N, device=dev)
+    grads = [torch.empty_like(q) for _ in range(3)]
+    ws = torch.empty(4 * B * H * N + 256, dtype=torch.uint8, device=dev)
+
+    def step(seed):
+        flash_attn_fwd_masked(q, k, v, None, True, out=o, lse=lse, dropout_p=p, seed=seed)
+        flash_attn_bwd_masked(do, q, k, v, o, lse, None, True, dq=grads[0], dk=grads[1], dv=grads[2], workspace=ws,
+                              dropout_p=p, seed=seed)
+
+    for s in range(5):
+        step(s)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for s in range(reps):
+        step(100 + s)
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) / reps * 1e3
+    flops = 3.5 * 4.0 * B * H * N * N * d / 2
+    return {"workload": f"fwdbwd_bf16_b{B}h{H}n{N}d{d}_causal_dropout{p}", "pass": "fwd+bwd (dropout)", "reps": reps,
+            "us": round(us, 2), "tflops": round(flops / (us * 1e-6) / 1e12, 1)}
+
+
 def time_fwdbwd(w, x, steps, warmup, dev, to_dev):
     """One step = forward, dQ (with delta), dK/dV on resident inputs of a 16-bit workload. Returns
     (ms per step over `steps` timed steps, {stage: average ms}) from HIP events on the stream."""
@@ -317,6 +351,8 @@ def main():
         for kind, shape in (("blocksparse", (2, 32, 4096, 128)), ("varlen", (8, 16, 4096, 128))):
             r = time_masked_forward(kind, *shape, dev)
             extras[r["workload"]] = r
+        r = time_dropout_step(4, 16, 2048, 64, 0.1, dev)
+        extras[r["workload"]] = r
         torch.cuda.empty_cache()
 
     # ------------------------------------------------------------------ CPU oracle baseline

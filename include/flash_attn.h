@@ -36,8 +36,8 @@
  *              error status has launched nothing and written nothing.
  *   Errors     The library never aborts and never prints. Launch failures are
  *              reported as FA_ERR_HIP.
- *   Support    bf16: d in {64, 128}, forward (also key-split and masked) and
- *              backward (also masked).
+ *   Support    bf16: d in {64, 128}, forward (also key-split, and masked with optional
+ *              dropout) and backward (also masked with optional dropout).
  *              fp16 (IEEE binary16): the same as bf16.
  *              fp32: d in {64, 128}, forward only (no masks).
  *              B, H, N >= 1, B*H*N*d < 2^31 elements per tensor and
@@ -63,7 +63,8 @@ typedef enum {
   FA_ERR_BAD_SCALE = 4,    /* scale is NaN or infinite */
   FA_ERR_MISALIGNED = 5,   /* a pointer is not 16-byte aligned (lse, seqlens: 4-byte) */
   FA_ERR_WORKSPACE = 6,    /* workspace NULL or smaller than flash_attn_bwd_workspace_size() */
-  FA_ERR_HIP = 7           /* the HIP runtime reported an error at launch */
+  FA_ERR_HIP = 7,          /* the HIP runtime reported an error at launch */
+  FA_ERR_BAD_DROPOUT = 8   /* dropout_p is NaN, infinite, negative or above 511/512 */
 } fa_status_t;
 
 typedef enum { FA_DTYPE_FP32 = 0, FA_DTYPE_BF16 = 1, FA_DTYPE_FP16 = 2 } fa_dtype_t;
@@ -99,13 +100,29 @@ fa_status_t flash_attn_fwd(const void* q, const void* k, const void* v, void* o,
  *               removes scores of query rows 128r .. 128r+127 against keys 128c .. 128c+127;
  *               whole blocks are skipped, never loaded.
  * Query i sees key j iff i < L_b, j < L_b, (not causal or j <= i) and the block of (i, j) is
- * enabled. A row that sees no key (padding rows included) gets O = 0 and LSE = -inf. bf16 and fp16;
- * other arguments as flash_attn_fwd. Deterministic.
+ * enabled. A row that sees no key (padding rows included) gets O = 0 and LSE = -inf.
+ *   dropout_p, seed  attention dropout (52jiny.com, "why standard attention is IO-bound": the
+ *               step between the softmax and the product with V). Each probability P_ij is kept
+ *               or zeroed by a byte of the counter-based generator Philox4x32-10 (Salmon, Moraes,
+ *               Dror, Shaw, SC 2011): counter (i, j / 32, b * H + h, (j / 4) % 2), key
+ *               (seed & 0xffffffff, seed >> 32); byte j % 4 of output word (j % 32) / 8 (byte 0 =
+ *               least significant); kept iff byte < T = round(256 (1 - dropout_p)). Kept
+ *               probabilities are scaled by 256 / T. LSE stays that of the undropped softmax.
+ *               dropout_p = 0 (T = 256) disables dropout; flash_attn_dropout_mask returns the mask.
+ * bf16 and fp16; other arguments as flash_attn_fwd. Deterministic for a given seed.
  */
 fa_status_t flash_attn_fwd_masked(const void* q, const void* k, const void* v, void* o, float* lse,
                                   int B, int H, int N, int d, float scale, int causal,
                                   const int32_t* seqlens, const uint8_t* block_mask,
-                                  int dtype, void* stream);
+                                  float dropout_p, uint64_t seed, int dtype, void* stream);
+
+/*
+ * The dropout keep mask flash_attn_fwd_masked applies for (dropout_p, seed), for inspection and
+ * testing: keep [B,H,Nq,Nk] uint8 on the device, written 1 (kept) or 0 (dropped) per score
+ * element. Not needed to run attention.
+ */
+fa_status_t flash_attn_dropout_mask(uint8_t* keep, int B, int H, int Nq, int Nk, float dropout_p,
+                                    uint64_t seed, void* stream);
 
 /*
  * Forward of Nq queries against Nk >= Nq keys (decoding one or a few new
@@ -167,9 +184,11 @@ fa_status_t flash_attn_bwd(const void* q, const void* k, const void* v, const vo
                            int dtype, void* stream);
 
 /*
- * Backward of flash_attn_fwd_masked (same seqlens and block_mask; o and lse from that call).
- * Rows that see no key contribute nothing; dQ rows of such queries and dK, dV rows of keys that
- * no query sees are 0 (padding rows included). Workspace and other arguments as flash_attn_bwd.
+ * Backward of flash_attn_fwd_masked (same seqlens, block_mask, dropout_p and seed; o and lse from
+ * that call). Rows that see no key contribute nothing; dQ rows of such queries and dK, dV rows of
+ * keys that no query sees are 0 (padding rows included). With dropout the keep mask is
+ * regenerated from the seed: dV = (P Z)^T dO, dP = (dO V^T) Z, dS = P (dP - D), with
+ * Z = keep * 256 / T and D = rowsum(dO * O). Workspace and other arguments as flash_attn_bwd.
  */
 fa_status_t flash_attn_bwd_masked(const void* q, const void* k, const void* v, const void* o,
                                   const float* lse, const void* dout,
@@ -177,7 +196,7 @@ fa_status_t flash_attn_bwd_masked(const void* q, const void* k, const void* v, c
                                   void* workspace, size_t workspace_bytes,
                                   int B, int H, int N, int d, float scale, int causal,
                                   const int32_t* seqlens, const uint8_t* block_mask,
-                                  int dtype, void* stream);
+                                  float dropout_p, uint64_t seed, int dtype, void* stream);
 
 /*
  * Backward stages, exposed so a caller can run (or time) them separately. Same

@@ -16,7 +16,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB_PATH = os.path.join(PKG, "libflashattn.so")
-SOURCES = ["flash_attn_abi.hip", "fa_fwd_16bit.hip", "fa_fwd_fp32.hip", "fa_bwd_16bit.hip"]
+SOURCES = ["flash_attn_abi.hip", "fa_fwd_16bit.hip", "fa_fwd_fp32.hip", "fa_bwd_16bit.hip", "fa_dropout.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 VALU forms are disabled for every HIP object: the compiler then emits only

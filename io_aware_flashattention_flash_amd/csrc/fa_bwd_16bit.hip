@@ -54,6 +54,11 @@ struct BwdParams {
   const uint8_t* block_mask;
   int heads;
   int n_mb;
+  // Dropout launches only: Philox key, keep threshold T and 256 / T.
+  uint32_t seed_lo;
+  uint32_t seed_hi;
+  int drop_thr;
+  float drop_scale;
 };
 
 // Valid rows of this head's sequence.
@@ -121,7 +126,11 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdParams<E> p) {
 // ---------------------------------------------------------------------------------------------
 // MASKED: padding rows (>= the sequence's length) and, with a block-sparse map, only the query
 // blocks enabled in this key tile's map column; keys no query sees get dK = dV = 0.
-template <typename E, int D, int NW, int BQ, bool CAUSAL, bool MASKED>
+// DROPOUT (with MASKED): the forward's keep mask is regenerated; the weights of dV are the kept
+// probabilities scaled by 256 / T, and the gradient reaching P is dP scaled by the same kept factor.
+// This kernel's lanes hold keys, not queries, so each wave draws the Philox words of its 32 x 32
+// block in the forward's layout (one call per lane) and transposes the bytes through LDS.
+template <typename E, int D, int NW, int BQ, bool CAUSAL, bool MASKED, bool DROPOUT>
 __global__ __launch_bounds__(NW * 64, (D > 64 ? 1 : 2)) void bwd_dkdv_kernel(BwdParams<E> p) {
   using H = Half16<E>;
   using e16x8 = typename H::x8;
@@ -143,6 +152,7 @@ __global__ __launch_bounds__(NW * 64, (D > 64 ? 1 : 2)) void bwd_dkdv_kernel(Bwd
   __shared__ __attribute__((aligned(16))) float sr0[2 * BQ];  // [lse * log2(e) | delta] of the tile's rows
   __shared__ __attribute__((aligned(16))) float sr1[2 * BQ];
   __shared__ short blist[MASKED ? kMaxMaskBlocks : 1];  // enabled query blocks of this key tile
+  __shared__ __attribute__((aligned(16))) uint8_t sdrop[DROPOUT ? NW * 1024 : 4];  // per wave: bytes [key][query]
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -256,6 +266,24 @@ __global__ __launch_bounds__(NW * 64, (D > 64 ? 1 : 2)) void bwd_dkdv_kernel(Bwd
       }
       // Register r holds query q0 + 8*(r/4) + 4*hf + r%4 against this lane's key.
       const int kmin = key - q0 - 4 * hf;  // (DIAG) query offsets below this are masked
+      uint32_t kwt[4];  // dropout: byte e of kwt[g] belongs to register 4g + e
+      if constexpr (DROPOUT) {
+        // Lane (q, h) draws the words of query q0 + q, half h of the wave's 32-key block, and
+        // stores byte (g, e) at [key 8g + 4h + e][query q]; lane (key, hf) then reads its key's row.
+        uint8_t* mt = sdrop + w * 1024;
+        uint32_t wd[4];
+        dropout_words(q0 + lq, key_w0 >> 5, head, hf, p.seed_lo, p.seed_hi, wd);
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) mt[(8 * g + 4 * hf + e) * 32 + lq] = (uint8_t)(wd[g] >> (8 * e));
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes have landed
+        __builtin_amdgcn_wave_barrier();
+#pragma unroll
+        for (int g = 0; g < 4; ++g) kwt[g] = *reinterpret_cast<const uint32_t*>(mt + lq * 32 + 8 * g + 4 * hf);
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // reads done before the next block's writes
+        __builtin_amdgcn_wave_barrier();
+      }
       e16x8 pb[2], dsb[2];
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
@@ -266,8 +294,15 @@ __global__ __launch_bounds__(NW * 64, (D > 64 ? 1 : 2)) void bwd_dkdv_kernel(Bwd
           const int r = 4 * g + e;
           float pr = fast_exp2(fmaf(s[r], c, -lse4[e]));
           if constexpr (DIAG) pr = (8 * g + e < kmin) ? 0.f : pr;
-          pb[r >> 3][r & 7] = (E)pr;
-          dsb[r >> 3][r & 7] = (E)(pr * (dp[r] - dl4[e]));
+          float dpr = dp[r];
+          if constexpr (DROPOUT) {
+            const bool kept = dropout_keep(kwt[g], e, p.drop_thr);
+            pb[r >> 3][r & 7] = (E)(kept ? pr * p.drop_scale : 0.f);
+            dpr = kept ? dpr * p.drop_scale : 0.f;
+          } else {
+            pb[r >> 3][r & 7] = (E)pr;
+          }
+          dsb[r >> 3][r & 7] = (E)(pr * (dpr - dl4[e]));
         }
       }
       // dV^T += dO^T P and dK^T += Q^T dS; k-step ks covers queries
@@ -334,7 +369,9 @@ __global__ __launch_bounds__(NW * 64, (D > 64 ? 1 : 2)) void bwd_dkdv_kernel(Bwd
 // ---------------------------------------------------------------------------------------------
 // MASKED: padding rows and, with a block-sparse map, only the key blocks enabled in this query
 // tile's map row; every tile takes the masked path.
-template <typename E, int D, int BC, int NW, bool CAUSAL, bool MASKED>
+// DROPOUT (with MASKED): dS = P * (dP * keep * 256 / T - delta), the keep mask regenerated in
+// the forward's layout.
+template <typename E, int D, int BC, int NW, bool CAUSAL, bool MASKED, bool DROPOUT>
 __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdParams<E> p) {
   using H = Half16<E>;
   using e16x8 = typename H::x8;
@@ -471,6 +508,11 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdParams<E> p) {
       }
     }
     const int lim = key_lim - key0 - 4 * hf;
+    uint32_t kw[NKB][4];  // dropout: Philox words of each 32-key half of the tile
+    if constexpr (DROPOUT) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) dropout_words(q, (key0 >> 5) + kb, head, hf, p.seed_lo, p.seed_hi, kw[kb]);
+    }
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
       e16x8 dsb;
@@ -482,7 +524,9 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdParams<E> p) {
           const int krel = 32 * (ks >> 1) + (r >> 2) * 8 + (r & 3);
           pr = krel <= lim ? pr : 0.f;
         }
-        dsb[e] = (E)(pr * (dp[ks >> 1][r] - dlt));
+        float dpr = dp[ks >> 1][r];
+        if constexpr (DROPOUT) dpr = dropout_keep(kw[ks >> 1][r >> 2], r & 3, p.drop_thr) ? dpr * p.drop_scale : 0.f;
+        dsb[e] = (E)(pr * (dpr - dlt));
       }
       // dQ^T += K^T dS^T; k-step ks covers keys 16ks + {4hf..4hf+3, 8+4hf..8+4hf+3}.
 #pragma unroll
@@ -567,6 +611,9 @@ BwdParams<E> make_params(const void* q, const void* k, const void* v, const void
   prm.block_mask = nullptr;
   prm.heads = 1;
   prm.n_mb = (N + kMaskBlock - 1) / kMaskBlock;
+  prm.seed_lo = prm.seed_hi = 0;
+  prm.drop_thr = 256;
+  prm.drop_scale = 1.f;
   return prm;
 }
 
@@ -578,20 +625,20 @@ hipError_t delta_d(BwdParams<E> prm, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <typename E, int D, bool CAUSAL, bool MASKED = false>
+template <typename E, int D, bool CAUSAL, bool MASKED = false, bool DROPOUT = false>
 hipError_t dkdv_d(BwdParams<E> prm, hipStream_t stream) {
   prm.n_tiles = (prm.N + 32 * kKvNW - 1) / (32 * kKvNW);
-  hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, kKvNW, kKvBQ, CAUSAL, MASKED>), dim3(prm.n_tiles * prm.nh),
+  hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, kKvNW, kKvBQ, CAUSAL, MASKED, DROPOUT>), dim3(prm.n_tiles * prm.nh),
                      dim3(kKvNW * 64), 0, stream, prm);
   return hipGetLastError();
 }
 
-template <typename E, int D, bool CAUSAL, bool MASKED = false>
+template <typename E, int D, bool CAUSAL, bool MASKED = false, bool DROPOUT = false>
 hipError_t dq_d(BwdParams<E> prm, hipStream_t stream) {
   prm.n_tiles = (prm.N + 32 * kDqNW - 1) / (32 * kDqNW);
   // Pair causal tiles when there are at least four workgroups per CU to begin with.
   prm.n_units = (CAUSAL && (long)prm.n_tiles * prm.nh >= 4L * device_cu_count()) ? (prm.n_tiles + 1) / 2 : prm.n_tiles;
-  hipLaunchKernelGGL((bwd_dq_kernel<E, D, dq_bc<D>(), kDqNW, CAUSAL, MASKED>), dim3(prm.n_units * prm.nh),
+  hipLaunchKernelGGL((bwd_dq_kernel<E, D, dq_bc<D>(), kDqNW, CAUSAL, MASKED, DROPOUT>), dim3(prm.n_units * prm.nh),
                      dim3(kDqNW * 64), 0, stream, prm);
   return hipGetLastError();
 }
@@ -625,35 +672,38 @@ hipError_t dq_typed(const void* q, const void* k, const void* v, const void* o, 
   if (d == 128) return causal ? dq_d<E, 128, true>(prm, stream) : dq_d<E, 128, false>(prm, stream);
   return hipErrorInvalidValue;
 }
+template <typename E, int D, bool DROPOUT>
+hipError_t masked_d(const BwdParams<E>& prm, bool causal, hipStream_t stream) {
+  hipError_t e = causal ? dq_d<E, D, true, true, DROPOUT>(prm, stream) : dq_d<E, D, false, true, DROPOUT>(prm, stream);
+  if (e != hipSuccess) return e;
+  return causal ? dkdv_d<E, D, true, true, DROPOUT>(prm, stream) : dkdv_d<E, D, false, true, DROPOUT>(prm, stream);
+}
+
 template <typename E>
 hipError_t masked_typed(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
                         float* delta, void* dq, void* dk, void* dv, int BH, int N, int d, float scale, bool causal,
-                        const Masks& m, hipStream_t stream) {
+                        const Masks& m, const Dropout& drop, hipStream_t stream) {
   BwdParams<E> prm = make_params<E>(q, k, v, o, lse, dout, delta, dq, dk, dv, BH, N, scale);
   prm.seqlens = m.seqlens;
   prm.block_mask = m.block_mask;
   prm.heads = m.heads;
-  hipError_t e;
-  if (d == 64) {
-    e = causal ? dq_d<E, 64, true, true>(prm, stream) : dq_d<E, 64, false, true>(prm, stream);
-    if (e == hipSuccess) e = causal ? dkdv_d<E, 64, true, true>(prm, stream) : dkdv_d<E, 64, false, true>(prm, stream);
-    return e;
-  }
-  if (d == 128) {
-    e = causal ? dq_d<E, 128, true, true>(prm, stream) : dq_d<E, 128, false, true>(prm, stream);
-    if (e == hipSuccess)
-      e = causal ? dkdv_d<E, 128, true, true>(prm, stream) : dkdv_d<E, 128, false, true>(prm, stream);
-    return e;
-  }
+  prm.seed_lo = (uint32_t)drop.seed;
+  prm.seed_hi = (uint32_t)(drop.seed >> 32);
+  prm.drop_thr = drop.threshold;
+  prm.drop_scale = drop.threshold > 0 ? 256.0f / (float)drop.threshold : 0.f;
+  const bool dr = drop.active();
+  if (d == 64) return dr ? masked_d<E, 64, true>(prm, causal, stream) : masked_d<E, 64, false>(prm, causal, stream);
+  if (d == 128) return dr ? masked_d<E, 128, true>(prm, causal, stream) : masked_d<E, 128, false>(prm, causal, stream);
   return hipErrorInvalidValue;
 }
 }  // namespace
 
 hipError_t launch_bwd_masked(bool fp16, const void* q, const void* k, const void* v, const void* o, const float* lse,
                              const void* dout, float* delta, void* dq, void* dk, void* dv, int BH, int N, int d,
-                             float scale, bool causal, const Masks& masks, hipStream_t stream) {
-  return fp16 ? masked_typed<f16>(q, k, v, o, lse, dout, delta, dq, dk, dv, BH, N, d, scale, causal, masks, stream)
-              : masked_typed<bf16>(q, k, v, o, lse, dout, delta, dq, dk, dv, BH, N, d, scale, causal, masks, stream);
+                             float scale, bool causal, const Masks& masks, const Dropout& drop, hipStream_t stream) {
+  return fp16 ? masked_typed<f16>(q, k, v, o, lse, dout, delta, dq, dk, dv, BH, N, d, scale, causal, masks, drop, stream)
+              : masked_typed<bf16>(q, k, v, o, lse, dout, delta, dq, dk, dv, BH, N, d, scale, causal, masks, drop,
+                                   stream);
 }
 
 hipError_t launch_bwd_delta(bool fp16, const void* o, const void* dout, float* delta, int BH, int N, int d,

@@ -107,6 +107,56 @@ __device__ __forceinline__ float half_swap_sum(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Philox4x32-10, the counter-based generator of Salmon, Moraes, Dror and Shaw ("Parallel Random
+// Numbers: As Easy as 1, 2, 3", SC 2011): ten rounds, each two 32 x 32 -> 64-bit products of
+// counter words with fixed multipliers, the high halves xored with the other counter words and the
+// key, the key advanced by two Weyl increments between rounds.
+__device__ __forceinline__ void philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t k0,
+                                              uint32_t k1, uint32_t (&out)[4]) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    c1 = (uint32_t)p1;
+    c3 = (uint32_t)p0;
+    c0 = n0;
+    c2 = n2;
+    k0 += 0x9E3779B9u;
+    k1 += 0xBB67AE85u;
+  }
+  out[0] = c0;
+  out[1] = c1;
+  out[2] = c2;
+  out[3] = c3;
+}
+
+// Attention dropout's random bytes. Score element (row i, key j) of flattened head bh uses byte
+// j % 4 of word (j % 32) / 8 of Philox4x32-10 at counter (i, j / 32, bh, (j / 4) % 2) and key
+// (seed low, seed high); it is kept iff that byte is below the threshold T = round(256 (1 - p)).
+// In the transposed score layout (a lane holds query i and, for its half hf of a 32-key block,
+// register r = 4 g + e holds key 8 g + 4 hf + e) one call gives the lane's 16 bytes: register r
+// takes byte e of word g.
+__device__ __forceinline__ void dropout_words(int row, int block32, int head, int half, uint32_t seed_lo,
+                                              uint32_t seed_hi, uint32_t (&w)[4]) {
+  philox4x32_10((uint32_t)row, (uint32_t)block32, (uint32_t)head, (uint32_t)half, seed_lo, seed_hi, w);
+}
+__device__ __forceinline__ bool dropout_keep(uint32_t word, int byte, int thr) {
+  return (int)((word >> (8 * byte)) & 0xffu) < thr;
+}
+// 0xffff in each 16-bit half of a packed pair whose element is kept: the pair is bytes 2c, 2c + 1
+// of `word`; thr2 = T | T << 16. (Byte minus T is negative iff kept; an arithmetic shift spreads
+// the sign over the half.)
+typedef short i16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t dropout_pair_mask(uint32_t word, int c, uint32_t thr2) {
+  const uint32_t y = word >> (16 * c);
+  const uint32_t x = (y & 0xffu) | ((y & 0xff00u) << 8);
+  i16x2 d = __builtin_bit_cast(i16x2, x) - __builtin_bit_cast(i16x2, thr2);
+  d = d >> (i16x2){15, 15};
+  return __builtin_bit_cast(uint32_t, d);
+}
+
 // 16-byte global load / store helpers (addresses are 16-byte aligned by contract).
 __device__ __forceinline__ u32x4 ld_global16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void st_global16(void* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }

@@ -95,6 +95,11 @@ struct Fwd16Params {
   const uint8_t* block_mask;
   int heads;
   int n_kb;
+  // kMaskedDropout only: Philox key, keep threshold T (twice, one per 16-bit half) and 256 / T.
+  uint32_t seed_lo;
+  uint32_t seed_hi;
+  uint32_t drop_thr2;
+  float drop_scale;
 };
 
 // A block's per-lane probability sum above this bound means some probability may have left the
@@ -113,11 +118,15 @@ constexpr float kInitMax = -1e30f;
 //  kMasked: square, with optional per-sequence lengths (rows >= L of Q and K/V are padding) and
 //           an optional block-sparse map; the workgroup walks only the key blocks its map row
 //           enables. Rows that see no key get O = 0, LSE = -inf.
-enum FwdMode : int { kDense = 0, kSplit = 1, kMasked = 2 };
+//  kMaskedDropout: kMasked plus attention dropout: each probability that multiplies V is kept
+//           or zeroed by its Philox byte (dropout_words), kept ones scaled by 256 / T at the end;
+//           the row sums (hence LSE and the normaliser) are those of the undropped softmax.
+enum FwdMode : int { kDense = 0, kSplit = 1, kMasked = 2, kMaskedDropout = 3 };
 
 template <typename E, int D, int BC, int NW, bool CAUSAL, int MODE>
 __global__ __launch_bounds__(NW * 64, 2) void fwd16_kernel(Fwd16Params<E> p) {
-  constexpr bool KV_SPLIT = MODE == kSplit, MASKED = MODE == kMasked;
+  constexpr bool KV_SPLIT = MODE == kSplit, DROPOUT = MODE == kMaskedDropout;
+  constexpr bool MASKED = MODE == kMasked || DROPOUT;
   using H = Half16<E>;
   using e16x8 = typename H::x8;
   using e16x4 = typename H::x4;
@@ -295,9 +304,11 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd16_kernel(Fwd16Params<E> p) {
   // O^T += V^T P^T for V half `hv` (from p_in), and the probabilities of s_in (into p_out), with
   // their fp32 sum in rs and the sum of their 16-bit roundings in rr. The work is issued in a fixed
   // interleave, fenced by scheduling barriers.
+  uint32_t kw[4];  // dropout: the Philox words of the half whose probabilities are being formed
   auto phase = [&](auto with_pv, f32x16& s_out, const char* kbuf, int hs, const e16x8 (&p_in)[2],
-                   const char* vbuf, int hv, const f32x16& s_in, e16x8 (&p_out)[2]) __attribute__((always_inline)) {
+                   const char* vbuf, int hv, const f32x16& s_in, e16x8 (&p_out)[2], int jh) __attribute__((always_inline)) {
     constexpr bool PV = decltype(with_pv)::value;
+    if constexpr (DROPOUT) dropout_words(q, jh, head, hf, p.seed_lo, p.seed_hi, kw);
     constexpr int NS = NKK, NPV = PV ? 2 * NDB : 0, NM = NS + NPV;
     auto frag = [&](int i) __attribute__((always_inline)) -> e16x8 {
       if (i < NS) return lds_read16<E>(kbuf, T::chunk_off(32 * hs + lq, 2 * i + hf));
@@ -328,8 +339,10 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd16_kernel(Fwd16Params<E> p) {
         asm volatile("" ::"v"(a0));
       } else {
         a1 += pv[k];
-        const e16x2 pr = {(E)pv[k - 1], (E)pv[k]};
-        r0 = H::dot2_ones(pr, r0);
+        e16x2 pr = {(E)pv[k - 1], (E)pv[k]};
+        r0 = H::dot2_ones(pr, r0);  // l~ sums the undropped probabilities
+        if constexpr (DROPOUT)
+          pr = __builtin_bit_cast(e16x2, __builtin_bit_cast(uint32_t, pr) & dropout_pair_mask(kw[k >> 2], (k >> 1) & 1, p.drop_thr2));
         p_out[t][e - 1] = pr[0];
         p_out[t][e] = pr[1];
         asm volatile("" ::"v"(a1), "v"(r0), "v"(pr));
@@ -377,8 +390,10 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd16_kernel(Fwd16Params<E> p) {
         const float pb = fast_exp2(fmaf(s[8 * t + e + 1], c, neg_m));
         a0 += pa;
         a1 += pb;
-        const e16x2 pr = {(E)pa, (E)pb};
+        e16x2 pr = {(E)pa, (E)pb};
         r0 = H::dot2_ones(pr, r0);
+        if constexpr (DROPOUT)
+          pr = __builtin_bit_cast(e16x2, __builtin_bit_cast(uint32_t, pr) & dropout_pair_mask(kw[t * 2 + (e >> 2)], (e >> 1) & 1, p.drop_thr2));
         pk[t][e] = pr[0];
         pk[t][e + 1] = pr[1];
       }
@@ -414,12 +429,12 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd16_kernel(Fwd16Params<E> p) {
   using no = std::integral_constant<bool, false>;
   auto phase_a = [&](int j, const char* kbuf, const char* vprev, auto with_pv) __attribute__((always_inline)) {
     mask_half(s0, j, 0);
-    phase(with_pv, s1, kbuf, 1, p1, vprev, 1, s0, p0);
+    phase(with_pv, s1, kbuf, 1, p1, vprev, 1, s0, p0, 2 * j);
     settle(s0, p0);
   };
   auto phase_b = [&](int j, const char* knext, const char* vcur) __attribute__((always_inline)) {
     mask_half(s1, j, 1);
-    phase(yes{}, s0, knext, 0, p0, vcur, 0, s1, p1);
+    phase(yes{}, s0, knext, 0, p0, vcur, 0, s1, p1, 2 * j + 1);
     settle(s1, p1);
   };
   // K(j) and V(j) live in buffer j % 2. K(j+2) / V(j+1) are issued right after the barrier that
@@ -486,6 +501,7 @@ __global__ __launch_bounds__(NW * 64, 2) void fwd16_kernel(Fwd16Params<E> p) {
   if (MASKED) {
     // padding rows, and rows whose visible keys all fell in disabled blocks or the causal mask
     const bool empty = q >= Lq || half_swap_sum(lr_run) == 0.f;
+    if (DROPOUT) inv *= p.drop_scale;
     inv = empty ? 0.f : inv;
     lse_row = empty ? -INFINITY : lse_row;
 #pragma unroll
@@ -517,6 +533,7 @@ struct FwdExtra {
   float* opart = nullptr;
   float* lsepart = nullptr;
   Masks masks;
+  Dropout drop;
 };
 
 template <typename E, int MODE>
@@ -546,6 +563,10 @@ static hipError_t launch_typed(const void* q, const void* k, const void* v, void
   prm.block_mask = x.masks.block_mask;
   prm.heads = x.masks.heads;
   prm.n_kb = (N + kMaskBlock - 1) / kMaskBlock;
+  prm.seed_lo = (uint32_t)x.drop.seed;
+  prm.seed_hi = (uint32_t)(x.drop.seed >> 32);
+  prm.drop_thr2 = (uint32_t)x.drop.threshold | ((uint32_t)x.drop.threshold << 16);
+  prm.drop_scale = x.drop.threshold > 0 ? 256.0f / (float)x.drop.threshold : 0.f;
   if (d == 64)
     return causal ? launch_cfg<E, 64, 64, NW, true, MODE>(prm, x.n_splits, stream)
                   : launch_cfg<E, 64, 64, NW, false, MODE>(prm, x.n_splits, stream);
@@ -564,10 +585,15 @@ hipError_t launch_fwd_16(bool fp16, const void* q, const void* k, const void* v,
 }
 
 hipError_t launch_fwd_16_masked(bool fp16, const void* q, const void* k, const void* v, void* o, float* lse, int BH,
-                                int N, int d, float scale, bool causal, const Masks& masks, hipStream_t stream) {
+                                int N, int d, float scale, bool causal, const Masks& masks, const Dropout& drop,
+                                hipStream_t stream) {
   FwdExtra x;
   x.Nk = N;
   x.masks = masks;
+  x.drop = drop;
+  if (drop.active())
+    return fp16 ? launch_typed<f16, kMaskedDropout>(q, k, v, o, lse, BH, N, d, scale, causal, x, stream)
+                : launch_typed<bf16, kMaskedDropout>(q, k, v, o, lse, BH, N, d, scale, causal, x, stream);
   return fp16 ? launch_typed<f16, kMasked>(q, k, v, o, lse, BH, N, d, scale, causal, x, stream)
               : launch_typed<bf16, kMasked>(q, k, v, o, lse, BH, N, d, scale, causal, x, stream);
 }

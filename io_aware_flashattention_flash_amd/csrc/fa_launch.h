@@ -19,6 +19,14 @@ struct Masks {
   int heads = 1;
 };
 
+// Attention dropout: keep iff the element's Philox byte < threshold (256 keeps everything; the
+// kernels then take their dropout-free path).
+struct Dropout {
+  uint64_t seed = 0;
+  int threshold = 256;
+  bool active() const { return threshold < 256; }
+};
+
 // Forward, 16-bit storage: bf16 (fp16 = false) or IEEE fp16 (fp16 = true). BH = B*H. d in {64, 128}.
 hipError_t launch_fwd_16(bool fp16, const void* q, const void* k, const void* v, void* o, float* lse,
                          int BH, int N, int d, float scale, bool causal, hipStream_t stream);
@@ -27,7 +35,10 @@ hipError_t launch_fwd_16(bool fp16, const void* q, const void* k, const void* v,
 // LSE = -inf).
 hipError_t launch_fwd_16_masked(bool fp16, const void* q, const void* k, const void* v, void* o, float* lse,
                                 int BH, int N, int d, float scale, bool causal, const Masks& masks,
-                                hipStream_t stream);
+                                const Dropout& drop, hipStream_t stream);
+
+// Writes the dropout keep mask (1 kept, 0 dropped) of every score element, uint8 [BH][Nq][Nk].
+hipError_t launch_dropout_mask(uint8_t* keep, int BH, int Nq, int Nk, const Dropout& drop, hipStream_t stream);
 
 // Key-split forward (Nq = N query rows against Nk >= N key rows; causal: query i sees keys
 // j <= i + L - N, L = the sequence's cache length, Nk without seqlens_k). The K/V tiles are dealt to
@@ -59,7 +70,7 @@ hipError_t launch_bwd_dq(bool fp16, const void* q, const void* k, const void* v,
 hipError_t launch_bwd_masked(bool fp16, const void* q, const void* k, const void* v, const void* o,
                              const float* lse, const void* dout, float* delta, void* dq, void* dk, void* dv,
                              int BH, int N, int d, float scale, bool causal, const Masks& masks,
-                             hipStream_t stream);
+                             const Dropout& drop, hipStream_t stream);
 
 // Work decomposition shared by the kernels: workgroup id -> (head, tile).
 // The hardware hands consecutive workgroup ids to the 8 XCDs round-robin, each with its own L2.

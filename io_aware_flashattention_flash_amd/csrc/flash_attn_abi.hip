@@ -73,6 +73,16 @@ fa_status_t check_masks(int N, const int32_t* seqlens, const uint8_t* block_mask
   return FA_OK;
 }
 
+// Dropout probability -> keep threshold T = round(256 (1 - p)); T must be >= 1 (p below 511/512).
+fa_status_t dropout_plan(float p, uint64_t seed, fa::Dropout* out) {
+  if (!isfinite(p) || p < 0.f || p > 1.f) return FA_ERR_BAD_DROPOUT;
+  const int t = (int)floor(256.0 * (1.0 - (double)p) + 0.5);
+  if (t < 1) return FA_ERR_BAD_DROPOUT;
+  out->seed = seed;
+  out->threshold = t;
+  return FA_OK;
+}
+
 fa_status_t check_kvsplit_shape(int B, int H, int Nq, int Nk, int d, int num_splits) {
   fa_status_t st = check_shape(B, H, Nq, d);
   if (st != FA_OK) return st;
@@ -112,7 +122,8 @@ size_t flash_attn_fwd_kvsplit_workspace_size(int B, int H, int Nq, int Nk, int d
 
 fa_status_t flash_attn_fwd_masked(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                                   int N, int d, float scale, int causal, const int32_t* seqlens,
-                                  const uint8_t* block_mask, int dtype, void* stream) {
+                                  const uint8_t* block_mask, float dropout_p, uint64_t seed, int dtype,
+                                  void* stream) {
   if (!q || !k || !v || !o) return FA_ERR_NULL_POINTER;
   fa_status_t st = check_shape(B, H, N, d);
   if (st != FA_OK) return st;
@@ -122,12 +133,15 @@ fa_status_t flash_attn_fwd_masked(const void* q, const void* k, const void* v, v
     return FA_ERR_MISALIGNED;
   st = check_masks(N, seqlens, block_mask);
   if (st != FA_OK) return st;
+  fa::Dropout drop;
+  st = dropout_plan(dropout_p, seed, &drop);
+  if (st != FA_OK) return st;
   fa::Masks m;
   m.seqlens = seqlens;
   m.block_mask = block_mask;
   m.heads = H;
   hipError_t e = fa::launch_fwd_16_masked(dtype == FA_DTYPE_FP16, q, k, v, o, lse, B * H, N, d, scale, causal != 0, m,
-                                          static_cast<hipStream_t>(stream));
+                                          drop, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
@@ -234,7 +248,8 @@ fa_status_t flash_attn_bwd(const void* q, const void* k, const void* v, const vo
 fa_status_t flash_attn_bwd_masked(const void* q, const void* k, const void* v, const void* o, const float* lse,
                                   const void* dout, void* dq, void* dk, void* dv, void* workspace,
                                   size_t workspace_bytes, int B, int H, int N, int d, float scale, int causal,
-                                  const int32_t* seqlens, const uint8_t* block_mask, int dtype, void* stream) {
+                                  const int32_t* seqlens, const uint8_t* block_mask, float dropout_p,
+                                  uint64_t seed, int dtype, void* stream) {
   if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FA_ERR_NULL_POINTER;
   fa_status_t st = check_bwd_common(B, H, N, d, scale, dtype);
   if (st != FA_OK) return st;
@@ -243,6 +258,9 @@ fa_status_t flash_attn_bwd_masked(const void* q, const void* k, const void* v, c
     return FA_ERR_MISALIGNED;
   st = check_masks(N, seqlens, block_mask);
   if (st != FA_OK) return st;
+  fa::Dropout drop;
+  st = dropout_plan(dropout_p, seed, &drop);
+  if (st != FA_OK) return st;
   if (!workspace || workspace_bytes < flash_attn_bwd_workspace_size(B, H, N, d, dtype)) return FA_ERR_WORKSPACE;
   if (!aligned16(workspace)) return FA_ERR_MISALIGNED;
   fa::Masks m;
@@ -250,7 +268,19 @@ fa_status_t flash_attn_bwd_masked(const void* q, const void* k, const void* v, c
   m.block_mask = block_mask;
   m.heads = H;
   hipError_t e = fa::launch_bwd_masked(dtype == FA_DTYPE_FP16, q, k, v, o, lse, dout, static_cast<float*>(workspace),
-                                       dq, dk, dv, B * H, N, d, scale, causal != 0, m, static_cast<hipStream_t>(stream));
+                                       dq, dk, dv, B * H, N, d, scale, causal != 0, m, drop,
+                                       static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+fa_status_t flash_attn_dropout_mask(uint8_t* keep, int B, int H, int Nq, int Nk, float dropout_p, uint64_t seed,
+                                    void* stream) {
+  if (!keep) return FA_ERR_NULL_POINTER;
+  if (B < 1 || H < 1 || Nq < 1 || Nk < 1 || (int64_t)B * H * Nq * Nk >= ((int64_t)1 << 40)) return FA_ERR_BAD_SHAPE;
+  fa::Dropout drop;
+  fa_status_t st = dropout_plan(dropout_p, seed, &drop);
+  if (st != FA_OK) return st;
+  hipError_t e = fa::launch_dropout_mask(keep, B * H, Nq, Nk, drop, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
@@ -264,6 +294,7 @@ const char* flash_attn_status_string(int status) {
     case FA_ERR_MISALIGNED: return "FA_ERR_MISALIGNED: pointers must be 16-byte aligned (lse 4-byte)";
     case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace missing or smaller than flash_attn_bwd_workspace_size()";
     case FA_ERR_HIP: return "FA_ERR_HIP: the HIP runtime reported a launch error";
+    case FA_ERR_BAD_DROPOUT: return "FA_ERR_BAD_DROPOUT: dropout_p must be finite and in [0, 511/512]";
     default: return "unknown flash_attn status";
   }
 }

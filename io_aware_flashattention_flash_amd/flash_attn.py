@@ -26,7 +26,7 @@ FA_MASK_BLOCK = 128  # rows and keys per block-sparse map entry
 _DTYPES = {torch.float32: FA_DTYPE_FP32, torch.bfloat16: FA_DTYPE_BF16, torch.float16: FA_DTYPE_FP16}
 
 # Names and C signatures of every exported entry point (mirrors include/flash_attn.h).
-_vp, _int, _float, _size = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+_vp, _int, _float, _size, _u64 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t, ctypes.c_uint64
 SIGNATURES = {
     "flash_attn_fwd": (_int, [_vp, _vp, _vp, _vp, _vp, _int, _int, _int, _int, _float, _int, _int, _vp]),
     "flash_attn_bwd_workspace_size": (_size, [_int, _int, _int, _int, _int]),
@@ -41,9 +41,10 @@ SIGNATURES = {
     "flash_attn_fwd_kvsplit": (_int, [_vp, _vp, _vp, _vp, _vp, _int, _int, _int, _int, _int, _float, _int, _vp,
                                       _int, _vp, _size, _int, _vp]),
     "flash_attn_fwd_masked": (_int, [_vp, _vp, _vp, _vp, _vp, _int, _int, _int, _int, _float, _int, _vp, _vp,
-                                     _int, _vp]),
+                                     _float, _u64, _int, _vp]),
     "flash_attn_bwd_masked": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _size,
-                                     _int, _int, _int, _int, _float, _int, _vp, _vp, _int, _vp]),
+                                     _int, _int, _int, _int, _float, _int, _vp, _vp, _float, _u64, _int, _vp]),
+    "flash_attn_dropout_mask": (_int, [_vp, _int, _int, _int, _int, _float, _u64, _vp]),
     "flash_attn_status_string": (ctypes.c_char_p, [_int]),
 }
 
@@ -147,11 +148,12 @@ def _check_block_mask(t: Optional[torch.Tensor], B: int, H: int, N: int, ref: to
 def flash_attn_fwd_masked(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: Optional[float] = None,
                           causal: bool = False, seqlens: Optional[torch.Tensor] = None,
                           block_mask: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
-                          lse: Optional[torch.Tensor] = None, want_lse: bool = True
-                          ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
-    """Forward with per-sequence lengths (int32 [B]: rows >= L_b of Q, K, V are padding) and/or a
-    block-sparse map (uint8 / bool [B, H, ceil(N/128), ceil(N/128)], zero = block skipped). Rows
-    that see no key get O = 0, LSE = -inf."""
+                          lse: Optional[torch.Tensor] = None, want_lse: bool = True, dropout_p: float = 0.0,
+                          seed: int = 0) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Forward with per-sequence lengths (int32 [B]: rows >= L_b of Q, K, V are padding), a
+    block-sparse map (uint8 / bool [B, H, ceil(N/128), ceil(N/128)], zero = block skipped) and/or
+    attention dropout (probability dropout_p, Philox key `seed`). Rows that see no key get O = 0,
+    LSE = -inf."""
     _check_tensor("q", q)
     _check_tensor("k", k, q)
     _check_tensor("v", v, q)
@@ -168,8 +170,8 @@ def flash_attn_fwd_masked(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, sca
     if lse is not None:
         _check_rows("lse", lse, q)
     st = load_library().flash_attn_fwd_masked(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, N, d, scale,
-                                              int(bool(causal)), _ptr(seqlens), _ptr(block_mask), _DTYPES[q.dtype],
-                                              _stream_handle(q))
+                                              int(bool(causal)), _ptr(seqlens), _ptr(block_mask), float(dropout_p),
+                                              int(seed) & (2 ** 64 - 1), _DTYPES[q.dtype], _stream_handle(q))
     _check(st)
     return out, lse
 
@@ -178,9 +180,9 @@ def flash_attn_bwd_masked(dout: torch.Tensor, q: torch.Tensor, k: torch.Tensor, 
                           lse: torch.Tensor, scale: Optional[float] = None, causal: bool = False,
                           seqlens: Optional[torch.Tensor] = None, block_mask: Optional[torch.Tensor] = None,
                           dq: Optional[torch.Tensor] = None, dk: Optional[torch.Tensor] = None,
-                          dv: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None
-                          ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
-    """Backward of flash_attn_fwd_masked (same seqlens and block_mask)."""
+                          dv: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                          dropout_p: float = 0.0, seed: int = 0) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """Backward of flash_attn_fwd_masked (same seqlens, block_mask, dropout_p and seed)."""
     _check_tensor("q", q)
     for name, t in (("k", k), ("v", v), ("o", o), ("dout", dout)):
         _check_tensor(name, t, q)
@@ -203,10 +205,25 @@ def flash_attn_bwd_masked(dout: torch.Tensor, q: torch.Tensor, k: torch.Tensor, 
     ws_bytes = workspace.numel() * workspace.element_size()
     st = load_library().flash_attn_bwd_masked(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
                                               _ptr(dk), _ptr(dv), _ptr(workspace), ws_bytes, B, H, N, d, scale,
-                                              int(bool(causal)), _ptr(seqlens), _ptr(block_mask), dt,
-                                              _stream_handle(q))
+                                              int(bool(causal)), _ptr(seqlens), _ptr(block_mask), float(dropout_p),
+                                              int(seed) & (2 ** 64 - 1), dt, _stream_handle(q))
     _check(st)
     return dq, dk, dv
+
+
+def flash_attn_dropout_mask(B: int, H: int, Nq: int, Nk: int, dropout_p: float, seed: int,
+                            device="cuda", out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The keep mask (uint8 [B, H, Nq, Nk], 1 = kept) that flash_attn_fwd_masked applies for
+    (dropout_p, seed)."""
+    if out is None:
+        out = torch.empty((B, H, Nq, Nk), dtype=torch.uint8, device=device)
+    if out.dtype != torch.uint8 or tuple(out.shape) != (B, H, Nq, Nk) or not out.is_contiguous() \
+            or out.device.type != "cuda":
+        raise ValueError("out must be a contiguous uint8 [B, H, Nq, Nk] GPU tensor")
+    st = load_library().flash_attn_dropout_mask(_ptr(out), B, H, Nq, Nk, float(dropout_p), int(seed) & (2 ** 64 - 1),
+                                                _stream_handle(out))
+    _check(st)
+    return out
 
 
 def flash_attn_fwd_kvsplit(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: Optional[float] = None,

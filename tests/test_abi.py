@@ -15,7 +15,7 @@ from io_aware_flashattention_flash_amd import flash_attn as fa
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "flash_attn.h")
 
-OK, NULLP, SHAPE, UNSUP, SCALE, ALIGN, WS, HIP = range(8)
+OK, NULLP, SHAPE, UNSUP, SCALE, ALIGN, WS, HIP, DROP = range(9)
 A = 0x10000  # a 16-byte-aligned fake address; never dereferenced (validation fails first)
 
 
@@ -52,7 +52,7 @@ def test_exports_have_c_linkage():
 
 
 def test_status_strings(lib):
-    for s in range(8):
+    for s in range(9):
         txt = fa.flash_attn_status_string(s)
         assert txt.startswith("FA_"), txt
     assert "unknown" in fa.flash_attn_status_string(99)
@@ -187,14 +187,15 @@ def test_kvsplit_validation(lib):
     assert _kvs(lib, seqlens_k=A + 2) == ALIGN       # int32 lengths: 4-byte aligned
 
 
-def _fm(lib, q=A, k=A, v=A, o=A, lse=A, B=1, H=1, N=8, d=64, scale=0.125, causal=0, seqlens=None, bm=None, dtype=1):
-    return lib.flash_attn_fwd_masked(q, k, v, o, lse, B, H, N, d, scale, causal, seqlens, bm, dtype, None)
+def _fm(lib, q=A, k=A, v=A, o=A, lse=A, B=1, H=1, N=8, d=64, scale=0.125, causal=0, seqlens=None, bm=None, p=0.0,
+        seed=0, dtype=1):
+    return lib.flash_attn_fwd_masked(q, k, v, o, lse, B, H, N, d, scale, causal, seqlens, bm, p, seed, dtype, None)
 
 
 def _bm(lib, q=A, k=A, v=A, o=A, lse=A, do=A, dq=A, dk=A, dv=A, ws=A, ws_bytes=1 << 20, B=1, H=1, N=8, d=64,
-        scale=0.125, causal=0, seqlens=None, bmask=None, dtype=1):
+        scale=0.125, causal=0, seqlens=None, bmask=None, p=0.0, seed=0, dtype=1):
     return lib.flash_attn_bwd_masked(q, k, v, o, lse, do, dq, dk, dv, ws, ws_bytes, B, H, N, d, scale, causal, seqlens,
-                                     bmask, dtype, None)
+                                     bmask, p, seed, dtype, None)
 
 
 def test_masked_validation(lib):
@@ -213,6 +214,19 @@ def test_masked_validation(lib):
     assert _fm(lib, N=1024 * 128 + 1, q=A + 8) == ALIGN  # without a map the length is fine
     assert _bm(lib, ws=None) == WS
     assert _bm(lib, lse=None) == NULLP
+    for call in (_fm, _bm):
+        for bad in (-0.1, 1.0, 0.999, math.nan, math.inf):
+            assert call(lib, p=bad, k=A + 8 if call is _fm else A) in (DROP, ALIGN), bad
+        assert call(lib, p=-0.1) == DROP and call(lib, p=1.0) == DROP and call(lib, p=math.nan) == DROP
+        assert call(lib, p=0.998, q=A + 8) == ALIGN   # T = round(256 * 0.002) = 1 is allowed
+        assert call(lib, p=0.5, seed=2 ** 64 - 1, q=A + 8) == ALIGN
+
+
+def test_dropout_mask_validation(lib):
+    assert lib.flash_attn_dropout_mask(None, 1, 1, 4, 4, 0.5, 1, None) == NULLP
+    assert lib.flash_attn_dropout_mask(A, 0, 1, 4, 4, 0.5, 1, None) == SHAPE
+    assert lib.flash_attn_dropout_mask(A, 1, 1, 4, 0, 0.5, 1, None) == SHAPE
+    assert lib.flash_attn_dropout_mask(A, 1, 1, 4, 4, 1.5, 1, None) == DROP
 
 
 def test_kvsplit_workspace_size(lib):

@@ -353,6 +353,17 @@ def main():
             extras[r["workload"]] = r
         r = time_dropout_step(4, 16, 2048, 64, 0.1, dev)
         extras[r["workload"]] = r
+        # head dims beyond 64 / 128: the causal forward at the 4096-token shape (same tokens x d as
+        # the d = 128 workload) and the headline fwd+bwd step shape
+        for d in (32, 96, 256):
+            fw = inputs.Workload(f"fwd_bf16_b2h32n4096d{d}_causal", "bf16", 2, 32, 4096, d, True, False)
+            extras[fw.name] = time_forward(fw.name, None, 10, dev, to_dev, wl=fw)
+            bw = inputs.Workload(f"fwdbwd_bf16_b4h16n2048d{d}_causal", "bf16", 4, 16, 2048, d, True, True)
+            ms, km = time_fwdbwd(bw, inputs.make_inputs(bw), 30, 5, dev, to_dev)
+            extras[bw.name] = {"workload": bw.name, "pass": "fwd+bwd", "us": round(ms * 1e3, 2),
+                               "tflops": round((bw.fwd_flops() + bw.bwd_flops()) / (ms * 1e-3) / 1e12, 1),
+                               "kernels_us": {n: round(t * 1e3, 2) for n, t in km.items()}}
+            torch.cuda.empty_cache()
         torch.cuda.empty_cache()
 
     # ------------------------------------------------------------------ CPU oracle baseline

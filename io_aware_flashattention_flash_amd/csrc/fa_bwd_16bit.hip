@@ -87,12 +87,15 @@ __device__ __forceinline__ int build_block_list(const uint8_t* map, size_t strid
 // ---------------------------------------------------------------------------------------------
 // 1. delta = rowsum(dO * O)
 // ---------------------------------------------------------------------------------------------
+template <int X>
+constexpr int pow2_at_least() { int t = 1; while (t < X) t *= 2; return t; }
+
 template <typename E, int D>
 __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdParams<E> p) {
   using e16x8 = typename Half16<E>::x8;
-  constexpr int TPR = D / 8;               // threads per row, one 16-byte chunk each
-  constexpr int RPI = 256 / TPR;           // rows per block per step
-  constexpr int STEPS = 4;                 // rows per thread (independent loads in flight)
+  constexpr int TPR = pow2_at_least<D / 8>();  // threads per row, one 16-byte chunk each (idle beyond D)
+  constexpr int RPI = 256 / TPR;               // rows per block per step
+  constexpr int STEPS = 4;                     // rows per thread (independent loads in flight)
   const int tid = threadIdx.x;
   const long rows = (long)p.nh * p.N;
   const long row0 = (long)blockIdx.x * RPI * STEPS + tid / TPR;
@@ -103,7 +106,7 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdParams<E> p) {
     const long row = row0 + (long)i * RPI;
     a[i] = u32x4{0, 0, 0, 0};
     b[i] = u32x4{0, 0, 0, 0};
-    if (row < rows) {
+    if (row < rows && 8 * c < D) {
       a[i] = ld_global16(p.o + row * D + 8 * c);
       b[i] = ld_global16(p.dout + row * D + 8 * c);
     }
@@ -372,7 +375,7 @@ __global__ __launch_bounds__(NW * 64, (D > 64 ? 1 : 2)) void bwd_dkdv_kernel(Bwd
 // DROPOUT (with MASKED): dS = P * (dP * keep * 256 / T - delta), the keep mask regenerated in
 // the forward's layout.
 template <typename E, int D, int BC, int NW, bool CAUSAL, bool MASKED, bool DROPOUT>
-__global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdParams<E> p) {
+__global__ __launch_bounds__(NW * 64, D > 128 ? 1 : 2) void bwd_dq_kernel(BwdParams<E> p) {
   using H = Half16<E>;
   using e16x8 = typename H::x8;
   using e16x4 = typename H::x4;
@@ -579,12 +582,12 @@ __global__ __launch_bounds__(NW * 64, 2) void bwd_dq_kernel(BwdParams<E> p) {
 // host side
 // ---------------------------------------------------------------------------------------------
 namespace {
-// dQ kernel: 4 waves x 32 query rows; key tiles of 64 (32 at d = 128, where the score and
-// dP blocks of a 64-key tile would not fit beside the operands in 256 VGPRs).
+// dQ kernel: 4 waves x 32 query rows; key tiles of 64 (32 at d >= 128, where the score and
+// dP blocks of a 64-key tile would not fit beside the operands).
 // dK/dV kernel: 4 waves x 32 keys; query tiles of 64.
 constexpr int kDqNW = 4, kKvNW = 4, kKvBQ = 64;
 template <int D>
-constexpr int dq_bc() { return D == 128 ? 32 : 64; }
+constexpr int dq_bc() { return D >= 128 ? 32 : 64; }
 
 template <typename E>
 BwdParams<E> make_params(const void* q, const void* k, const void* v, const void* o, const float* lse,
@@ -619,7 +622,7 @@ BwdParams<E> make_params(const void* q, const void* k, const void* v, const void
 
 template <typename E, int D>
 hipError_t delta_d(BwdParams<E> prm, hipStream_t stream) {
-  constexpr int RPB = 256 / (D / 8) * 4;  // rows per block (4 per thread group)
+  constexpr int RPB = 256 / pow2_at_least<D / 8>() * 4;  // rows per block (4 per thread group)
   const long rows = (long)prm.nh * prm.N;
   hipLaunchKernelGGL((bwd_delta_kernel<E, D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0, stream, prm);
   return hipGetLastError();
@@ -649,9 +652,7 @@ template <typename E>
 hipError_t delta_typed(const void* o, const void* dout, float* delta, int BH, int N, int d, hipStream_t stream) {
   BwdParams<E> prm = make_params<E>(nullptr, nullptr, nullptr, o, nullptr, dout, delta, nullptr, nullptr, nullptr, BH,
                                     N, 1.f);
-  if (d == 64) return delta_d<E, 64>(prm, stream);
-  if (d == 128) return delta_d<E, 128>(prm, stream);
-  return hipErrorInvalidValue;
+  return with_head_dim(d, [&](auto dd) { return delta_d<E, decltype(dd)::value>(prm, stream); });
 }
 
 template <typename E>
@@ -659,18 +660,20 @@ hipError_t dkdv_typed(const void* q, const void* k, const void* v, const float* 
                       const float* delta, void* dk, void* dv, int BH, int N, int d, float scale, bool causal,
                       hipStream_t stream) {
   BwdParams<E> prm = make_params<E>(q, k, v, nullptr, lse, dout, delta, nullptr, dk, dv, BH, N, scale);
-  if (d == 64) return causal ? dkdv_d<E, 64, true>(prm, stream) : dkdv_d<E, 64, false>(prm, stream);
-  if (d == 128) return causal ? dkdv_d<E, 128, true>(prm, stream) : dkdv_d<E, 128, false>(prm, stream);
-  return hipErrorInvalidValue;
+  return with_head_dim(d, [&](auto dd) {
+    constexpr int D = decltype(dd)::value;
+    return causal ? dkdv_d<E, D, true>(prm, stream) : dkdv_d<E, D, false>(prm, stream);
+  });
 }
 
 template <typename E>
 hipError_t dq_typed(const void* q, const void* k, const void* v, const void* o, const float* lse, const void* dout,
                     float* delta, void* dq, int BH, int N, int d, float scale, bool causal, hipStream_t stream) {
   BwdParams<E> prm = make_params<E>(q, k, v, o, lse, dout, delta, dq, nullptr, nullptr, BH, N, scale);
-  if (d == 64) return causal ? dq_d<E, 64, true>(prm, stream) : dq_d<E, 64, false>(prm, stream);
-  if (d == 128) return causal ? dq_d<E, 128, true>(prm, stream) : dq_d<E, 128, false>(prm, stream);
-  return hipErrorInvalidValue;
+  return with_head_dim(d, [&](auto dd) {
+    constexpr int D = decltype(dd)::value;
+    return causal ? dq_d<E, D, true>(prm, stream) : dq_d<E, D, false>(prm, stream);
+  });
 }
 template <typename E, int D, bool DROPOUT>
 hipError_t masked_d(const BwdParams<E>& prm, bool causal, hipStream_t stream) {
@@ -692,9 +695,10 @@ hipError_t masked_typed(const void* q, const void* k, const void* v, const void*
   prm.drop_thr = drop.threshold;
   prm.drop_scale = drop.threshold > 0 ? 256.0f / (float)drop.threshold : 0.f;
   const bool dr = drop.active();
-  if (d == 64) return dr ? masked_d<E, 64, true>(prm, causal, stream) : masked_d<E, 64, false>(prm, causal, stream);
-  if (d == 128) return dr ? masked_d<E, 128, true>(prm, causal, stream) : masked_d<E, 128, false>(prm, causal, stream);
-  return hipErrorInvalidValue;
+  return with_head_dim(d, [&](auto dd) {
+    constexpr int D = decltype(dd)::value;
+    return dr ? masked_d<E, D, true>(prm, causal, stream) : masked_d<E, D, false>(prm, causal, stream);
+  });
 }
 }  // namespace
 

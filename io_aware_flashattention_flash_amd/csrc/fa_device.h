@@ -164,13 +164,24 @@ __device__ __forceinline__ void st_global16(void* p, u32x4 v) { *reinterpret_cas
 // Row-major 16-bit tile of ROWS x D in LDS, stored as 16-byte chunks with an XOR swizzle so that
 // (a) 16 consecutive rows read at the same logical chunk, and (b) 4 consecutive rows times 4
 // consecutive chunks (the transpose-read pattern), both land on distinct 16-byte bank groups.
+//
+// The XOR value depends on the head dim (chunks per row):
+//   4, 8, 16 chunks: rows are grouped by 256-byte bank line; the value combines the row's line and
+//                    quarter so both patterns above spread over all 16 bank groups;
+//   12 chunks:       (row / 4) % 4 flips only the low two chunk bits (the row stays inside its 12
+//                    chunks); the 192-byte row stride already puts 4 consecutive rows in distinct
+//                    quarters of a bank line, and the XOR separates the 4 rows within a quarter;
+//   32 chunks:       4 (row % 4) + (row / 4) % 4, a different low-4-bit value for each of 16 rows.
 template <int D>
 struct SwizzledTile {
   static constexpr int kChunks = D / 8;                       // 16-byte chunks per row
   static constexpr int kRowsPerLine = kChunks >= 16 ? 1 : 16 / kChunks;  // rows per 256-byte bank line
   static constexpr int kQuarter = kChunks / 4;
-  static_assert(kChunks == 8 || kChunks == 16, "D must be 64 or 128");
+  static_assert(kChunks == 4 || kChunks == 8 || kChunks == 12 || kChunks == 16 || kChunks == 32,
+                "D must be 32, 64, 96, 128 or 256");
   __device__ __forceinline__ static int swz(int row) {
+    if constexpr (kChunks == 12) return (row >> 2) & 3;
+    if constexpr (kChunks == 32) return 4 * (row & 3) + ((row >> 2) & 3);
     int m = row / kRowsPerLine;
     return 4 * (m % kQuarter) + (m / kQuarter) % 4;
   }

@@ -123,8 +123,10 @@ constexpr float kInitMax = -1e30f;
 //           the row sums (hence LSE and the normaliser) are those of the undropped softmax.
 enum FwdMode : int { kDense = 0, kSplit = 1, kMasked = 2, kMaskedDropout = 3 };
 
+// d = 256 needs more than half the register file per lane (O accumulator 128, Q operand 64): one
+// workgroup per CU, one wave per SIMD. Smaller head dims run two workgroups per CU.
 template <typename E, int D, int BC, int NW, bool CAUSAL, int MODE>
-__global__ __launch_bounds__(NW * 64, 2) void fwd16_kernel(Fwd16Params<E> p) {
+__global__ __launch_bounds__(NW * 64, D > 128 ? 1 : 2) void fwd16_kernel(Fwd16Params<E> p) {
   constexpr bool KV_SPLIT = MODE == kSplit, DROPOUT = MODE == kMaskedDropout;
   constexpr bool MASKED = MODE == kMasked || DROPOUT;
   using H = Half16<E>;
@@ -567,13 +569,11 @@ static hipError_t launch_typed(const void* q, const void* k, const void* v, void
   prm.seed_hi = (uint32_t)(x.drop.seed >> 32);
   prm.drop_thr2 = (uint32_t)x.drop.threshold | ((uint32_t)x.drop.threshold << 16);
   prm.drop_scale = x.drop.threshold > 0 ? 256.0f / (float)x.drop.threshold : 0.f;
-  if (d == 64)
-    return causal ? launch_cfg<E, 64, 64, NW, true, MODE>(prm, x.n_splits, stream)
-                  : launch_cfg<E, 64, 64, NW, false, MODE>(prm, x.n_splits, stream);
-  if (d == 128)
-    return causal ? launch_cfg<E, 128, 64, NW, true, MODE>(prm, x.n_splits, stream)
-                  : launch_cfg<E, 128, 64, NW, false, MODE>(prm, x.n_splits, stream);
-  return hipErrorInvalidValue;
+  return with_head_dim(d, [&](auto dd) {
+    constexpr int D = decltype(dd)::value;
+    return causal ? launch_cfg<E, D, 64, NW, true, MODE>(prm, x.n_splits, stream)
+                  : launch_cfg<E, D, 64, NW, false, MODE>(prm, x.n_splits, stream);
+  });
 }
 
 hipError_t launch_fwd_16(bool fp16, const void* q, const void* k, const void* v, void* o, float* lse, int BH, int N,
@@ -614,8 +614,7 @@ __global__ __launch_bounds__(256) void kvsplit_merge_kernel(const float* opart, 
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
   if (mx == -INFINITY) {  // the row sees no key in any split (cache shorter than its position)
-#pragma unroll
-    for (int c = 0; c < D / 64; ++c) o[(size_t)row * D + l + 64 * c] = (E)0.f;
+    for (int c = l; c < D; c += 64) o[(size_t)row * D + c] = (E)0.f;
     if (l == 0 && lse) lse[row] = -INFINITY;
     return;
   }
@@ -625,7 +624,7 @@ __global__ __launch_bounds__(256) void kvsplit_merge_kernel(const float* opart, 
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) sum += __shfl_xor(sum, off);
   wgt /= sum;
-  constexpr int CPL = D / 64;  // columns per lane
+  constexpr int CPL = (D + 63) / 64;  // columns per lane: l, l + 64, ... below D
   float acc[CPL];
 #pragma unroll
   for (int c = 0; c < CPL; ++c) acc[c] = 0.f;
@@ -633,10 +632,12 @@ __global__ __launch_bounds__(256) void kvsplit_merge_kernel(const float* opart, 
     const float ws = __shfl(wgt, sp);
     const float* src = opart + ((size_t)sp * rows + row) * D;
 #pragma unroll
-    for (int c = 0; c < CPL; ++c) acc[c] += ws * src[l + 64 * c];
+    for (int c = 0; c < CPL; ++c)
+      if (l + 64 * c < D) acc[c] += ws * src[l + 64 * c];
   }
 #pragma unroll
-  for (int c = 0; c < CPL; ++c) o[(size_t)row * D + l + 64 * c] = (E)acc[c];
+  for (int c = 0; c < CPL; ++c)
+    if (l + 64 * c < D) o[(size_t)row * D + l + 64 * c] = (E)acc[c];
   if (l == 0 && lse) lse[row] = mx + __logf(sum);
 }
 
@@ -650,13 +651,12 @@ static hipError_t launch_split_typed(const void* q, const void* k, const void* v
   float* lsepart = x.lsepart;
   const int rows = BH * N;
   const dim3 grid((rows + 3) / 4);
-  if (d == 64)
-    hipLaunchKernelGGL((kvsplit_merge_kernel<E, 64>), grid, dim3(256), 0, stream, opart, lsepart, static_cast<E*>(o),
+  return with_head_dim(d, [&](auto dd) {
+    constexpr int D = decltype(dd)::value;
+    hipLaunchKernelGGL((kvsplit_merge_kernel<E, D>), grid, dim3(256), 0, stream, opart, lsepart, static_cast<E*>(o),
                        lse, rows, n_splits);
-  else
-    hipLaunchKernelGGL((kvsplit_merge_kernel<E, 128>), grid, dim3(256), 0, stream, opart, lsepart, static_cast<E*>(o),
-                       lse, rows, n_splits);
-  return hipGetLastError();
+    return hipGetLastError();
+  });
 }
 
 hipError_t launch_fwd_16_kvsplit(bool fp16, const void* q, const void* k, const void* v, void* o, float* lse, int BH,

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace fa {
 
 // Block-sparse maps hold one byte per kMaskBlock x kMaskBlock block of scores; a workgroup keeps the
@@ -27,7 +29,8 @@ struct Dropout {
   bool active() const { return threshold < 256; }
 };
 
-// Forward, 16-bit storage: bf16 (fp16 = false) or IEEE fp16 (fp16 = true). BH = B*H. d in {64, 128}.
+// Forward, 16-bit storage: bf16 (fp16 = false) or IEEE fp16 (fp16 = true). BH = B*H.
+// d in {32, 64, 96, 128, 256} for every 16-bit launcher below.
 hipError_t launch_fwd_16(bool fp16, const void* q, const void* k, const void* v, void* o, float* lse,
                          int BH, int N, int d, float scale, bool causal, hipStream_t stream);
 
@@ -56,7 +59,7 @@ int device_cu_count();
 hipError_t launch_fwd_fp32(const void* q, const void* k, const void* v, void* o, float* lse,
                            int BH, int N, int d, float scale, bool causal, hipStream_t stream);
 
-// Backward stages, 16-bit storage (bf16 or fp16), d in {64, 128}. delta: float32 [BH, N].
+// Backward stages, 16-bit storage (bf16 or fp16). delta: float32 [BH, N].
 hipError_t launch_bwd_delta(bool fp16, const void* o, const void* dout, float* delta, int BH, int N, int d,
                             hipStream_t stream);
 hipError_t launch_bwd_dkdv(bool fp16, const void* q, const void* k, const void* v, const float* lse,
@@ -71,6 +74,20 @@ hipError_t launch_bwd_masked(bool fp16, const void* q, const void* k, const void
                              const float* lse, const void* dout, float* delta, void* dq, void* dk, void* dv,
                              int BH, int N, int d, float scale, bool causal, const Masks& masks,
                              const Dropout& drop, hipStream_t stream);
+
+// Head dims of the 16-bit kernels: calls f(std::integral_constant<int, D>) for d in
+// {32, 64, 96, 128, 256}; any other d is an invalid value.
+template <typename F>
+hipError_t with_head_dim(int d, F&& f) {
+  switch (d) {
+    case 32: return f(std::integral_constant<int, 32>{});
+    case 64: return f(std::integral_constant<int, 64>{});
+    case 96: return f(std::integral_constant<int, 96>{});
+    case 128: return f(std::integral_constant<int, 128>{});
+    case 256: return f(std::integral_constant<int, 256>{});
+    default: return hipErrorInvalidValue;
+  }
+}
 
 // Work decomposition shared by the kernels: workgroup id -> (head, tile).
 // The hardware hands consecutive workgroup ids to the 8 XCDs round-robin, each with its own L2.

@@ -21,7 +21,8 @@ fa_status_t check_shape(int B, int H, int N, int d) {
   return FA_OK;
 }
 
-bool supported_d(int d) { return d == 64 || d == 128; }
+bool supported_d(int d) { return d == 32 || d == 64 || d == 96 || d == 128 || d == 256; }  // 16-bit paths
+bool supported_d_fp32(int d) { return d == 64 || d == 128; }
 bool is_16bit(int dtype) { return dtype == FA_DTYPE_BF16 || dtype == FA_DTYPE_FP16; }
 
 }  // namespace
@@ -100,7 +101,7 @@ fa_status_t flash_attn_fwd(const void* q, const void* k, const void* v, void* o,
   if (!q || !k || !v || !o) return FA_ERR_NULL_POINTER;
   fa_status_t st = check_shape(B, H, N, d);
   if (st != FA_OK) return st;
-  if ((!is_16bit(dtype) && dtype != FA_DTYPE_FP32) || !supported_d(d)) return FA_ERR_UNSUPPORTED;
+  if (is_16bit(dtype) ? !supported_d(d) : (dtype != FA_DTYPE_FP32 || !supported_d_fp32(d))) return FA_ERR_UNSUPPORTED;
   if (!isfinite(scale)) return FA_ERR_BAD_SCALE;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || (lse && !aligned4(lse)))
     return FA_ERR_MISALIGNED;

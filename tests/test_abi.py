@@ -81,9 +81,25 @@ def test_fwd_bad_shape(lib, shape):
     assert _fwd(lib, B=B, H=H, N=N, d=d) == SHAPE
 
 
-@pytest.mark.parametrize("d,dtype", [(32, 1), (96, 1), (256, 1), (80, 0), (96, 2), (64, 3), (64, -1)])
+@pytest.mark.parametrize("d,dtype", [(48, 1), (80, 2), (160, 1), (512, 1), (32, 0), (96, 0), (256, 0), (80, 0),
+                                     (64, 3), (64, -1)])
 def test_fwd_unsupported(lib, d, dtype):
     assert _fwd(lib, d=d, dtype=dtype) == UNSUP
+
+
+@pytest.mark.parametrize("d", [32, 64, 96, 128, 256])
+@pytest.mark.parametrize("dtype", [1, 2])
+def test_16bit_head_dims_pass_the_support_check(lib, d, dtype):
+    """Every 16-bit entry point accepts d in {32, 64, 96, 128, 256}: these calls fail at the
+    alignment check that follows (the fake pointers never reach a launch)."""
+    assert _fwd(lib, d=d, dtype=dtype, q=A + 8) == ALIGN
+    assert _bwd(lib, ptrs={"q": A + 8}, d=d, dtype=dtype) == ALIGN
+    assert _kvs(lib, d=d, dtype=dtype, q=A + 8) == ALIGN
+    assert _fm(lib, d=d, dtype=dtype, q=A + 8) == ALIGN
+    assert _bm(lib, d=d, dtype=dtype, q=A + 8) == ALIGN
+    assert _dq(lib, d=d, dtype=dtype, q=A + 8) == ALIGN
+    assert _dkdv(lib, d=d, dtype=dtype, q=A + 8) == ALIGN
+    assert lib.flash_attn_bwd_delta(A, A, A + 2, 1, 1, 8, d, dtype, None) == ALIGN
 
 
 @pytest.mark.parametrize("scale", [math.nan, math.inf, -math.inf])
@@ -103,7 +119,7 @@ def test_bwd_null_pointer(lib, which):
 
 def test_bwd_unsupported_fp32_and_head_dim(lib):
     assert _bwd(lib, dtype=0) == UNSUP
-    assert _bwd(lib, d=96) == UNSUP
+    assert _bwd(lib, d=80) == UNSUP
 
 
 def test_bwd_bad_scale_and_shape(lib):
@@ -177,7 +193,7 @@ def test_kvsplit_validation(lib):
     assert _kvs(lib, splits=-1) == SHAPE
     assert _kvs(lib, Nq=0) == SHAPE
     assert _kvs(lib, dtype=0) == UNSUP              # 16-bit types only
-    assert _kvs(lib, d=96) == UNSUP
+    assert _kvs(lib, d=80) == UNSUP
     assert _kvs(lib, scale=math.inf) == SCALE
     assert _kvs(lib, k=A + 8) == ALIGN
     assert _kvs(lib, ws=None) == WS
@@ -203,7 +219,7 @@ def test_masked_validation(lib):
         assert call(lib, q=None) == NULLP
         assert call(lib, N=0) == SHAPE
         assert call(lib, dtype=0) == UNSUP            # 16-bit types only
-        assert call(lib, d=96) == UNSUP
+        assert call(lib, d=80) == UNSUP
         assert call(lib, scale=math.nan) == SCALE
         assert call(lib, k=A + 8) == ALIGN
         assert call(lib, seqlens=A + 2) == ALIGN
@@ -250,13 +266,13 @@ def test_fp16_passes_the_dtype_check(lib):
 def test_bwd_stage_validation(lib):
     assert lib.flash_attn_bwd_delta(None, A, A, 1, 1, 8, 64, 1, None) == NULLP
     assert lib.flash_attn_bwd_delta(A, A, A + 2, 1, 1, 8, 64, 1, None) == ALIGN
-    assert lib.flash_attn_bwd_delta(A, A, A, 1, 1, 8, 96, 1, None) == UNSUP
+    assert lib.flash_attn_bwd_delta(A, A, A, 1, 1, 8, 80, 1, None) == UNSUP
     assert lib.flash_attn_bwd_delta(A, A, A, 1, 1, 0, 64, 1, None) == SHAPE
     for fn in (_dkdv, _dq):
         assert fn(lib, q=None) == NULLP
         assert fn(lib, delta=None) == NULLP
         assert fn(lib, dtype=0) == UNSUP
-        assert fn(lib, d=32) == UNSUP
+        assert fn(lib, d=200) == UNSUP
         assert fn(lib, scale=math.inf) == SCALE
         assert fn(lib, N=0) == SHAPE
         assert fn(lib, k=A + 8) == ALIGN

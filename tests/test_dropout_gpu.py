@@ -3,16 +3,16 @@
 The keep mask is integer work and must match the oracle's Philox4x32-10 mask bit for bit. The
 forward and backward with dropout are then held to the dense gates (O <= 1e-2 and LSE <= 1e-3
 max-abs on rows that see a key, gradients <= 5e-2 relative to their norm), the oracle using its
-own mask. Kept weights grow by 256 / T, so O's gate is applied to O * T / 256 (the same error
-budget per unit of weight)."""
+own mask. Kept weights grow by 256 / T, so |O| can pass 4, where half a bf16 ulp alone is 0.0156:
+as for the other outputs that large, O's gate applies to the error beyond O's own rounding."""
 import numpy as np
 import pytest
 import torch
 
 from io_aware_flashattention_flash_amd import (flash_attn_bwd_masked, flash_attn_dropout_mask, flash_attn_fwd_masked,
                                                inputs)
-from oracle import attn_bwd_dropout, attn_fwd_dropout, keep_mask, keep_threshold, padded_batch_visible
-from tests.test_parity_gpu import BF16_LSE, BF16_O, DEV, GRAD, dev, grad_errors, host
+from oracle import attn_bwd_dropout, attn_fwd_dropout, keep_mask, padded_batch_visible
+from tests.test_parity_gpu import BF16_LSE, BF16_O, DEV, GRAD, beyond_rounding, dev, grad_errors, host
 
 pytestmark = pytest.mark.gpu
 
@@ -40,9 +40,8 @@ def _case(B, H, N, d, causal, p, seed, seqlens=None, bmap=None, dtype="bf16", ba
     O, L = attn_fwd_dropout(x["q"], x["k"], x["v"], scale, vis, keep, p)
     full = np.isfinite(L)
     ho, hl = host(o), host(lse)
-    shrink = keep_threshold(p) / 256.0
     assert np.isfinite(ho).all() and (ho[~full] == 0).all() and np.isneginf(hl[~full]).all()
-    assert np.abs(ho[full] - O[full]).max(initial=0) * shrink <= BF16_O
+    assert beyond_rounding(ho[full], O[full]) <= BF16_O
     assert np.abs(hl[full] - L[full]).max(initial=0) <= BF16_LSE
     if not backward:
         return o, lse

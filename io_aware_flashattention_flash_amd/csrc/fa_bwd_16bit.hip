@@ -133,8 +133,14 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdParams<E> p) {
 // probabilities scaled by 256 / T, and the gradient reaching P is dP scaled by the same kept factor.
 // This kernel's lanes hold keys, not queries, so each wave draws the Philox words of its 32 x 32
 // block in the forward's layout (one call per lane) and transposes the bytes through LDS.
-template <typename E, int D, int NW, int BQ, bool CAUSAL, bool MASKED, bool DROPOUT>
+//
+// PART: 0 computes dK and dV; 1 only dV (needs K, not V); 2 only dK. d = 256 runs parts 1 and 2 as
+// two launches: K and V operands (128 registers per lane) plus both accumulators (256) do not fit
+// one wave's 512 registers beside the temporaries, and recomputing S once more is cheaper than
+// spilling.
+template <typename E, int D, int NW, int BQ, bool CAUSAL, bool MASKED, bool DROPOUT, int PART>
 __global__ __launch_bounds__(NW * 64, (D > 64 ? 1 : 2)) void bwd_dkdv_kernel(BwdParams<E> p) {
+  constexpr bool WANT_DV = PART != 2, WANT_DK = PART != 1;
   using H = Half16<E>;
   using e16x8 = typename H::x8;
   constexpr int BKV = 32 * NW;
@@ -179,7 +185,7 @@ __global__ __launch_bounds__(NW * 64, (D > 64 ? 1 : 2)) void bwd_dkdv_kernel(Bwd
     for (int kk = 0; kk < NKK; ++kk) {
       const int off = key * (D * 2) + (16 * kk + 8 * hf) * 2;
       kreg[kk] = __builtin_bit_cast(e16x8, buf_load16(rk, off));
-      vreg[kk] = __builtin_bit_cast(e16x8, buf_load16(rv, off));
+      if (WANT_DK) vreg[kk] = __builtin_bit_cast(e16x8, buf_load16(rv, off));
     }
   }
 
@@ -265,7 +271,7 @@ __global__ __launch_bounds__(NW * 64, (D > 64 ? 1 : 2)) void bwd_dkdv_kernel(Bwd
       for (int kk = 0; kk < NKK; ++kk) {
         const int off = T::chunk_off(32 * qb + lq, 2 * kk + hf);
         s = H::mfma(lds_read16<E>(qbuf, off), kreg[kk], s);
-        dp = H::mfma(lds_read16<E>(obuf, off), vreg[kk], dp);
+        if (WANT_DK) dp = H::mfma(lds_read16<E>(obuf, off), vreg[kk], dp);
       }
       // Register r holds query q0 + 8*(r/4) + 4*hf + r%4 against this lane's key.
       const int kmin = key - q0 - 4 * hf;  // (DIAG) query offsets below this are masked
@@ -317,8 +323,10 @@ __global__ __launch_bounds__(NW * 64, (D > 64 ? 1 : 2)) void bwd_dkdv_kernel(Bwd
         for (int ks = 0; ks < 2; ++ks) {
           const int r0 = 32 * qb + 16 * ks + tr_row_lane;
           const int o0 = T::elem_off(r0, col), o1 = T::elem_off(r0 + 8, col);
-          dv[db] = H::mfma(cat4<E>(lds_read_tr16<E>(obuf, o0), lds_read_tr16<E>(obuf, o1)), pb[ks], dv[db]);
-          dk[db] = H::mfma(cat4<E>(lds_read_tr16<E>(qbuf, o0), lds_read_tr16<E>(qbuf, o1)), dsb[ks], dk[db]);
+          if (WANT_DV)
+            dv[db] = H::mfma(cat4<E>(lds_read_tr16<E>(obuf, o0), lds_read_tr16<E>(obuf, o1)), pb[ks], dv[db]);
+          if (WANT_DK)
+            dk[db] = H::mfma(cat4<E>(lds_read_tr16<E>(qbuf, o0), lds_read_tr16<E>(qbuf, o1)), dsb[ks], dk[db]);
         }
       }
     }
@@ -363,8 +371,8 @@ __global__ __launch_bounds__(NW * 64, (D > 64 ? 1 : 2)) void bwd_dkdv_kernel(Bwd
   // dK = scale * dK^T^T and dV, written as whole rows through this wave's idle tile buffer.
   __syncthreads();  // every wave is done reading the last Q / dO tile
   char* stage = w == 0 ? sq0 : (w == 1 ? so0 : (w == 2 ? sq1 : so1));
-  store_rows_via_lds<E, D, TILE_BYTES>(stage, dk, p.scale, make_rsrc(p.dk + base, head_bytes), key_w0, l);
-  store_rows_via_lds<E, D, TILE_BYTES>(stage, dv, 1.0f, make_rsrc(p.dv + base, head_bytes), key_w0, l);
+  if (WANT_DK) store_rows_via_lds<E, D, TILE_BYTES>(stage, dk, p.scale, make_rsrc(p.dk + base, head_bytes), key_w0, l);
+  if (WANT_DV) store_rows_via_lds<E, D, TILE_BYTES>(stage, dv, 1.0f, make_rsrc(p.dv + base, head_bytes), key_w0, l);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -631,8 +639,15 @@ hipError_t delta_d(BwdParams<E> prm, hipStream_t stream) {
 template <typename E, int D, bool CAUSAL, bool MASKED = false, bool DROPOUT = false>
 hipError_t dkdv_d(BwdParams<E> prm, hipStream_t stream) {
   prm.n_tiles = (prm.N + 32 * kKvNW - 1) / (32 * kKvNW);
-  hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, kKvNW, kKvBQ, CAUSAL, MASKED, DROPOUT>), dim3(prm.n_tiles * prm.nh),
-                     dim3(kKvNW * 64), 0, stream, prm);
+  const dim3 grid(prm.n_tiles * prm.nh), block(kKvNW * 64);
+  if constexpr (D > 128) {  // dV, then dK (see bwd_dkdv_kernel)
+    hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, kKvNW, kKvBQ, CAUSAL, MASKED, DROPOUT, 1>), grid, block, 0, stream, prm);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, kKvNW, kKvBQ, CAUSAL, MASKED, DROPOUT, 2>), grid, block, 0, stream, prm);
+  } else {
+    hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, kKvNW, kKvBQ, CAUSAL, MASKED, DROPOUT, 0>), grid, block, 0, stream, prm);
+  }
   return hipGetLastError();
 }
 

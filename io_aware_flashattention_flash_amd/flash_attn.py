@@ -359,22 +359,40 @@ def flash_attn_bwd_dq(q, k, v, o, lse, dout, scale=None, causal=False, dq=None, 
 
 
 class FlashAttnFunction(torch.autograd.Function):
-    """autograd wrapper: forward saves (q, k, v, o, lse); backward calls flash_attn_bwd."""
+    """autograd wrapper: forward saves (q, k, v, o, lse); backward recomputes through the library.
+    With lengths, a block map or dropout it uses the masked entry points, and the dropout seed is
+    kept so the backward regenerates the same keep mask."""
 
     @staticmethod
-    def forward(ctx, q, k, v, scale=None, causal=False):
-        o, lse = flash_attn_fwd(q, k, v, scale, causal)
+    def forward(ctx, q, k, v, scale=None, causal=False, seqlens=None, block_mask=None, dropout_p=0.0, seed=0):
+        ctx.masked = seqlens is not None or block_mask is not None or dropout_p > 0.0
+        if ctx.masked:
+            o, lse = flash_attn_fwd_masked(q, k, v, scale, causal, seqlens=seqlens, block_mask=block_mask,
+                                           dropout_p=dropout_p, seed=seed)
+        else:
+            o, lse = flash_attn_fwd(q, k, v, scale, causal)
         ctx.save_for_backward(q, k, v, o, lse)
-        ctx.scale = scale
-        ctx.causal = causal
+        ctx.scale, ctx.causal = scale, causal
+        ctx.seqlens, ctx.block_mask, ctx.dropout_p, ctx.seed = seqlens, block_mask, dropout_p, seed
         return o
 
     @staticmethod
     def backward(ctx, do):
         q, k, v, o, lse = ctx.saved_tensors
-        dq, dk, dv = flash_attn_bwd(do.contiguous(), q, k, v, o, lse, ctx.scale, ctx.causal)
-        return dq, dk, dv, None, None
+        if ctx.masked:
+            dq, dk, dv = flash_attn_bwd_masked(do.contiguous(), q, k, v, o, lse, ctx.scale, ctx.causal,
+                                               seqlens=ctx.seqlens, block_mask=ctx.block_mask,
+                                               dropout_p=ctx.dropout_p, seed=ctx.seed)
+        else:
+            dq, dk, dv = flash_attn_bwd(do.contiguous(), q, k, v, o, lse, ctx.scale, ctx.causal)
+        return dq, dk, dv, None, None, None, None, None, None
 
 
-def flash_attention(q, k, v, scale=None, causal=False):
-    return FlashAttnFunction.apply(q, k, v, scale, causal)
+def flash_attention(q, k, v, scale=None, causal=False, seqlens=None, block_mask=None, dropout_p=0.0, seed=None):
+    """Differentiable exact attention on [B, H, N, d] tensors. seqlens (int32 [B]) and block_mask
+    (uint8 [B, H, ceil(N/128), ceil(N/128)]) mask as in flash_attn_fwd_masked; dropout_p > 0 drops
+    attention probabilities with a Philox seed (drawn from torch's CPU generator when None)."""
+    if dropout_p > 0.0 and seed is None:
+        seed = int(torch.randint(0, 2 ** 62, (1,)).item())
+    return FlashAttnFunction.apply(q, k, v, scale, causal, seqlens, block_mask, float(dropout_p),
+                                   0 if seed is None else int(seed))

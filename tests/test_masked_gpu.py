@@ -195,3 +195,24 @@ def test_kvsplit_cache_lengths(Nq, Nk, lens, splits, causal, d):
     torch.cuda.synchronize()
     O, L = attn_fwd_masked(x["q"], x["k"], x["v"], d ** -0.5, kv_cache_visible(B, H, Nq, Nk, causal, lens))
     _check_fwd(o, lse, O, L)
+
+
+def test_autograd_wrapper_routes_masks_and_dropout():
+    """flash_attention(...) with lengths, a map and dropout: its gradients are the masked backward's
+    with the same seed, and its output the masked forward's."""
+    from io_aware_flashattention_flash_amd import flash_attention
+
+    B, H, N, d = 2, 2, 500, 64
+    x = _inputs(B, H, N, d, seed=21, with_do=True)
+    q, k, v, do = (dev(x[n], torch.bfloat16) for n in ("q", "k", "v", "do"))
+    sl = torch.tensor([500, 260], dtype=torch.int32, device=DEV)
+    bm = torch.from_numpy(_random_map(B, H, N, seed=8, density=0.7)).to(DEV)
+    qa, ka, va = (t.clone().requires_grad_(True) for t in (q, k, v))
+    out = flash_attention(qa, ka, va, 0.125, True, seqlens=sl, block_mask=bm, dropout_p=0.2, seed=99)
+    out.backward(do)
+    o, lse = flash_attn_fwd_masked(q, k, v, 0.125, True, seqlens=sl, block_mask=bm, dropout_p=0.2, seed=99)
+    ref = flash_attn_bwd_masked(do, q, k, v, o, lse, 0.125, True, seqlens=sl, block_mask=bm, dropout_p=0.2, seed=99)
+    torch.cuda.synchronize()
+    assert torch.equal(out.detach(), o)
+    for g, r in zip((qa.grad, ka.grad, va.grad), ref):
+        assert torch.equal(g, r)

@@ -60,11 +60,13 @@ def keep_threshold(p: float) -> int:
     return int(np.floor(256.0 * (1.0 - p) + 0.5))
 
 
-def random_bytes(B, H, Nq, Nk, seed: int):
-    """uint8 [B, H, Nq, Nk]: the random byte of every score element under the contract above."""
+def random_bytes(B, H, Nq, Nk, seed: int, heads=None):
+    """uint8 [B, H, Nq, Nk]: the random byte of every score element under the contract above.
+    With `heads` (flattened indices b * H + h), only those heads: uint8 [len(heads), Nq, Nk]."""
     key = (seed & MASK32, (seed >> 32) & MASK32)
     nJ = -(-Nk // 32)
-    bh = np.arange(B * H, dtype=np.uint64).reshape(B * H, 1, 1, 1)
+    hs = np.arange(B * H) if heads is None else np.asarray(heads)
+    bh = hs.astype(np.uint64).reshape(-1, 1, 1, 1)
     i = np.arange(Nq, dtype=np.uint64).reshape(1, Nq, 1, 1)
     J = np.arange(nJ, dtype=np.uint64).reshape(1, 1, nJ, 1)
     t = np.arange(2, dtype=np.uint64).reshape(1, 1, 1, 2)
@@ -74,6 +76,8 @@ def random_bytes(B, H, Nq, Nk, seed: int):
     jj = j % 32
     w = words[:, :, j // 32, (j // 4) % 2, jj // 8]            # [BH, Nq, Nk]
     byte = (w >> (8 * (jj % 4)).astype(np.uint64)) & np.uint64(0xFF)
+    if heads is not None:
+        return byte.astype(np.uint8)
     return byte.astype(np.uint8).reshape(B, H, Nq, Nk)
 
 

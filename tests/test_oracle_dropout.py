@@ -165,3 +165,9 @@ def test_planted_generator_mistakes_are_caught():
     for kind in ("nine_rounds", "swapped", "fixed_key"):
         f = variant(kind)
         assert any(f(c, k) != list(o) for c, k, o in KAT), kind
+
+
+def test_head_subset_equals_slice_of_full():
+    full = od.random_bytes(2, 3, 9, 70, seed=5)
+    sub = od.random_bytes(2, 3, 9, 70, seed=5, heads=[0, 4, 5])
+    np.testing.assert_array_equal(sub, full.reshape(6, 9, 70)[[0, 4, 5]])

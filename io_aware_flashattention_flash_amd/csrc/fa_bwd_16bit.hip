@@ -139,7 +139,7 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdParams<E> p) {
 // one wave's 512 registers beside the temporaries, and recomputing S once more is cheaper than
 // spilling.
 template <typename E, int D, int NW, int BQ, bool CAUSAL, bool MASKED, bool DROPOUT, int PART>
-__global__ __launch_bounds__(NW * 64, (D > 64 ? 1 : 2)) void bwd_dkdv_kernel(BwdParams<E> p) {
+__global__ __launch_bounds__(NW * 64, (D > 64 && D != 96 ? 1 : 2)) void bwd_dkdv_kernel(BwdParams<E> p) {
   constexpr bool WANT_DV = PART != 2, WANT_DK = PART != 1;
   using H = Half16<E>;
   using e16x8 = typename H::x8;

@@ -137,9 +137,15 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdParams<E> p) {
 // PART: 0 computes dK and dV; 1 only dV (needs K, not V); 2 only dK. d = 256 runs parts 1 and 2 as
 // two launches: K and V operands (128 registers per lane) plus both accumulators (256) do not fit
 // one wave's 512 registers beside the temporaries, and recomputing S once more is cheaper than
-// spilling.
+// spilling. Non-causal d = 128 also runs the two parts, each at two waves per SIMD (measured
+// faster than one wave per SIMD for the whole; causal d = 128 is faster whole).
+// Waves per SIMD: 2 where the registers fit 256 per lane (d <= 64, d = 96, the parts at d = 128),
+// else 1.
+template <int D, int PART>
+constexpr int dkdv_waves_per_simd() { return (D > 128 || (D == 128 && PART == 0)) ? 1 : 2; }
+
 template <typename E, int D, int NW, int BQ, bool CAUSAL, bool MASKED, bool DROPOUT, int PART>
-__global__ __launch_bounds__(NW * 64, (D > 64 && D != 96 ? 1 : 2)) void bwd_dkdv_kernel(BwdParams<E> p) {
+__global__ __launch_bounds__(NW * 64, (dkdv_waves_per_simd<D, PART>())) void bwd_dkdv_kernel(BwdParams<E> p) {
   constexpr bool WANT_DV = PART != 2, WANT_DK = PART != 1;
   using H = Half16<E>;
   using e16x8 = typename H::x8;
@@ -640,7 +646,7 @@ template <typename E, int D, bool CAUSAL, bool MASKED = false, bool DROPOUT = fa
 hipError_t dkdv_d(BwdParams<E> prm, hipStream_t stream) {
   prm.n_tiles = (prm.N + 32 * kKvNW - 1) / (32 * kKvNW);
   const dim3 grid(prm.n_tiles * prm.nh), block(kKvNW * 64);
-  if constexpr (D > 128) {  // dV, then dK (see bwd_dkdv_kernel)
+  if constexpr (D > 128 || (D == 128 && !CAUSAL)) {  // dV, then dK (see bwd_dkdv_kernel)
     hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, kKvNW, kKvBQ, CAUSAL, MASKED, DROPOUT, 1>), grid, block, 0, stream, prm);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;

@@ -75,7 +75,7 @@ def extra_workload(name):
     return inputs.Workload(name, "fp16", base.B, base.H, base.N, base.d, base.causal, base.backward, base.q_mult)
 
 
-def time_forward(name, reps, warmup, dev, to_dev, wl=None):
+def time_forward(name, reps, warmup, dev, to_dev, wl=None, cold=False):
     """Forward-only timing of one workload (HIP events around `reps` back-to-back launches)."""
     import torch
 
@@ -107,8 +107,44 @@ def time_forward(name, reps, warmup, dev, to_dev, wl=None):
     tf = wl.fwd_flops() / (us * 1e-6) / 1e12
     peak = PEAK_FP32_TFLOPS if wl.dtype == "fp32" else PEAK_BF16_TFLOPS  # fp16 dense MFMA peak = bf16's
     nbytes = wl.B * wl.H * (4 * wl.N * wl.d * (4 if wl.dtype == "fp32" else 2) + 4 * wl.N)
-    return {"workload": name, "pass": "fwd", "reps": reps, "us": round(us, 2), "tflops": round(tf, 1),
-            "pct_of_peak": round(100 * tf / peak, 2), "gbps_algorithmic": round(nbytes / (us * 1e-6) / 1e9, 1)}
+    out = {"workload": name, "pass": "fwd", "reps": reps, "us": round(us, 2), "tflops": round(tf, 1),
+           "pct_of_peak": round(100 * tf / peak, 2), "gbps_algorithmic": round(nbytes / (us * 1e-6) / 1e9, 1)}
+
+    def call():
+        flash_attn_fwd(qi, ki, vi, wl.scale, wl.causal, out=oi, lse=li)
+
+    # per-call distribution: each of 50 calls bracketed by its own events (warm caches)
+    p10, p50, p90 = percentiles_us(call, 50)
+    out.update({"p10_us": p10, "p50_us": p50, "p90_us": p90})
+    if cold:
+        # cold caches: before each timed call, a fill kernel writes 1 GiB (more than the 256 MB
+        # MALL plus the L2s), evicting Q, K, V; only the attention call is inside the events
+        flush = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        c10, c50, c90 = percentiles_us(call, 20, before=flush.zero_)
+        out.update({"cold_p50_us": c50, "cold_p10_us": c10, "cold_p90_us": c90,
+                    "cold_tflops": round(wl.fwd_flops() / (c50 * 1e-6) / 1e12, 2)})
+        del flush
+    return out
+
+
+def percentiles_us(call, n, before=None):
+    """(p10, p50, p90) in microseconds of `call`, each run bracketed by its own HIP events on the
+    current stream; `before` (untimed) runs ahead of each call."""
+    import torch
+
+    evs = []
+    for _ in range(n):
+        if before is not None:
+            before()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        call()
+        b.record()
+        evs.append((a, b))
+    torch.cuda.synchronize()
+    t = sorted(a.elapsed_time(b) * 1e3 for a, b in evs)
+    pick = lambda q: round(t[min(len(t) - 1, int(q * len(t)))], 2)
+    return pick(0.1), pick(0.5), pick(0.9)
 
 
 def time_decode(B, H, Nk, d, reps, dev):
@@ -332,7 +368,8 @@ def main():
     if not args.no_workloads:
         for name, wl in inputs.WORKLOADS.items():
             if not wl.backward:
-                workloads[name] = time_forward(name, None, 10, dev, to_dev)
+                # the short workloads (N <= 1024) also get cold-cache timings
+                workloads[name] = time_forward(name, None, 10, dev, to_dev, cold=wl.N <= 1024)
         torch.cuda.empty_cache()
 
     # ------------------------------------------------------------------ extra lines: fp16 storage
@@ -414,7 +451,8 @@ def main():
         "kernels": kernels,
         "workloads": workloads,
         "extras": extras,
-        "device": {"name": props.name, "arch": getattr(props, "gcnArchName", ""), "cus": props.multi_processor_count},
+        "device": {"name": props.name, "arch": getattr(props, "gcnArchName", ""), "cus": props.multi_processor_count,
+                   "torch": torch.__version__, "hip": getattr(torch.version, "hip", None)},
     }
     print(json.dumps(out))
 

@@ -139,6 +139,72 @@ def traffic(a) -> dict:
     return out
 
 
+# One counter pass per workload (at most 8 SQ and 2 GRBM counters, so they fit a single pass).
+COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS "
+            "SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_WAVE_CYCLES GRBM_GUI_ACTIVE")
+N_XCD, N_SIMD = 8, 1024  # MI355X: GRBM_GUI_ACTIVE is summed over the 8 XCDs; 256 CUs x 4 SIMDs
+
+
+def counter_summary(directory: str, formula_flops: dict) -> list:
+    """Per attention kernel in one counter pass: averages per dispatch and the derived figures.
+
+    formula_flops: kernel key -> algorithmic MFMA flops per launch (the workload's counting
+    convention). SQ_INSTS_VALU_MFMA_MOPS_BF16 counts matrix work in units of 512 flops, so
+    512 x MOPS / formula is the executed-to-counted ratio: about 1 + tile / N for a causal forward
+    whose above-diagonal tiles are skipped (2 if they were not), about 3 for dQ (it recomputes S
+    and dP beside its one counted product), about 1 for dK/dV."""
+    path = glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True)
+    if not path:
+        raise FileNotFoundError(f"no counter_collection.csv under {directory}")
+    total, dispatches = defaultdict(lambda: defaultdict(float)), defaultdict(set)
+    for row in csv.DictReader(open(path[0])):
+        key = kernel_key(row["Kernel_Name"])
+        if key is None:
+            continue
+        total[key][row["Counter_Name"]] += float(row["Counter_Value"])
+        dispatches[key].add(row["Dispatch_Id"])
+    out = []
+    for key in sorted(total):
+        c = {n: v / len(dispatches[key]) for n, v in total[key].items()}
+        cycles = c["GRBM_GUI_ACTIVE"] / N_XCD
+        mfma_flops = 512.0 * c["SQ_INSTS_VALU_MFMA_MOPS_BF16"]
+        out.append({
+            "kernel": key,
+            "dispatches": len(dispatches[key]),
+            "gpu_cycles": cycles,
+            "mfma_busy_frac": c["SQ_VALU_MFMA_BUSY_CYCLES"] / N_SIMD / cycles,
+            "mfma_flops": mfma_flops,
+            "executed_over_formula": mfma_flops / formula_flops[key] if key in formula_flops else None,
+            "valu_per_mfma": (c["SQ_INSTS_VALU"] - c["SQ_INSTS_MFMA"]) / c["SQ_INSTS_MFMA"],
+            "lds_instr_per_mfma": c["SQ_INSTS_LDS"] / c["SQ_INSTS_MFMA"],
+            "lds_bank_conflict_frac": c["SQ_LDS_BANK_CONFLICT"] / max(1.0, c["SQ_LDS_IDX_ACTIVE"]),
+        })
+    return out
+
+
+def counters_md(runs: list, out_md: str, commands: str) -> str:
+    """runs: [(workload label, counter directory, {kernel: formula flops})]."""
+    lines = ["# MFMA, VALU and LDS counters per attention kernel (rocprofv3 --pmc, one pass per workload)", "",
+             "Commands (run from the repository root on one MI355X):", "", "```", commands, "```", "",
+             "Derived figures: MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / 1024 SIMDs / (GRBM_GUI_ACTIVE / 8 XCDs); "
+             "executed / counted = 512 x SQ_INSTS_VALU_MFMA_MOPS_BF16 / the workload's flop formula (causal "
+             "forward: about 1 + 128/N when tiles above the diagonal are skipped, 2 if they were not; dQ: "
+             "about 3, it recomputes S and dP beside its one counted product); LDS bank conflicts = "
+             "SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE. Counts are averages per dispatch.", "",
+             "| workload | kernel | dispatches | MFMA busy | executed / counted flops | VALU instr per MFMA | "
+             "LDS instr per MFMA | LDS bank-conflict cycles |", "|---|---|---|---|---|---|---|---|"]
+    for label, directory, formula in runs:
+        for r in counter_summary(directory, formula):
+            ratio = "–" if r["executed_over_formula"] is None else f"{r['executed_over_formula']:.3f}"
+            lines.append(f"| {label} | {r['kernel']} | {r['dispatches']} | {r['mfma_busy_frac']:.1%} | {ratio} | "
+                         f"{r['valu_per_mfma']:.2f} | {r['lds_instr_per_mfma']:.2f} | "
+                         f"{r['lds_bank_conflict_frac']:.2%} |")
+    text = "\n".join(lines) + "\n"
+    with open(out_md, "w") as f:
+        f.write(text)
+    return text
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -151,9 +217,21 @@ def main():
     for name in ("--fetch", "--write", "--copy-fetch", "--copy-write", "--out-json", "--out-md", "--commands"):
         r.add_argument(name, required=True)
     r.add_argument("--copy-bytes", type=int, required=True)
+    c = sub.add_parser("counters", help="MFMA / VALU / LDS counter summary; --run LABEL DIR WORKLOAD per workload")
+    c.add_argument("--run", nargs=3, action="append", required=True, metavar=("LABEL", "DIR", "WORKLOAD"))
+    c.add_argument("--out-md", required=True)
+    c.add_argument("--commands", required=True)
     a = ap.parse_args()
     if a.cmd == "trace":
         print(trace(a.stats_csv, a.out_md, a.command, a.title))
+    elif a.cmd == "counters":
+        from . import inputs
+        runs = []
+        for label, directory, wname in a.run:
+            w = inputs.WORKLOADS[wname]
+            f = w.fwd_flops()
+            runs.append((label, directory, {"fwd": f, "bwd_dq": 0.5 * f, "bwd_dkdv": 2.0 * f}))
+        print(counters_md(runs, a.out_md, a.commands))
     else:
         print(json.dumps(traffic(a), indent=1))
 

@@ -57,7 +57,23 @@ def build(verbose: bool = False, extra_flags=()) -> str:
     tmp = LIB_PATH + ".tmp"
     _run([hipcc, "--offload-arch=" + ARCH, "-shared", "-fPIC", *objs, "-o", tmp])
     os.replace(tmp, LIB_PATH)
+    build_abi_roundtrip(hipcc)
     return LIB_PATH
+
+
+ROUNDTRIP_SRC = os.path.join(os.path.dirname(PKG), "tests", "c_abi", "abi_roundtrip.cpp")
+ROUNDTRIP_BIN = os.path.join(os.path.dirname(PKG), "tests", "c_abi", "abi_roundtrip")
+
+
+def build_abi_roundtrip(hipcc: str) -> None:
+    """The host program that exercises the C ABI without Python (tests/c_abi), linked against the
+    in-tree library with a relative run path."""
+    if not os.path.exists(ROUNDTRIP_SRC):
+        return
+    rpath = "-Wl,-rpath,$ORIGIN/" + os.path.relpath(PKG, os.path.dirname(ROUNDTRIP_BIN))
+    _run([hipcc, "-O2", "-std=c++17", ROUNDTRIP_SRC, "-o", ROUNDTRIP_BIN + ".tmp", "-L" + PKG, "-lflashattn",
+          rpath])
+    os.replace(ROUNDTRIP_BIN + ".tmp", ROUNDTRIP_BIN)
 
 
 if __name__ == "__main__":

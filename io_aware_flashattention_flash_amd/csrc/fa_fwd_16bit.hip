@@ -37,7 +37,9 @@
 //    scores, each stage a step after the previous one, and LDS fragments are
 //    fetched four instructions ahead; scheduling barriers keep this order.
 //    One barrier per tile: K(j+2) and V(j+1) are issued right after the barrier
-//    that follows A(j), the last reader of the buffers they overwrite.
+//    that follows A(j), the last reader of the buffers they overwrite. The last two
+//    tiles run without the look-ahead: no scores of a tile past the end, and a final
+//    O += P V for the last half on its own.
 //  * softmax in the log2 domain: p = exp2(s*c - m) with c = |scale| * log2(e)
 //    (a negative scale is applied by negating Q, which is exact in 16 bits). There
 //    is no per-tile row maximum: any reference m gives the same O = sum p V /
@@ -302,16 +304,16 @@ __global__ __launch_bounds__(NW * 64, D > 128 ? 1 : 2) void fwd16_kernel(Fwd16Pa
   f32x16 s0, s1;
   e16x8 p0[2], p1[2];
   float rs, rr;
-  // One pipeline phase: NS = NKK MFMAs of S^T for K half `hs` (into s_out), NPV = 2 * NDB MFMAs of
-  // O^T += V^T P^T for V half `hv` (from p_in), and the probabilities of s_in (into p_out), with
-  // their fp32 sum in rs and the sum of their 16-bit roundings in rr. The work is issued in a fixed
-  // interleave, fenced by scheduling barriers.
+  // One pipeline phase: NS = NKK MFMAs of S^T for K half `hs` (into s_out; none without with_s),
+  // NPV = 2 * NDB MFMAs of O^T += V^T P^T for V half `hv` (from p_in), and the probabilities of s_in
+  // (into p_out), with their fp32 sum in rs and the sum of their 16-bit roundings in rr. The work is
+  // issued in a fixed interleave, fenced by scheduling barriers.
   uint32_t kw[4];  // dropout: the Philox words of the half whose probabilities are being formed
-  auto phase = [&](auto with_pv, f32x16& s_out, const char* kbuf, int hs, const e16x8 (&p_in)[2],
+  auto phase = [&](auto with_pv, auto with_s, f32x16& s_out, const char* kbuf, int hs, const e16x8 (&p_in)[2],
                    const char* vbuf, int hv, const f32x16& s_in, e16x8 (&p_out)[2], int jh) __attribute__((always_inline)) {
     constexpr bool PV = decltype(with_pv)::value;
     if constexpr (DROPOUT) dropout_words(q, jh, head, hf, p.seed_lo, p.seed_hi, kw);
-    constexpr int NS = NKK, NPV = PV ? 2 * NDB : 0, NM = NS + NPV;
+    constexpr int NS = decltype(with_s)::value ? NKK : 0, NPV = PV ? 2 * NDB : 0, NM = NS + NPV;
     auto frag = [&](int i) __attribute__((always_inline)) -> e16x8 {
       if (i < NS) return lds_read16<E>(kbuf, T::chunk_off(32 * hs + lq, 2 * i + hf));
       const int t = (i - NS) / NDB, db = (i - NS) % NDB, ks = 2 * hv + t;
@@ -431,13 +433,25 @@ __global__ __launch_bounds__(NW * 64, D > 128 ? 1 : 2) void fwd16_kernel(Fwd16Pa
   using no = std::integral_constant<bool, false>;
   auto phase_a = [&](int j, const char* kbuf, const char* vprev, auto with_pv) __attribute__((always_inline)) {
     mask_half(s0, j, 0);
-    phase(with_pv, s1, kbuf, 1, p1, vprev, 1, s0, p0, 2 * j);
+    phase(with_pv, yes{}, s1, kbuf, 1, p1, vprev, 1, s0, p0, 2 * j);
     settle(s0, p0);
   };
-  auto phase_b = [&](int j, const char* knext, const char* vcur) __attribute__((always_inline)) {
+  // with_s = no: the last tile's B phase, with no scores of a following tile to start.
+  auto phase_b = [&](int j, const char* knext, const char* vcur, auto with_s) __attribute__((always_inline)) {
     mask_half(s1, j, 1);
-    phase(yes{}, s0, knext, 0, p0, vcur, 0, s1, p1, 2 * j + 1);
+    phase(yes{}, with_s, s0, knext, 0, p0, vcur, 0, s1, p1, 2 * j + 1);
     settle(s1, p1);
+  };
+  // O^T += V^T P^T for V half `hv` alone (the pipeline's drain after the last tile).
+  auto pv_only = [&](const char* vbuf, int hv, const e16x8 (&p_in)[2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 2 * NDB; ++i) {
+      const int t = i / NDB, db = i % NDB, ks = 2 * hv + t;
+      const int col = 32 * db + v_col_lane;
+      const e16x4 a0 = lds_read_tr16<E>(vbuf, T::elem_off(16 * ks + v_row_lane, col));
+      const e16x4 a1 = lds_read_tr16<E>(vbuf, T::elem_off(16 * ks + 8 + v_row_lane, col));
+      acc_o[db] = H::mfma(cat4<E>(a0, a1), p_in[t], acc_o[db]);
+    }
   };
   // K(j) and V(j) live in buffer j % 2. K(j+2) / V(j+1) are issued right after the barrier that
   // follows phase A(j), the last reader of K(j) and V(j-1), and are awaited one tile later. The
@@ -453,20 +467,33 @@ __global__ __launch_bounds__(NW * 64, D > 128 ? 1 : 2) void fwd16_kernel(Fwd16Pa
   s_half(s0, sk0, 0);
   phase_a(j_first, sk0, sv1, no{});
 #pragma unroll 1
-  for (int t = 0; t < n_eff; t += 2) {
+  for (int t = 0; t < n_eff - 2; t += 2) {
     const int j0 = tile(t), j1 = tile(t + 1), j2 = tile(t + 2);
     wait_vmem();
     __syncthreads();
     if (t + 2 < n_t) dma(Kh, j2, sk0);
     dma(Vh, j1, sv1);
-    phase_b(j0, sk1, sv0);
+    phase_b(j0, sk1, sv0, yes{});
     phase_a(j1, sk1, sv0, yes{});
     wait_vmem();
     __syncthreads();
     if (t + 3 < n_t) dma(Kh, tile(t + 3), sk1);
-    if (t + 2 < n_eff) dma(Vh, j2, sv0);
-    phase_b(j1, sk0, sv1);
+    dma(Vh, j2, sv0);
+    phase_b(j1, sk0, sv1, yes{});
     phase_a(j2, sk0, sv1, yes{});
+  }
+  {  // the last two tiles: the same steps without scoring a tile past the end
+    const int t = n_eff - 2;
+    const int j0 = tile(t), j1 = tile(t + 1);
+    wait_vmem();
+    __syncthreads();
+    dma(Vh, j1, sv1);
+    phase_b(j0, sk1, sv0, yes{});
+    phase_a(j1, sk1, sv0, yes{});
+    wait_vmem();
+    __syncthreads();
+    phase_b(j1, sk0, sv1, no{});
+    pv_only(sv1, 1, p1);
   }
 
   // Epilogue: O = O_acc / l~, LSE = ln2 * (m + log2 l). The accumulator holds one query row per

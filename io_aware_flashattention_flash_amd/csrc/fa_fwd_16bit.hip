@@ -354,17 +354,28 @@ __global__ __launch_bounds__(NW * 64, D > 128 ? 1 : 2) void fwd16_kernel(Fwd16Pa
     };
     constexpr int PF = 4;          // LDS fragment prefetch distance (matrix steps)
     constexpr int NSTEP = NM + 2;  // two extra steps drain the element pipeline
+    // Matrix step i issues slot(i) (slots 0 .. NS-1 are S, NS .. NM-1 are P V). At d <= 64 the S
+    // and P V instructions alternate, so none waits on the accumulator the one before it wrote
+    // (measured 3-5% faster there; at larger d the plain order is as fast or faster).
+    constexpr int NMIN = NS < NPV ? NS : NPV;
+    auto slot = [](int i) constexpr -> int {
+      if (D > 64) return i;
+      return i < 2 * NMIN ? ((i & 1) ? NS + (i >> 1) : (i >> 1)) : (NS > NPV ? i - NMIN : NS + (i - NMIN));
+    };
     e16x8 fr[NM];
 #pragma unroll
-    for (int i = 0; i < PF && i < NM; ++i) fr[i] = frag(i);
+    for (int i = 0; i < PF && i < NM; ++i) fr[i] = frag(slot(i));
 #pragma unroll
     for (int i = 0; i < NSTEP; ++i) {
-      if (i + PF < NM) fr[i + PF] = frag(i + PF);
-      if (i < NS) {
-        s_out = H::mfma(fr[i], qreg[i], i == 0 ? f32x16{} : s_out);
-      } else if (i < NM) {
-        const int t = (i - NS) / NDB, db = (i - NS) % NDB;
-        acc_o[db] = H::mfma(fr[i], p_in[t], acc_o[db]);
+      if (i + PF < NM) fr[i + PF] = frag(slot(i + PF));
+      if (i < NM) {
+        const int u = slot(i);
+        if (u < NS) {
+          s_out = H::mfma(fr[i], qreg[u], u == 0 ? f32x16{} : s_out);
+        } else {
+          const int t = (u - NS) / NDB, db = (u - NS) % NDB;
+          acc_o[db] = H::mfma(fr[i], p_in[t], acc_o[db]);
+        }
       }
       // element work per step: stage f of element k runs at step (k * NM / 16) + f
       // (stages: 0 fma, 1 exp, 2 sums)

@@ -159,6 +159,10 @@ __global__ __launch_bounds__(NW * 64, (dkdv_waves_per_simd<D, PART>())) void bwd
   static_assert(!MASKED || BKV == kMaskBlock, "a key tile is one column of the block map");
   constexpr int NKK = D / 16, NDB = D / 32, NQB = BQ / 32;
   using T = SwizzledTile<D>;
+  // dS = P * (dP - delta): without dropout, delta is folded into the dP product's initial
+  // accumulator, one VALU operation less per score (not in the one-wave d = 128 kernel, whose
+  // registers are full: measured slower there).
+  constexpr bool FOLD_DELTA = !DROPOUT && !(D == 128 && PART == 0);
 
   __shared__ __attribute__((aligned(16))) char sq0[TILE_BYTES];
   __shared__ __attribute__((aligned(16))) char so0[TILE_BYTES];
@@ -254,7 +258,7 @@ __global__ __launch_bounds__(NW * 64, (dkdv_waves_per_simd<D, PART>())) void bwd
   auto stage_rows = [&](float* sr) __attribute__((always_inline)) {
     if (w == 0) {
       sr[l] = st_l;
-      sr[BQ + l] = st_d;
+      sr[BQ + l] = FOLD_DELTA ? -st_d : st_d;
     }
   };
 
@@ -272,7 +276,17 @@ __global__ __launch_bounds__(NW * 64, (dkdv_waves_per_simd<D, PART>())) void bwd
     for (int qb = 0; qb < NQB; ++qb) {
       const int q0 = i * BQ + 32 * qb;
       if (DIAG && q0 + 31 < key_w0) continue;  // wave-uniform: every query precedes every key
+      // FOLD_DELTA: the dP product starts from -delta of each register's query, so it yields
+      // dP - delta directly (the staged row statistics hold -delta then).
       f32x16 s = f32x16{}, dp = f32x16{};
+      if constexpr (FOLD_DELTA) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 nd4 = *reinterpret_cast<const f32x4*>(sr + BQ + 32 * qb + 8 * g + 4 * hf);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) dp[4 * g + e] = nd4[e];
+        }
+      }
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
         const int off = T::chunk_off(32 * qb + lq, 2 * kk + hf);
@@ -303,7 +317,7 @@ __global__ __launch_bounds__(NW * 64, (dkdv_waves_per_simd<D, PART>())) void bwd
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const f32x4 lse4 = *reinterpret_cast<const f32x4*>(sr + 32 * qb + 8 * g + 4 * hf);
-        const f32x4 dl4 = *reinterpret_cast<const f32x4*>(sr + BQ + 32 * qb + 8 * g + 4 * hf);
+        const f32x4 dl4 = FOLD_DELTA ? f32x4{} : *reinterpret_cast<const f32x4*>(sr + BQ + 32 * qb + 8 * g + 4 * hf);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const int r = 4 * g + e;
@@ -317,7 +331,7 @@ __global__ __launch_bounds__(NW * 64, (dkdv_waves_per_simd<D, PART>())) void bwd
           } else {
             pb[r >> 3][r & 7] = (E)pr;
           }
-          dsb[r >> 3][r & 7] = (E)(pr * (dpr - dl4[e]));
+          dsb[r >> 3][r & 7] = (E)(FOLD_DELTA ? pr * dpr : pr * (dpr - dl4[e]));
         }
       }
       // dV^T += dO^T P and dK^T += Q^T dS; k-step ks covers queries
@@ -400,6 +414,10 @@ __global__ __launch_bounds__(NW * 64, D > 128 ? 1 : 2) void bwd_dq_kernel(BwdPar
   static_assert(NLD * 64 * NW == BC * NCH, "tile must split evenly over the workgroup's waves");
   constexpr int NKB = BC / 32, NDB = D / 32, NKK = D / 16, NKS = BC / 16;
   using T = SwizzledTile<D>;
+  // dS = P * (dP - delta): without dropout, -delta (constant per lane: one query) is the dP
+  // product's initial accumulator, one VALU operation less per score. Not at d = 96, where the 16
+  // extra registers spill (measured slower).
+  constexpr bool FOLD_DELTA = !DROPOUT && D != 96;
   static_assert(!MASKED || BR == kMaskBlock, "a query tile is one row of the block map");
 
   __shared__ __attribute__((aligned(16))) char sk0[TILE_BYTES];
@@ -506,6 +524,9 @@ __global__ __launch_bounds__(NW * 64, D > 128 ? 1 : 2) void bwd_dq_kernel(BwdPar
   const int tr_col_lane = 16 * (g16 & 1) + 4 * (j16 & 3);
   const int key_lim = CAUSAL ? min(q, Lb - 1) : Lb - 1;
   const float c = p.c;
+  f32x16 ndlt;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) ndlt[r] = -dlt;
 
   // One key tile; MASK for diagonal and ragged tiles (compiled separately from the clean path).
   auto compute = [&](auto mask_tag, int j, const char* kbuf, const char* vbuf) __attribute__((always_inline)) {
@@ -516,7 +537,8 @@ __global__ __launch_bounds__(NW * 64, D > 128 ? 1 : 2) void bwd_dq_kernel(BwdPar
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
       s[kb] = f32x16{};
-      dp[kb] = f32x16{};
+      // FOLD_DELTA: dP starts from -delta (the lane's query), giving dP - delta directly
+      dp[kb] = FOLD_DELTA ? ndlt : f32x16{};
 #pragma unroll
       for (int kk = 0; kk < NKK; ++kk) {
         const int off = T::chunk_off(32 * kb + lq, 2 * kk + hf);
@@ -543,7 +565,7 @@ __global__ __launch_bounds__(NW * 64, D > 128 ? 1 : 2) void bwd_dq_kernel(BwdPar
         }
         float dpr = dp[ks >> 1][r];
         if constexpr (DROPOUT) dpr = dropout_keep(kw[ks >> 1][r >> 2], r & 3, p.drop_thr) ? dpr * p.drop_scale : 0.f;
-        dsb[e] = (E)(pr * (dpr - dlt));
+        dsb[e] = (E)(FOLD_DELTA ? pr * dpr : pr * (dpr - dlt));
       }
       // dQ^T += K^T dS^T; k-step ks covers keys 16ks + {4hf..4hf+3, 8+4hf..8+4hf+3}.
 #pragma unroll

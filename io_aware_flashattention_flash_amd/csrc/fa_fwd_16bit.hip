@@ -339,10 +339,10 @@ __global__ __launch_bounds__(NW * 64, D > 128 ? 1 : 2) void fwd16_kernel(Fwd16Pa
     auto st_acc = [&](int k) __attribute__((always_inline)) {
       const int t = k >> 3, e = k & 7;
       if ((k & 1) == 0) {
-        a0 += pv[k];
+        a0 = k == 0 ? pv[k] : a0 + pv[k];
         asm volatile("" ::"v"(a0));
       } else {
-        a1 += pv[k];
+        a1 = k == 1 ? pv[k] : a1 + pv[k];
         e16x2 pr = {(E)pv[k - 1], (E)pv[k]};
         r0 = H::dot2_ones(pr, r0);  // l~ sums the undropped probabilities
         if constexpr (DROPOUT)

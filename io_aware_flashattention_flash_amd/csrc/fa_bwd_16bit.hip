@@ -140,12 +140,15 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdParams<E> p) {
 // spilling. Non-causal d = 128 also runs the two parts, each at two waves per SIMD (measured
 // faster than one wave per SIMD for the whole; causal d = 128 is faster whole).
 // Waves per SIMD: 2 where the registers fit 256 per lane (d <= 64, d = 96, the parts at d = 128),
-// else 1.
-template <int D, int PART>
-constexpr int dkdv_waves_per_simd() { return (D > 128 || (D == 128 && PART == 0)) ? 1 : 2; }
+// else 1. The dense causal d = 64 kernel fits 168 registers and runs 3 (measured 2.5% faster; the
+// non-causal one was 2.4% slower at 3, and the masked ones spill there).
+template <int D, int PART, bool CAUSAL, bool MASKED>
+constexpr int dkdv_waves_per_simd() {
+  return (D > 128 || (D == 128 && PART == 0)) ? 1 : ((D == 64 && CAUSAL && !MASKED) ? 3 : 2);
+}
 
 template <typename E, int D, int NW, int BQ, bool CAUSAL, bool MASKED, bool DROPOUT, int PART>
-__global__ __launch_bounds__(NW * 64, (dkdv_waves_per_simd<D, PART>())) void bwd_dkdv_kernel(BwdParams<E> p) {
+__global__ __launch_bounds__(NW * 64, (dkdv_waves_per_simd<D, PART, CAUSAL, MASKED>())) void bwd_dkdv_kernel(BwdParams<E> p) {
   constexpr bool WANT_DV = PART != 2, WANT_DK = PART != 1;
   using H = Half16<E>;
   using e16x8 = typename H::x8;
@@ -529,51 +532,147 @@ __global__ __launch_bounds__(NW * 64, D > 128 ? 1 : 2) void bwd_dq_kernel(BwdPar
   for (int r = 0; r < 16; ++r) ndlt[r] = -dlt;
 
   // One key tile; MASK for diagonal and ragged tiles (compiled separately from the clean path).
+  // Two 32-key blocks per tile (d <= 96) are software-pipelined inside the tile:
+  //   A: S and dP of block 0 on the matrix cores;
+  //   B: S and dP of block 1, interleaved with block 0's elementwise work (P, dS);
+  //   C: dQ += K^T dS^T for block 0, interleaved with block 1's elementwise work;
+  //   D: dQ for block 1.
+  // Every matrix instruction is followed by a slice of the elementwise work (stages: exponent
+  // argument, exp2 and mask, dS and 16-bit packing; each a step after the previous), fenced by
+  // scheduling barriers, so a wave keeps the matrix cores and the VALU busy together. The
+  // arithmetic and its order per element are those of the plain sequence.
   auto compute = [&](auto mask_tag, int j, const char* kbuf, const char* vbuf) __attribute__((always_inline)) {
     constexpr bool MASK = decltype(mask_tag)::value;
     const int key0 = j * BC;
-    // (A wave whose rows all precede this tile's keys still runs it; the mask zeroes it.)
-    f32x16 s[NKB], dp[NKB];
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      s[kb] = f32x16{};
-      // FOLD_DELTA: dP starts from -delta (the lane's query), giving dP - delta directly
-      dp[kb] = FOLD_DELTA ? ndlt : f32x16{};
-#pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
-        const int off = T::chunk_off(32 * kb + lq, 2 * kk + hf);
-        s[kb] = H::mfma(lds_read16<E>(kbuf, off), qreg[kk], s[kb]);
-        dp[kb] = H::mfma(lds_read16<E>(vbuf, off), oreg[kk], dp[kb]);
-      }
-    }
     const int lim = key_lim - key0 - 4 * hf;
     uint32_t kw[NKB][4];  // dropout: Philox words of each 32-key half of the tile
-    if constexpr (DROPOUT) {
+    // K^T fragment of dQ k-step ks, output columns 32*db ..: keys 16ks + {4hf..4hf+3, 8+4hf..}.
+    auto frag_dq = [&](int ks, int db) __attribute__((always_inline)) -> e16x8 {
+      const int col = 32 * db + tr_col_lane;
+      const e16x4 a0 = lds_read_tr16<E>(kbuf, T::elem_off(16 * ks + tr_row_lane, col));
+      const e16x4 a1 = lds_read_tr16<E>(kbuf, T::elem_off(16 * ks + 8 + tr_row_lane, col));
+      return cat4<E>(a0, a1);
+    };
+    if constexpr (NKB == 2) {
+      // fragment i of block kb's S / dP products: even i = K (S), odd i = V (dP), k-step i / 2
+      auto frag_sdp = [&](int kb, int i) __attribute__((always_inline)) -> e16x8 {
+        return lds_read16<E>((i & 1) ? vbuf : kbuf, T::chunk_off(32 * kb + lq, 2 * (i >> 1) + hf));
+      };
+      f32x16 s0, dp0, s1, dp1;
+      s0 = f32x16{};
+      dp0 = FOLD_DELTA ? ndlt : f32x16{};
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) dropout_words(q, (key0 >> 5) + kb, head, hf, p.seed_lo, p.seed_hi, kw[kb]);
-    }
-#pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      e16x8 dsb;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int r = (ks & 1) * 8 + e;
-        float pr = fast_exp2(fmaf(s[ks >> 1][r], c, -lse2));
-        if constexpr (MASK) {
-          const int krel = 32 * (ks >> 1) + (r >> 2) * 8 + (r & 3);
-          pr = krel <= lim ? pr : 0.f;
-        }
-        float dpr = dp[ks >> 1][r];
-        if constexpr (DROPOUT) dpr = dropout_keep(kw[ks >> 1][r >> 2], r & 3, p.drop_thr) ? dpr * p.drop_scale : 0.f;
-        dsb[e] = (E)(FOLD_DELTA ? pr * dpr : pr * (dpr - dlt));
+      for (int kk = 0; kk < NKK; ++kk) {
+        s0 = H::mfma(frag_sdp(0, 2 * kk), qreg[kk], s0);
+        dp0 = H::mfma(frag_sdp(0, 2 * kk + 1), oreg[kk], dp0);
       }
-      // dQ^T += K^T dS^T; k-step ks covers keys 16ks + {4hf..4hf+3, 8+4hf..8+4hf+3}.
+      if constexpr (DROPOUT) {
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const int col = 32 * db + tr_col_lane;
-        const e16x4 a0 = lds_read_tr16<E>(kbuf, T::elem_off(16 * ks + tr_row_lane, col));
-        const e16x4 a1 = lds_read_tr16<E>(kbuf, T::elem_off(16 * ks + 8 + tr_row_lane, col));
-        dq[db] = H::mfma(cat4<E>(a0, a1), dsb, dq[db]);
+        for (int kb = 0; kb < NKB; ++kb) dropout_words(q, (key0 >> 5) + kb, head, hf, p.seed_lo, p.seed_hi, kw[kb]);
+      }
+      float xv[16], pv[16], dv[16];
+      // stage st of score r of block kb (scores sb, dP - delta or dP in db), packed into dsb
+      auto elem = [&](int kb, const f32x16& sb, const f32x16& db, e16x8 (&dsb)[2], int r, int st)
+                      __attribute__((always_inline)) {
+        if (st == 0) {
+          xv[r] = fmaf(sb[r], c, -lse2);
+          asm volatile("" ::"v"(xv[r]));
+        } else if (st == 1) {
+          float pr = fast_exp2(xv[r]);
+          if constexpr (MASK) {
+            const int krel = 32 * kb + (r >> 2) * 8 + (r & 3);
+            pr = krel <= lim ? pr : 0.f;
+          }
+          pv[r] = pr;
+          asm volatile("" ::"v"(pv[r]));
+        } else {
+          float dpr = db[r];
+          if constexpr (DROPOUT) dpr = dropout_keep(kw[kb][r >> 2], r & 3, p.drop_thr) ? dpr * p.drop_scale : 0.f;
+          dv[r] = FOLD_DELTA ? pv[r] * dpr : pv[r] * (dpr - dlt);
+          if (r & 1) {
+            dsb[r >> 3][(r & 7) - 1] = (E)dv[r - 1];
+            dsb[r >> 3][r & 7] = (E)dv[r];
+            asm volatile("" ::"v"(dsb[r >> 3]));
+          }
+        }
+      };
+      // NM matrix instructions (fragment i from frag(i), issued by issue(i, fragment)) with the
+      // 16 scores' elementwise stages spread over them; fragments fetched PF instructions ahead.
+      auto stage = [&](auto nm_c, auto&& frag, auto&& issue, auto&& work) __attribute__((always_inline)) {
+        constexpr int NM = decltype(nm_c)::value;
+        constexpr int PF = NM < 3 ? NM : 3;
+        e16x8 fr[NM];
+#pragma unroll
+        for (int i = 0; i < PF; ++i) fr[i] = frag(i);
+#pragma unroll
+        for (int i = 0; i < NM + 2; ++i) {
+          if (i + PF < NM) fr[i + PF] = frag(i + PF);
+          if (i < NM) issue(i, fr[i]);
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int s0_ = r * NM / 16;
+            if (s0_ + 2 == i) work(r, 2);
+            if (s0_ + 1 == i) work(r, 1);
+            if (s0_ == i) work(r, 0);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      };
+      e16x8 dsb0[2], dsb1[2];
+      // B
+      stage(std::integral_constant<int, 2 * NKK>{}, [&](int i) __attribute__((always_inline)) { return frag_sdp(1, i); },
+            [&](int i, const e16x8& f) __attribute__((always_inline)) {
+              if (i & 1)
+                dp1 = H::mfma(f, oreg[i >> 1], i == 1 ? (FOLD_DELTA ? ndlt : f32x16{}) : dp1);
+              else
+                s1 = H::mfma(f, qreg[i >> 1], i == 0 ? f32x16{} : s1);
+            },
+            [&](int r, int st) __attribute__((always_inline)) { elem(0, s0, dp0, dsb0, r, st); });
+      // C
+      stage(std::integral_constant<int, 2 * NDB>{},
+            [&](int i) __attribute__((always_inline)) { return frag_dq(i / NDB, i % NDB); },
+            [&](int i, const e16x8& f) __attribute__((always_inline)) { dq[i % NDB] = H::mfma(f, dsb0[i / NDB], dq[i % NDB]); },
+            [&](int r, int st) __attribute__((always_inline)) { elem(1, s1, dp1, dsb1, r, st); });
+      // D
+#pragma unroll
+      for (int i = 0; i < 2 * NDB; ++i) dq[i % NDB] = H::mfma(frag_dq(2 + i / NDB, i % NDB), dsb1[i / NDB], dq[i % NDB]);
+    } else {
+      // (A wave whose rows all precede this tile's keys still runs it; the mask zeroes it.)
+      f32x16 s[NKB], dp[NKB];
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        s[kb] = f32x16{};
+        // FOLD_DELTA: dP starts from -delta (the lane's query), giving dP - delta directly
+        dp[kb] = FOLD_DELTA ? ndlt : f32x16{};
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) {
+          const int off = T::chunk_off(32 * kb + lq, 2 * kk + hf);
+          s[kb] = H::mfma(lds_read16<E>(kbuf, off), qreg[kk], s[kb]);
+          dp[kb] = H::mfma(lds_read16<E>(vbuf, off), oreg[kk], dp[kb]);
+        }
+      }
+      if constexpr (DROPOUT) {
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) dropout_words(q, (key0 >> 5) + kb, head, hf, p.seed_lo, p.seed_hi, kw[kb]);
+      }
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        e16x8 dsb;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int r = (ks & 1) * 8 + e;
+          float pr = fast_exp2(fmaf(s[ks >> 1][r], c, -lse2));
+          if constexpr (MASK) {
+            const int krel = 32 * (ks >> 1) + (r >> 2) * 8 + (r & 3);
+            pr = krel <= lim ? pr : 0.f;
+          }
+          float dpr = dp[ks >> 1][r];
+          if constexpr (DROPOUT) dpr = dropout_keep(kw[ks >> 1][r >> 2], r & 3, p.drop_thr) ? dpr * p.drop_scale : 0.f;
+          dsb[e] = (E)(FOLD_DELTA ? pr * dpr : pr * (dpr - dlt));
+        }
+        // dQ^T += K^T dS^T; k-step ks covers keys 16ks + {4hf..4hf+3, 8+4hf..8+4hf+3}.
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) dq[db] = H::mfma(frag_dq(ks, db), dsb, dq[db]);
       }
     }
   };

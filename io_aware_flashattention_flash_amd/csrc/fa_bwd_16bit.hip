@@ -682,14 +682,20 @@ __global__ __launch_bounds__(NW * 64, D > 128 ? 1 : 2) void bwd_dq_kernel(BwdPar
   if (N % BC != 0) j_mask = min(j_mask, n_kv - 1);
   j_mask = min(j_mask, n_kv);
   if (MASKED) j_mask = 0;
+  // Causal: a masked-path tile whose first key follows every row of this wave contributes nothing
+  // to the wave's rows (all its scores are masked); the wave skips it but still issues its share of
+  // the tile loads and meets the barriers.
+  auto run = [&](auto mask_tag, int j, const char* kbuf, const char* vbuf) __attribute__((always_inline)) {
+    if (!(CAUSAL && decltype(mask_tag)::value) || j * BC <= q_w0 + 31) compute(mask_tag, j, kbuf, vbuf);
+  };
   auto pair = [&](auto mask_tag, int u, int u_end) __attribute__((always_inline)) {
     if (u + 1 < n_t) dma(tile(u + 1), sk1, sv1);
-    compute(mask_tag, tile(u), sk0, sv0);
+    run(mask_tag, tile(u), sk0, sv0);
     wait_vmem();
     __syncthreads();
     if (u + 1 < u_end) {
       if (u + 2 < n_t) dma(tile(u + 2), sk0, sv0);
-      compute(mask_tag, tile(u + 1), sk1, sv1);
+      run(mask_tag, tile(u + 1), sk1, sv1);
       wait_vmem();
       __syncthreads();
     }

@@ -29,8 +29,9 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256) void fwd_fp32_kernel(FwdF32Params p) {
   constexpr int NW = 4, BR = 32 * NW, BC = 32, LD = D + 1, NT = 256;
   constexpr int NDB = D / 32;
-  __shared__ float ks[BC * LD];
-  __shared__ float vs[BC * LD];
+  constexpr int PER = BC * D / NT;  // K (and V) elements each thread moves per tile
+  __shared__ float ks_buf[2][BC * LD];
+  __shared__ float vs_buf[2][BC * LD];
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, l = tid & 63, lq = l & 31, hf = l >> 5;
@@ -54,55 +55,78 @@ __global__ __launch_bounds__(256) void fwd_fp32_kernel(FwdF32Params p) {
   for (int db = 0; db < NDB; ++db) acc_o[db] = f32x16{};
   float m_run = -INFINITY, l_run = 0.f;
 
+  // K/V tiles are double-buffered: tile j+1's global loads are issued into registers before tile
+  // j is computed and stored to the other buffer after it, so their latency hides behind the
+  // compute. The barrier at the top of an iteration makes the stores visible and guarantees that
+  // every wave is done with the buffer the next stores overwrite.
+  float kx[PER], vx[PER];
+  auto fetch = [&](int j) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int x = tid + NT * i, r = x / D, c = x % D, key = j * BC + r;
+      kx[i] = key < N ? p.k[base + (size_t)key * D + c] : 0.f;
+      vx[i] = key < N ? p.v[base + (size_t)key * D + c] : 0.f;
+    }
+  };
+  auto deposit = [&](int b) {
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int x = tid + NT * i, r = x / D, c = x % D;
+      ks_buf[b][r * LD + c] = kx[i];
+      vs_buf[b][r * LD + c] = vx[i];
+    }
+  };
+  if (n_kv > 0) {
+    fetch(0);
+    deposit(0);
+  }
   for (int j = 0; j < n_kv; ++j) {
     const int key0 = j * BC;
-    __syncthreads();  // every wave is done with the previous tile
-    for (int x = tid; x < BC * D; x += NT) {
-      const int r = x / D, c = x % D, key = key0 + r;
-      ks[r * LD + c] = key < N ? p.k[base + (size_t)key * D + c] : 0.f;
-      vs[r * LD + c] = key < N ? p.v[base + (size_t)key * D + c] : 0.f;
-    }
-    __syncthreads();
-    if (CAUSAL && key0 > q_w0 + 31) continue;  // wave-uniform: all keys above this wave's rows
-
-    f32x16 s = f32x16{};
+    __syncthreads();  // tile j is in buffer j % 2; every wave is done with buffer (j + 1) % 2
+    if (j + 1 < n_kv) fetch(j + 1);
+    const float* ks = ks_buf[j & 1];
+    const float* vs = vs_buf[j & 1];
+    if (!(CAUSAL && key0 > q_w0 + 31)) {  // wave-uniform: skip tiles whose keys all follow this wave's rows
+      f32x16 s = f32x16{};
 #pragma unroll
-    for (int kk = 0; kk < D / 2; ++kk) s = mfma_f32_32x32x2(ks[lq * LD + 2 * kk + hf], qreg[kk], s);
+      for (int kk = 0; kk < D / 2; ++kk) s = mfma_f32_32x32x2(ks[lq * LD + 2 * kk + hf], qreg[kk], s);
 
-    const bool need_mask = (key0 + BC > N) || (CAUSAL && key0 + BC - 1 > q_w0);
-    float mx = -INFINITY;
+      const bool need_mask = (key0 + BC > N) || (CAUSAL && key0 + BC - 1 > q_w0);
+      float mx = -INFINITY;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float x = s[r] * p.c;
-      if (need_mask) {
-        const int key = key0 + (r >> 2) * 8 + 4 * hf + (r & 3);
-        if (key >= N || (CAUSAL && key > q)) x = -INFINITY;
+      for (int r = 0; r < 16; ++r) {
+        float x = s[r] * p.c;
+        if (need_mask) {
+          const int key = key0 + (r >> 2) * 8 + 4 * hf + (r & 3);
+          if (key >= N || (CAUSAL && key > q)) x = -INFINITY;
+        }
+        s[r] = x;
+        mx = fmaxf(mx, x);
       }
-      s[r] = x;
-      mx = fmaxf(mx, x);
-    }
-    mx = half_swap_max(mx);
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - m_use);
-    m_run = m_new;
-    float rs = 0.f;
+      mx = half_swap_max(mx);
+      const float m_new = fmaxf(m_run, mx);
+      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+      const float alpha = fast_exp2(m_run - m_use);
+      m_run = m_new;
+      float rs = 0.f;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      s[r] = fast_exp2(s[r] - m_use);
-      rs += s[r];
-    }
-    l_run = l_run * alpha + rs;
+      for (int r = 0; r < 16; ++r) {
+        s[r] = fast_exp2(s[r] - m_use);
+        rs += s[r];
+      }
+      l_run = l_run * alpha + rs;
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      acc_o[db] *= alpha;
-      // k-step t pairs register t of both halves: keys (t/4)*8 + 4*hf + t%4.
+      for (int db = 0; db < NDB; ++db) {
+        acc_o[db] *= alpha;
+        // k-step t pairs register t of both halves: keys (t/4)*8 + 4*hf + t%4.
 #pragma unroll
-      for (int t = 0; t < 16; ++t) {
-        const int key = (t >> 2) * 8 + 4 * hf + (t & 3);
-        acc_o[db] = mfma_f32_32x32x2(vs[key * LD + 32 * db + lq], s[t], acc_o[db]);
+        for (int t = 0; t < 16; ++t) {
+          const int key = (t >> 2) * 8 + 4 * hf + (t & 3);
+          acc_o[db] = mfma_f32_32x32x2(vs[key * LD + 32 * db + lq], s[t], acc_o[db]);
+        }
       }
     }
+    if (j + 1 < n_kv) deposit((j + 1) & 1);
   }
 
   const float l_tot = half_swap_sum(l_run);

@@ -140,7 +140,7 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdParams<E> p) {
 // spilling. Non-causal d = 128 also runs the two parts, each at two waves per SIMD (measured
 // faster than one wave per SIMD for the whole; causal d = 128 is faster whole).
 // Waves per SIMD: 2 where the registers fit 256 per lane (d <= 64, d = 96, the parts at d = 128),
-// else 1. The dense causal d = 64 kernel fits 168 registers and runs 3 (measured 2.5% faster; the
+// else 1. The dense causal d = 64 kernel fits 168 registers and runs 3 (measured 2.4% faster; the
 // non-causal one was 2.4% slower at 3, and the masked ones spill there).
 template <int D, int PART, bool CAUSAL, bool MASKED>
 constexpr int dkdv_waves_per_simd() {
@@ -637,7 +637,6 @@ __global__ __launch_bounds__(NW * 64, D > 128 ? 1 : 2) void bwd_dq_kernel(BwdPar
 #pragma unroll
       for (int i = 0; i < 2 * NDB; ++i) dq[i % NDB] = H::mfma(frag_dq(2 + i / NDB, i % NDB), dsb1[i / NDB], dq[i % NDB]);
     } else {
-      // (A wave whose rows all precede this tile's keys still runs it; the mask zeroes it.)
       f32x16 s[NKB], dp[NKB];
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {

@@ -6,8 +6,11 @@
 // fp32 matrix instruction v_mfma_f32_32x32x2_f32, so no operand is rounded:
 // P stays fp32 in the P V product. A wave owns 32 query rows and computes
 // S^T = K Q^T; K/V tiles of 32 keys pass through LDS (rows padded by one float
-// to spread banks). This path serves small or precision-sensitive problems;
-// the bf16 kernel is the throughput path.
+// to spread banks). On longer rows two waves share each 32-row group, one on
+// the even and one on the odd key tiles, and their partial (m, l, O) are merged
+// by the online softmax's block merge (same pages, same sections). This path
+// serves small or precision-sensitive problems; the bf16 kernel is the
+// throughput path.
 #include "fa_device.h"
 #include "fa_launch.h"
 
@@ -25,21 +28,28 @@ struct FwdF32Params {
   float c;  // scale * log2(e)
 };
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256) void fwd_fp32_kernel(FwdF32Params p) {
-  constexpr int NW = 4, BR = 32 * NW, BC = 32, LD = D + 1, NT = 256;
+// KH = 1: 4 waves, one per 32-row query group, each over all key tiles. KH = 2: 8 waves, two per
+// query group taking the even and the odd key tiles, merged at the end (two waves per SIMD hide
+// each other's load and exp latencies on long rows; on a few tiles the merge costs more).
+template <int D, bool CAUSAL, int KH>
+__global__ __launch_bounds__(256 * KH) void fwd_fp32_kernel(FwdF32Params p) {
+  constexpr int NQG = 4, BR = 32 * NQG, BC = 32, LD = D + 1, NT = 256 * KH;
   constexpr int NDB = D / 32;
-  constexpr int PER = BC * D / NT;  // K (and V) elements each thread moves per tile
-  __shared__ float ks_buf[2][BC * LD];
-  __shared__ float vs_buf[2][BC * LD];
+  constexpr int TILE = BC * LD;                  // floats of one K (or V) tile in LDS
+  constexpr int PER = KH * BC * D / NT;          // K (and V) elements each thread moves per stage
+  constexpr int REC = 2 + 16 * NDB;              // merge record per lane: m, l, O accumulator
+  static_assert(KH == 1 || NQG * 64 * REC <= 4 * KH * TILE, "merge records fit in the tile buffers");
+  // [buffer][key half] K tiles, then the same for V; reused for the merge at the end
+  __shared__ float lds[4 * KH * TILE];
 
   const int tid = threadIdx.x;
   const int w = tid >> 6, l = tid & 63, lq = l & 31, hf = l >> 5;
+  const int qg = w & 3, kh = KH == 1 ? 0 : w >> 2;  // query group (32 rows) and key half
   const int N = p.N;
   int head, qt;
   map_workgroup(blockIdx.x, p.n_qt, p.nh, CAUSAL ? Order::kLongestFirst : Order::kHeadMajor, true, head, qt);
   const size_t base = (size_t)head * N * D;
-  const int q_w0 = qt * BR + 32 * w;
+  const int q_w0 = qt * BR + 32 * qg;
   const int q = q_w0 + lq;
 
   // Q^T operand of the K=2 instruction: lane (q, hf) holds Q[q][2*kk + hf].
@@ -49,44 +59,47 @@ __global__ __launch_bounds__(256) void fwd_fp32_kernel(FwdF32Params p) {
 
   int n_kv = (N + BC - 1) / BC;
   if (CAUSAL) n_kv = min(n_kv, (min(N, (qt + 1) * BR) - 1) / BC + 1);
+  const int n_st = (n_kv + KH - 1) / KH;  // stage i holds tiles KH i .. KH i + KH - 1 (one per key half)
 
   f32x16 acc_o[NDB];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) acc_o[db] = f32x16{};
   float m_run = -INFINITY, l_run = 0.f;
 
-  // K/V tiles are double-buffered: tile j+1's global loads are issued into registers before tile
-  // j is computed and stored to the other buffer after it, so their latency hides behind the
-  // compute. The barrier at the top of an iteration makes the stores visible and guarantees that
-  // every wave is done with the buffer the next stores overwrite.
+  // The two tiles of a stage are double-buffered: stage i+1's global loads are issued into
+  // registers before stage i is computed and stored to the other buffer after it, so their latency
+  // hides behind the compute. The barrier at the top of an iteration makes the stores visible and
+  // guarantees that every wave is done with the buffer the next stores overwrite.
   float kx[PER], vx[PER];
-  auto fetch = [&](int j) {
+  auto fetch = [&](int i) {
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int x = tid + NT * i, r = x / D, c = x % D, key = j * BC + r;
-      kx[i] = key < N ? p.k[base + (size_t)key * D + c] : 0.f;
-      vx[i] = key < N ? p.v[base + (size_t)key * D + c] : 0.f;
+    for (int e = 0; e < PER; ++e) {
+      const int x = tid + NT * e, h = x / (BC * D), y = x % (BC * D), r = y / D, c = y % D;
+      const int key = (KH * i + h) * BC + r;
+      kx[e] = key < N ? p.k[base + (size_t)key * D + c] : 0.f;
+      vx[e] = key < N ? p.v[base + (size_t)key * D + c] : 0.f;
     }
   };
   auto deposit = [&](int b) {
 #pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      const int x = tid + NT * i, r = x / D, c = x % D;
-      ks_buf[b][r * LD + c] = kx[i];
-      vs_buf[b][r * LD + c] = vx[i];
+    for (int e = 0; e < PER; ++e) {
+      const int x = tid + NT * e, h = x / (BC * D), y = x % (BC * D), r = y / D, c = y % D;
+      lds[(KH * b + h) * TILE + r * LD + c] = kx[e];
+      lds[(2 * KH + KH * b + h) * TILE + r * LD + c] = vx[e];
     }
   };
-  if (n_kv > 0) {
+  if (n_st > 0) {
     fetch(0);
     deposit(0);
   }
-  for (int j = 0; j < n_kv; ++j) {
-    const int key0 = j * BC;
-    __syncthreads();  // tile j is in buffer j % 2; every wave is done with buffer (j + 1) % 2
-    if (j + 1 < n_kv) fetch(j + 1);
-    const float* ks = ks_buf[j & 1];
-    const float* vs = vs_buf[j & 1];
-    if (!(CAUSAL && key0 > q_w0 + 31)) {  // wave-uniform: skip tiles whose keys all follow this wave's rows
+  for (int i = 0; i < n_st; ++i) {
+    __syncthreads();  // stage i is in buffer i % 2; every wave is done with buffer (i + 1) % 2
+    if (i + 1 < n_st) fetch(i + 1);
+    const int j = KH * i + kh, key0 = j * BC;
+    const float* ks = lds + (KH * (i & 1) + kh) * TILE;
+    const float* vs = lds + (2 * KH + KH * (i & 1) + kh) * TILE;
+    // wave-uniform: this wave's tile exists and some of its keys precede this wave's last row
+    if (j < n_kv && !(CAUSAL && key0 > q_w0 + 31)) {
       f32x16 s = f32x16{};
 #pragma unroll
       for (int kk = 0; kk < D / 2; ++kk) s = mfma_f32_32x32x2(ks[lq * LD + 2 * kk + hf], qreg[kk], s);
@@ -126,7 +139,37 @@ __global__ __launch_bounds__(256) void fwd_fp32_kernel(FwdF32Params p) {
         }
       }
     }
-    if (j + 1 < n_kv) deposit((j + 1) & 1);
+    if (i + 1 < n_st) deposit((i + 1) & 1);
+  }
+
+  // KH = 2: merge the two key halves of each query group. The odd-tile wave publishes its running
+  // max, sum and output accumulator; the even-tile wave rescales both to the common max (the
+  // online softmax's block merge) and writes the result.
+  if constexpr (KH == 2) {
+    __syncthreads();  // every wave is done with the tile buffers
+    float* rec = lds + (qg * 64 + l) * REC;
+    if (kh == 1) {
+      rec[0] = m_run;
+      rec[1] = l_run;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) rec[2 + 16 * db + e] = acc_o[db][e];
+    }
+    __syncthreads();
+    if (kh == 1) return;
+    {
+      const float m1 = rec[0], l1 = rec[1];
+      const float m_new = fmaxf(m_run, m1);
+      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+      const float a0 = fast_exp2(m_run - m_use), a1 = fast_exp2(m1 - m_use);
+      l_run = l_run * a0 + l1 * a1;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc_o[db][e] = acc_o[db][e] * a0 + rec[2 + 16 * db + e] * a1;
+      m_run = m_new;
+    }
   }
 
   const float l_tot = half_swap_sum(l_run);
@@ -149,7 +192,12 @@ __global__ __launch_bounds__(256) void fwd_fp32_kernel(FwdF32Params p) {
 
 template <int D, bool CAUSAL>
 static hipError_t launch_cfg(const FwdF32Params& prm, hipStream_t stream) {
-  hipLaunchKernelGGL((fwd_fp32_kernel<D, CAUSAL>), dim3(prm.n_qt * prm.nh), dim3(256), 0, stream, prm);
+  // two key halves pay from about eight key tiles per row (measured: N = 128 is 10% faster with
+  // one, N = 1000 16% faster with two)
+  if (prm.N > 256)
+    hipLaunchKernelGGL((fwd_fp32_kernel<D, CAUSAL, 2>), dim3(prm.n_qt * prm.nh), dim3(512), 0, stream, prm);
+  else
+    hipLaunchKernelGGL((fwd_fp32_kernel<D, CAUSAL, 1>), dim3(prm.n_qt * prm.nh), dim3(256), 0, stream, prm);
   return hipGetLastError();
 }
 

@@ -171,8 +171,10 @@ def test_fwd_bf16_ragged(N, causal, d):
 
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("N", [1, 17, 100, 129, 300])
+@pytest.mark.parametrize("N", [1, 17, 100, 129, 257, 300, 333])
 def test_fwd_fp32_ragged(N, causal, d):
+    """Rows up to 256 keys run one wave per 32-row group; longer rows two (even / odd key tiles,
+    merged). 257 and 333 give an odd key-tile count, so the last stage has no odd tile."""
     w = inputs.Workload("t", "fp32", 1, 3, N, d, causal, False)
     x = inputs.make_inputs(w, seed=7 * N + d)
     o, lse = gpu_fwd(x, w)

@@ -36,10 +36,11 @@
  *              error status has launched nothing and written nothing.
  *   Errors     The library never aborts and never prints. Launch failures are
  *              reported as FA_ERR_HIP.
- *   Support    bf16: d in {64, 128}, forward (also key-split, and masked with optional
- *              dropout) and backward (also masked with optional dropout).
- *              fp16 (IEEE binary16): the same as bf16.
- *              fp32: d in {64, 128}, forward only (no masks).
+ *   Support    (any call outside this matrix returns FA_ERR_UNSUPPORTED)
+ *              bf16, fp16: d in {32, 64, 96, 128, 256}; every entry point (forward,
+ *                          key-split, masked with optional dropout, backward and its
+ *                          stages, masked backward). fp16 is IEEE binary16.
+ *              fp32:       d in {64, 128}; flash_attn_fwd only (no masks, no backward).
  *              B, H, N >= 1, B*H*N*d < 2^31 elements per tensor and
  *              N*d < 2^29 (one head is addressed with 32-bit byte offsets).
  */
@@ -76,6 +77,10 @@ typedef enum { FA_DTYPE_FP32 = 0, FA_DTYPE_BF16 = 1, FA_DTYPE_FP16 = 2 } fa_dtyp
 
 /*
  * Forward: O = softmax(scale * Q K^T [+ causal mask]) V and LSE.
+ * Defined by codechina.net CUDA/FlashAttention article, section 3 (S = Q K^T, P = softmax(S),
+ * O = P V) and section 4.2 (per-block running maximum m and sum l merged across key blocks);
+ * 52jiny.com FlashAttention explainer, "key ideas" parts 1-3 (tiles in on-chip memory, online
+ * softmax, one fused kernel that writes back only O and the row statistics, here LSE = m + ln l).
  *   q, k, v  [B,H,N,d] of `dtype`, read only.
  *   o        [B,H,N,d] of `dtype`, written (rounded to nearest even for bf16 and fp16).
  *   lse      [B,H,N] float32, written; may be NULL when not wanted.
@@ -161,7 +166,11 @@ fa_status_t flash_attn_fwd_kvsplit(const void* q, const void* k, const void* v, 
 size_t flash_attn_bwd_workspace_size(int B, int H, int N, int d, int dtype);
 
 /*
- * Backward with recomputation, for the loss sum(O * dO):
+ * Backward with recomputation, for the loss sum(O * dO). Defined by 52jiny.com FlashAttention
+ * explainer, "key ideas" part 4 (the backward keeps only O and the softmax statistics and
+ * recomputes the probabilities block by block instead of storing the N x N matrix) and
+ * codechina.net article, section 4.2 (the statistics m, l that make the recomputation exact);
+ * the gradient formulas below are the chain rule through the row softmax of section 3.
  *   D  = rowsum(dO * O)                     (into the workspace)
  *   P  = exp(scale * Q K^T - LSE)           (recomputed tile by tile)
  *   dV = P^T dO,  dP = dO V^T,  dS = P * (dP - D),

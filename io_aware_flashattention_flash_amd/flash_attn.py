@@ -95,6 +95,16 @@ def _check_tensor(name: str, t: torch.Tensor, like: Optional[torch.Tensor] = Non
         raise ValueError(f"{name} must match q in shape, dtype and device")
 
 
+def _check_workspace(workspace: torch.Tensor, q: torch.Tensor) -> int:
+    """A caller-supplied workspace must be a contiguous tensor on q's device (its address is passed
+    to kernels that write it); returns its size in bytes."""
+    if not isinstance(workspace, torch.Tensor):
+        raise TypeError("workspace must be a torch.Tensor")
+    if workspace.device != q.device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on q's device")
+    return workspace.numel() * workspace.element_size()
+
+
 def _stream_handle(t: torch.Tensor) -> int:
     return torch.cuda.current_stream(t.device).cuda_stream
 
@@ -200,9 +210,7 @@ def flash_attn_bwd_masked(dout: torch.Tensor, q: torch.Tensor, k: torch.Tensor, 
     need = flash_attn_bwd_workspace_size(B, H, N, d, dt)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    if workspace.device != q.device or not workspace.is_contiguous():
-        raise ValueError("workspace must be a contiguous tensor on q's device")
-    ws_bytes = workspace.numel() * workspace.element_size()
+    ws_bytes = _check_workspace(workspace, q)
     st = load_library().flash_attn_bwd_masked(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
                                               _ptr(dk), _ptr(dv), _ptr(workspace), ws_bytes, B, H, N, d, scale,
                                               int(bool(causal)), _ptr(seqlens), _ptr(block_mask), float(dropout_p),
@@ -257,10 +265,10 @@ def flash_attn_fwd_kvsplit(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, sc
     need = flash_attn_fwd_kvsplit_workspace_size(B, H, Nq, Nk, d, num_splits, dt)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    ws_bytes = _check_workspace(workspace, q)
     st = load_library().flash_attn_fwd_kvsplit(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Nq, Nk, d,
                                                scale, int(bool(causal)), _ptr(seqlens_k), int(num_splits),
-                                               _ptr(workspace),
-                                               workspace.numel() * workspace.element_size(), dt, _stream_handle(q))
+                                               _ptr(workspace), ws_bytes, dt, _stream_handle(q))
     _check(st)
     return out, lse
 
@@ -292,9 +300,7 @@ def flash_attn_bwd(dout: torch.Tensor, q: torch.Tensor, k: torch.Tensor, v: torc
     need = flash_attn_bwd_workspace_size(B, H, N, d, dt)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
-    if workspace.device != q.device or not workspace.is_contiguous():
-        raise ValueError("workspace must be a contiguous tensor on q's device")
-    ws_bytes = workspace.numel() * workspace.element_size()
+    ws_bytes = _check_workspace(workspace, q)
     st = load_library().flash_attn_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout), _ptr(dq),
                                        _ptr(dk), _ptr(dv), _ptr(workspace), ws_bytes, B, H, N, d, scale,
                                        int(bool(causal)), dt, _stream_handle(q))

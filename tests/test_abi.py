@@ -281,3 +281,75 @@ def test_bwd_stage_validation(lib):
     assert _dq(lib, dq=A + 8) == ALIGN
     assert _dq(lib, o=None) == NULLP
     assert _dq(lib, o=A + 4) == ALIGN
+
+
+def _support_matrix():
+    """{dtype code: set of head dims} from the header's 'Support' paragraph."""
+    text = open(HEADER).read()
+    m16 = re.search(r"bf16, fp16:\s*d in \{([0-9, ]+)\}", text)
+    m32 = re.search(r"fp32:\s*d in \{([0-9, ]+)\};\s*flash_attn_fwd only", text)
+    assert m16 and m32, "support lines not found in the header"
+    d16 = {int(x) for x in m16.group(1).split(",")}
+    d32 = {int(x) for x in m32.group(1).split(",")}
+    return {0: d32, 1: d16, 2: d16}
+
+
+def test_header_support_matrix_matches_the_abi(lib):
+    """Every entry point accepts exactly the (dtype, d) pairs the header lists: a supported pair
+    gets past the support check to the alignment check (the fake pointers never reach a launch),
+    any other pair is FA_ERR_UNSUPPORTED. fp32 is listed for flash_attn_fwd only."""
+    support = _support_matrix()
+    assert support[1] == {32, 64, 96, 128, 256} and support[0] == {64, 128}
+    for dtype in (0, 1, 2):
+        for d in range(1, 300):
+            ok16 = dtype in (1, 2) and d in support[dtype]
+            ok_fwd = d in support[dtype]
+            want = lambda ok: ALIGN if ok else UNSUP  # noqa: E731
+            assert _fwd(lib, d=d, dtype=dtype, q=A + 8) == want(ok_fwd), (dtype, d)
+            assert _kvs(lib, d=d, dtype=dtype, q=A + 8) == want(ok16), (dtype, d)
+            assert _fm(lib, d=d, dtype=dtype, q=A + 8) == want(ok16), (dtype, d)
+            assert _bwd(lib, ptrs={"q": A + 8}, d=d, dtype=dtype) == want(ok16), (dtype, d)
+            assert _bm(lib, d=d, dtype=dtype, q=A + 8) == want(ok16), (dtype, d)
+            assert _dq(lib, d=d, dtype=dtype, q=A + 8) == want(ok16), (dtype, d)
+            assert _dkdv(lib, d=d, dtype=dtype, q=A + 8) == want(ok16), (dtype, d)
+            assert lib.flash_attn_bwd_delta(A, A, A + 2, 1, 1, 8, d, dtype, None) == want(ok16), (dtype, d)
+
+
+class _StubLib:
+    """Stands in for the library in binding-only tests: sizes are answered, compute calls fail."""
+
+    def flash_attn_fwd_kvsplit_workspace_size(self, *args):
+        return 4096
+
+    def flash_attn_bwd_workspace_size(self, *args):
+        return 4096
+
+    def __getattr__(self, name):
+        raise AssertionError(f"{name} must not be reached: the binding should have rejected the call")
+
+
+@pytest.mark.parametrize("entry", ["kvsplit", "bwd", "bwd_masked"])
+@pytest.mark.parametrize("bad", ["other_device", "non_contiguous", "not_a_tensor"])
+def test_binding_rejects_a_bad_workspace_before_any_library_call(monkeypatch, entry, bad):
+    """A workspace on another device than q (here: q on the host, workspace on the meta device), a
+    non-contiguous one, or a non-tensor is rejected in Python; the library's compute entry point is
+    never called, so no foreign address reaches a kernel."""
+    import torch
+    monkeypatch.setattr(fa, "load_library", lambda *a: _StubLib())
+    monkeypatch.setattr(fa, "_check_tensor", lambda name, t, like=None: None)  # accept host tensors here
+    q = torch.zeros(1, 2, 8, 64, dtype=torch.bfloat16)
+    if bad == "other_device":
+        ws = torch.empty(4096, dtype=torch.uint8, device="meta")
+    elif bad == "non_contiguous":
+        ws = torch.empty(2, 4096, dtype=torch.uint8)[:, ::2]
+    else:
+        ws = 12345
+    with pytest.raises((ValueError, TypeError), match="workspace"):
+        if entry == "kvsplit":
+            fa.flash_attn_fwd_kvsplit(q, q, q, workspace=ws)
+        elif entry == "bwd":
+            lse = torch.zeros(1, 2, 8)
+            fa.flash_attn_bwd(q, q, q, q, q, lse, workspace=ws)
+        else:
+            lse = torch.zeros(1, 2, 8)
+            fa.flash_attn_bwd_masked(q, q, q, q, q, lse, workspace=ws)

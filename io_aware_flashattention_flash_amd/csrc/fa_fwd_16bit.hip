@@ -180,7 +180,7 @@ __global__ __launch_bounds__(NW * 64, D > 128 ? 1 : 2) void fwd16_kernel(Fwd16Pa
     if (q < N) {
       const __amdgpu_buffer_rsrc_t ro = make_rsrc(p.o + base, head_bytes);
 #pragma unroll
-      for (int c8 = hf; c8 < D / 8; c8 += 2) buf_store16(ro, (q * D + 8 * c8) * 2, u32x4{0, 0, 0, 0});
+      for (int i = 0; i < D / 16; ++i) buf_store16(ro, (q * D + 8 * (2 * i + hf)) * 2, u32x4{0, 0, 0, 0});
       if (p.lse && hf == 0) p.lse[(size_t)head * N + q] = -INFINITY;
     }
   };

@@ -4,6 +4,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "../../include/flash_attn.h"
 #include "fa_launch.h"
 
@@ -28,17 +30,18 @@ bool is_16bit(int dtype) { return dtype == FA_DTYPE_BF16 || dtype == FA_DTYPE_FP
 }  // namespace
 
 namespace fa {
-// Compute units of the current device (cached per device; a benign race writes the same value).
+// Compute units of the current device, cached per device. Concurrent first calls may each query
+// the runtime, but every store and load of the cache is atomic.
 int device_cu_count() {
-  static int cache[64];
+  static std::atomic<int> cache[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cache[dev] == 0) {
-    int n = 0;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cache[dev] = n;
+    cache[dev].store(n, std::memory_order_relaxed);
   }
-  return cache[dev];
+  return n;
 }
 }  // namespace fa
 

@@ -10,7 +10,7 @@ from io_aware_flashattention_flash_amd import (flash_attn_bwd_masked, flash_attn
                                                flash_attn_fwd_masked, inputs)
 from oracle import attn_fwd_dropout, attn_fwd_kv, attn_fwd_masked, keep_mask, keep_threshold, padded_batch_visible
 from oracle.dropout import random_bytes
-from tests.test_parity_gpu import BF16_LSE, BF16_O, DEV, GRAD, beyond_rounding, dev, grad_errors, host
+from tests.test_parity_gpu import BF16_LSE, BF16_O, DEV, GRAD, beyond_rounding, dev, grad_errors, half_ulp_bf16, host
 
 pytestmark = pytest.mark.gpu
 
@@ -99,7 +99,13 @@ def test_decode_bench_config():
 
 @pytest.mark.parametrize("p", [0.998, 1.0 / 512, 0.0039])
 def test_dropout_threshold_extremes(p):
-    """T = 1 (keep 1/256, weights x256), T = 256 (p rounds to 0: no dropout) and T = 255."""
+    """T = 1 (keep 1/256, weights x256), T = 256 (p rounds to 0: no dropout) and T = 255.
+
+    O is checked on the scale of the kept weights: dividing O by 256 / T gives sum over kept keys of
+    (P_ij) V_j, a sub-convex combination of V rows like an undropped output, and the error beyond
+    the rounding of the stored output, measured on that scale, is held to the bf16 O gate. The kept
+    weights themselves are checked exactly by a run with V = 1: every column of O is then
+    (256 / T) * (sum of the kept probabilities of the row)."""
     B, H, N, d = 1, 2, 300, 64
     x = {n: inputs.random_tensor((B, H, N, d), 60 + i, "bf16") for i, n in enumerate(("q", "k", "v", "do"))}
     tq, tk, tv, tdo = (dev(x[n], torch.bfloat16) for n in ("q", "k", "v", "do"))
@@ -111,8 +117,27 @@ def test_dropout_threshold_extremes(p):
     torch.cuda.synchronize()
     vis = padded_batch_visible(B, H, N, False, None)
     O, L = attn_fwd_dropout(x["q"], x["k"], x["v"], d ** -0.5, vis, keep, p)
-    assert beyond_rounding(host(o), O) <= BF16_O * 256 / max(1, int(np.floor(256 * (1 - p) + 0.5)))
+    T = keep_threshold(p)
+    go = host(o)
+    err_scaled = float(np.max(np.abs(go - O) - half_ulp_bf16(O))) * T / 256
+    print(f"p={p} T={T}: O error beyond output rounding, on the kept-weight scale {err_scaled:.3e}")
+    assert err_scaled <= BF16_O
     assert np.abs(host(lse) - L).max() <= BF16_LSE
+    # kept-weight sums: V = 1 makes every output column (256 / T) * sum_j keep_ij P_ij
+    ones = torch.ones_like(tv)
+    o1, _ = flash_attn_fwd_masked(tq, tk, ones, None, False, dropout_p=p, seed=7)
+    torch.cuda.synchronize()
+    O1, _ = attn_fwd_dropout(x["q"], x["k"], np.ones_like(x["v"]), d ** -0.5, vis, keep, p)
+    g1 = host(o1) * T / 256
+    r1 = O1 * T / 256
+    assert (r1 >= 0).all() and (r1 <= 1 + 1e-12).all()
+    # each kept weight P_ij / l carries the bf16 rounding of P_ij (2^-9 relative) and of the
+    # normaliser's terms (at most 2^-9 relative), and the stored output one more rounding (2^-9 of a
+    # value <= 1): at most 3 * 2^-9 in all
+    err1 = np.abs(g1 - r1).max()
+    print(f"kept-weight sum error {err1:.3e}")
+    assert err1 <= 3 * 2.0 ** -9, err1
+    assert np.array_equal(g1 == 0, r1 == 0)  # rows with no kept key are exactly zero
     from oracle import attn_bwd_dropout
     ref = attn_bwd_dropout(x["q"], x["k"], x["v"], x["do"], d ** -0.5, vis, keep, p)
     for name, gg, r in zip(("dQ", "dK", "dV"), g, ref[:3]):

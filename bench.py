@@ -13,12 +13,15 @@ Prints ONE JSON line. Besides the headline it carries:
                 committed rocprofv3 counter summary, or null if that kernel's source changed since
   cpu_baseline  the float64 CPU oracle timed on the host cores over a bounded sample of heads
   workloads     forward-only TFLOPS of the other bf16 workloads and the fp32 workload's latency
+                (timed before the headline, which therefore starts on a GPU already out of idle)
+  shader clock  the gfx clock sampled from the host (amdsmi) during each timed region, or null
   extras        the same kernels on fp16 storage (the long causal forward and the fwd+bwd step) and
                 the key-split decoding step (one query against 8192 keys, HBM-bound: GB/s)
 """
 from __future__ import annotations
 
 import argparse
+import contextlib
 import json
 import os
 import sys
@@ -63,6 +66,65 @@ def traffic_for(kernel: str):
     return rec.get("bytes_per_launch")
 
 
+class ClockSampler:
+    """Samples the GPU's current shader (gfx) clock in MHz from a host thread while a timed region
+    runs (amdsmi's read-only clock query, every 10 ms). The device is matched to torch's by PCI bus
+    id. If the query is unavailable the summary is None; nothing else depends on it."""
+
+    def __init__(self, props):
+        self.samples, self._stop, self._thread, self._handle = [], None, None, None
+        try:
+            import amdsmi
+
+            amdsmi.amdsmi_init()
+            want = getattr(props, "pci_bus_id", None)
+            handles = amdsmi.amdsmi_get_processor_handles()
+            for h in handles:
+                bdf = amdsmi.amdsmi_get_gpu_device_bdf(h)
+                if (want is None and len(handles) == 1) or (want is not None and int(bdf.split(":")[1], 16) == want):
+                    self._handle = h
+                    break
+            self._amdsmi = amdsmi
+        except Exception:
+            self._handle = None
+
+    def _read(self):
+        info = self._amdsmi.amdsmi_get_clock_info(self._handle, self._amdsmi.AmdSmiClkType.GFX)
+        return float(info["clk"])
+
+    def __enter__(self):
+        import threading
+
+        self.samples = []
+        if self._handle is None:
+            return self
+        self._stop = threading.Event()
+
+        def run():
+            while not self._stop.is_set():
+                try:
+                    self.samples.append(self._read())
+                except Exception:
+                    return
+                self._stop.wait(0.01)
+
+        self._thread = threading.Thread(target=run, daemon=True)
+        self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        if self._thread is not None:
+            self._stop.set()
+            self._thread.join()
+        return False
+
+    def summary(self):
+        if not self.samples:
+            return None
+        t = sorted(self.samples)
+        return {"median_mhz": t[len(t) // 2], "min_mhz": t[0], "max_mhz": t[-1], "samples": len(t)}
+
+
 TORCH_DTYPE = {"bf16": "bfloat16", "fp16": "float16", "fp32": "float32"}
 # Extra lines (not workloads of the metric): the fp16 storage path on the same shapes.
 EXTRAS = ("fwd_fp16_b2h32n4096d128_causal", "fwdbwd_fp16_b4h16n2048d64_causal")
@@ -75,8 +137,9 @@ def extra_workload(name):
     return inputs.Workload(name, "fp16", base.B, base.H, base.N, base.d, base.causal, base.backward, base.q_mult)
 
 
-def time_forward(name, reps, warmup, dev, to_dev, wl=None, cold=False):
-    """Forward-only timing of one workload (HIP events around `reps` back-to-back launches)."""
+def time_forward(name, reps, warmup, dev, to_dev, wl=None, cold=False, clock=None):
+    """Forward-only timing of one workload (HIP events around `reps` back-to-back launches; the
+    shader clock is sampled over them when a ClockSampler is given)."""
     import torch
 
     from io_aware_flashattention_flash_amd import flash_attn_fwd, inputs
@@ -98,17 +161,20 @@ def time_forward(name, reps, warmup, dev, to_dev, wl=None, cold=False):
         reps = int(min(2000, max(20, 300.0 / max(a.elapsed_time(b), 1e-3))))
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    a.record()
-    for _ in range(reps):
-        flash_attn_fwd(qi, ki, vi, wl.scale, wl.causal, out=oi, lse=li)
-    b.record()
-    torch.cuda.synchronize()
+    with (clock if clock is not None else contextlib.nullcontext()):
+        a.record()
+        for _ in range(reps):
+            flash_attn_fwd(qi, ki, vi, wl.scale, wl.causal, out=oi, lse=li)
+        b.record()
+        torch.cuda.synchronize()
     us = a.elapsed_time(b) / reps * 1e3
     tf = wl.fwd_flops() / (us * 1e-6) / 1e12
     peak = PEAK_FP32_TFLOPS if wl.dtype == "fp32" else PEAK_BF16_TFLOPS  # fp16 dense MFMA peak = bf16's
     nbytes = wl.B * wl.H * (4 * wl.N * wl.d * (4 if wl.dtype == "fp32" else 2) + 4 * wl.N)
     out = {"workload": name, "pass": "fwd", "reps": reps, "us": round(us, 2), "tflops": round(tf, 1),
            "pct_of_peak": round(100 * tf / peak, 2), "gbps_algorithmic": round(nbytes / (us * 1e-6) / 1e9, 1)}
+    if clock is not None:
+        out["shader_clock"] = clock.summary()
 
     def call():
         flash_attn_fwd(qi, ki, vi, wl.scale, wl.causal, out=oi, lse=li)
@@ -255,7 +321,7 @@ def time_dropout_step(B, H, N, d, p, dev, reps=50):
             "us": round(us, 2), "tflops": round(flops / (us * 1e-6) / 1e12, 1)}
 
 
-def time_fwdbwd(w, x, steps, warmup, dev, to_dev):
+def time_fwdbwd(w, x, steps, warmup, dev, to_dev, clock=None):
     """One step = forward, dQ (with delta), dK/dV on resident inputs of a 16-bit workload. Returns
     (ms per step over `steps` timed steps, {stage: average ms}) from HIP events on the stream."""
     import torch
@@ -283,18 +349,19 @@ def time_fwdbwd(w, x, steps, warmup, dev, to_dev):
             evs[3].record()
 
     names = ["fwd", "bwd_dq", "bwd_dkdv"]
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(steps)]
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    t0.record()
-    for i in range(steps):
-        step(ev[i])
-    t1.record()
-    torch.cuda.synchronize()
+    with (clock if clock is not None else contextlib.nullcontext()):
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        t0.record()
+        for i in range(steps):
+            step(ev[i])
+        t1.record()
+        torch.cuda.synchronize()
     ms_step = t0.elapsed_time(t1) / steps
     kern_ms = {n: sum(e[j].elapsed_time(e[j + 1]) for e in ev) / steps for j, n in enumerate(names)}
     if not (torch.isfinite(o.float()).all() and torch.isfinite(dq.float()).all()):
@@ -334,10 +401,24 @@ def main():
         print(json.dumps(time_forward(args.workload, args.steps, args.warmup, dev, to_dev)))
         return
 
+    clock = ClockSampler(props)
+
+    # ------------------------------------------------------------------ forward-only workloads
+    # (timed first: their ~0.3 s runs of back-to-back launches also take the GPU out of its idle
+    # clock state before the headline's warm-up steps)
+    workloads = {}
+    if not args.no_workloads:
+        for name, wl in inputs.WORKLOADS.items():
+            if not wl.backward:
+                # the short workloads (N <= 1024) also get cold-cache timings
+                workloads[name] = time_forward(name, None, 10, dev, to_dev, cold=wl.N <= 1024, clock=clock)
+        torch.cuda.empty_cache()
+
     # ------------------------------------------------------------------ headline: fwd + bwd
     w = inputs.WORKLOADS[HEADLINE]
     x = inputs.make_inputs(w)
-    ms_step, kern_ms = time_fwdbwd(w, x, args.steps, args.warmup, dev, to_dev)
+    ms_step, kern_ms = time_fwdbwd(w, x, args.steps, args.warmup, dev, to_dev, clock=clock)
+    headline_clock = clock.summary()
     names = ["fwd", "bwd_dq", "bwd_dkdv"]
 
     f_fwd, f_bwd = w.fwd_flops(), w.bwd_flops()
@@ -362,15 +443,6 @@ def main():
                    "tflops": round(kflops[n] / (kern_ms[n] * 1e-3) / 1e12, 1) if kflops[n] else None,
                    "gbps_algorithmic": round(kbytes[n] / (kern_ms[n] * 1e-3) / 1e9, 1)} for n in names}
     bwd_ms = kern_ms["bwd_dkdv"] + kern_ms["bwd_dq"]
-
-    # ------------------------------------------------------------------ forward-only workloads
-    workloads = {}
-    if not args.no_workloads:
-        for name, wl in inputs.WORKLOADS.items():
-            if not wl.backward:
-                # the short workloads (N <= 1024) also get cold-cache timings
-                workloads[name] = time_forward(name, None, 10, dev, to_dev, cold=wl.N <= 1024)
-        torch.cuda.empty_cache()
 
     # ------------------------------------------------------------------ extra lines: fp16 storage
     extras = {}
@@ -407,11 +479,13 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         from oracle import attn_bwd, attn_fwd
+        affinity = len(os.sched_getaffinity(0))
         try:
             from threadpoolctl import threadpool_info
-            cores = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+            blas = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
         except Exception:
-            cores = len(os.sched_getaffinity(0))
+            blas = None
+        cores = blas if blas is not None else affinity
         heads = [(b, h) for b in range(w.B) for h in range(w.H)]
         done = 0
         c0 = time.perf_counter()
@@ -424,7 +498,9 @@ def main():
                 break
         secs = time.perf_counter() - c0
         per_head = (f_fwd + f_bwd) / len(heads)
-        cpu = {"value": round(per_head * done / secs / 1e12, 6), "unit": "TFLOPS", "cores": cores, "kind": "oracle",
+        cpu = {"value": round(per_head * done / secs / 1e12, 6), "unit": "TFLOPS", "cores": cores,
+               "cores_meaning": "BLAS threads that ran the oracle's matrix products (NumPy's exp runs on one)",
+               "blas_threads": blas, "affinity_cores": affinity, "kind": "oracle",
                "sample": f"float64 oracle forward+backward on {done} of {len(heads)} (batch, head) slices of "
                          f"{HEADLINE}, {secs:.1f} s; value scaled by the workload's flop count per head"}
 
@@ -453,6 +529,7 @@ def main():
         "extras": extras,
         "device": {"name": props.name, "arch": getattr(props, "gcnArchName", ""), "cus": props.multi_processor_count,
                    "torch": torch.__version__, "hip": getattr(torch.version, "hip", None)},
+        "shader_clock_headline": headline_clock,
     }
     print(json.dumps(out))
 

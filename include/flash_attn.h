@@ -65,7 +65,9 @@ typedef enum {
   FA_ERR_MISALIGNED = 5,   /* a pointer is not 16-byte aligned (lse, seqlens: 4-byte) */
   FA_ERR_WORKSPACE = 6,    /* workspace NULL or smaller than flash_attn_bwd_workspace_size() */
   FA_ERR_HIP = 7,          /* the HIP runtime reported an error at launch */
-  FA_ERR_BAD_DROPOUT = 8   /* dropout_p is NaN, infinite, negative or above 511/512 */
+  FA_ERR_BAD_DROPOUT = 8,  /* dropout_p is NaN, infinite, negative or above 511/512 */
+  FA_ERR_SCRATCH_LIMIT = 9 /* (no-allocation entry point) the call needs more scratch than
+                              FA_NOALLOC_SCRATCH_BYTES */
 } fa_status_t;
 
 typedef enum { FA_DTYPE_FP32 = 0, FA_DTYPE_BF16 = 1, FA_DTYPE_FP16 = 2 } fa_dtype_t;
@@ -158,6 +160,26 @@ fa_status_t flash_attn_fwd_kvsplit(const void* q, const void* k, const void* v, 
                                    int B, int H, int Nq, int Nk, int d, float scale, int causal,
                                    const int32_t* seqlens_k, int num_splits, void* workspace,
                                    size_t workspace_bytes, int dtype, void* stream);
+
+/*
+ * flash_attn_fwd_kvsplit without a workspace argument and without any allocation, for callers that
+ * cannot allocate device memory: code being captured into a HIP graph, tight decoding loops, and
+ * harnesses that forbid hipMalloc. Same arguments, checks, kernels and results as
+ * flash_attn_fwd_kvsplit (bitwise equal for the same inputs and num_splits).
+ * The fp32 partials live in a fixed device array of FA_NOALLOC_SCRATCH_BYTES inside the library: one
+ * copy on each GPU the library runs on, held until the process ends. A call whose
+ * flash_attn_fwd_kvsplit_workspace_size() exceeds FA_NOALLOC_SCRATCH_BYTES returns
+ * FA_ERR_SCRATCH_LIMIT and launches nothing. Every call on a GPU shares that GPU's array: calls that
+ * may overlap on one GPU (different streams, or threads issuing without ordering) race on it and
+ * must be serialised by the caller. The array's contents on entry are ignored (every partial is
+ * written before it is read). The first call on a device looks up the array's address there; a
+ * failure of that lookup returns FA_ERR_HIP.
+ */
+#define FA_NOALLOC_SCRATCH_BYTES (16u << 20)
+fa_status_t flash_attn_fwd_kvsplit_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                                           int B, int H, int Nq, int Nk, int d, float scale, int causal,
+                                           const int32_t* seqlens_k, int num_splits, int dtype,
+                                           void* stream);
 
 /*
  * Bytes of device workspace flash_attn_bwd needs for this shape (the per-row

@@ -6,11 +6,11 @@ package holds its Python binding, the in-tree build step and the seeded input re
 from .flash_attn import (FA_DTYPE_BF16, FA_DTYPE_FP16, FA_DTYPE_FP32, FA_MASK_BLOCK, FlashAttnFunction,
                          flash_attention, flash_attn_bwd, flash_attn_bwd_delta, flash_attn_bwd_dkdv, flash_attn_bwd_dq,
                          flash_attn_bwd_masked, flash_attn_bwd_workspace_size, flash_attn_dropout_mask, flash_attn_fwd, flash_attn_fwd_kvsplit,
-                         flash_attn_fwd_kvsplit_workspace_size, flash_attn_fwd_masked, flash_attn_status_string,
+                         flash_attn_fwd_kvsplit_noalloc, flash_attn_fwd_kvsplit_workspace_size, flash_attn_fwd_masked, flash_attn_status_string,
                          load_library)
 
 __all__ = ["FA_DTYPE_BF16", "FA_DTYPE_FP16", "FA_DTYPE_FP32", "FA_MASK_BLOCK", "FlashAttnFunction", "flash_attention", "flash_attn_bwd",
            "flash_attn_bwd_delta", "flash_attn_bwd_dkdv", "flash_attn_bwd_dq", "flash_attn_bwd_workspace_size",
-           "flash_attn_fwd", "flash_attn_fwd_kvsplit", "flash_attn_fwd_kvsplit_workspace_size", "flash_attn_fwd_masked",
+           "flash_attn_fwd", "flash_attn_fwd_kvsplit", "flash_attn_fwd_kvsplit_noalloc", "flash_attn_fwd_kvsplit_workspace_size", "flash_attn_fwd_masked",
            "flash_attn_bwd_masked", "flash_attn_dropout_mask",
            "flash_attn_status_string", "load_library"]

@@ -5,9 +5,35 @@
 #include <stdint.h>
 
 #include <atomic>
+#include <mutex>
 
 #include "../../include/flash_attn.h"
 #include "fa_launch.h"
+
+// Scratch of flash_attn_fwd_kvsplit_noalloc: a fixed device array, one copy per GPU the library
+// runs on, held until the process ends. Host code never uses the array's name as an address: each
+// device's address is looked up once (hipGetSymbolAddress, with that device current) and kept.
+static __device__ __align__(256) char scratch[FA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_addr[kMaxDevices];  // guarded by g_scratch_mutex
+
+// Address of the current device's scratch array (looked up on the first call on that device).
+fa_status_t scratch_of_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return FA_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_addr[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return FA_ERR_HIP;
+    g_scratch_addr[dev] = p;
+  }
+  *out = g_scratch_addr[dev];
+  return FA_OK;
+}
+}  // namespace
 
 namespace {
 
@@ -95,6 +121,37 @@ fa_status_t check_kvsplit_shape(int B, int H, int Nq, int Nk, int d, int num_spl
   if (Nq > Nk || num_splits < 0 || num_splits > kMaxSplits) return FA_ERR_BAD_SHAPE;
   return FA_OK;
 }
+
+// Argument checks of the key-split forward (everything but the workspace).
+fa_status_t check_kvsplit_args(const void* q, const void* k, const void* v, const void* o, const float* lse, int B,
+                               int H, int Nq, int Nk, int d, float scale, const int32_t* seqlens_k, int num_splits,
+                               int dtype) {
+  if (!q || !k || !v || !o) return FA_ERR_NULL_POINTER;
+  fa_status_t st = check_kvsplit_shape(B, H, Nq, Nk, d, num_splits);
+  if (st != FA_OK) return st;
+  if (!is_16bit(dtype) || !supported_d(d)) return FA_ERR_UNSUPPORTED;
+  if (!isfinite(scale)) return FA_ERR_BAD_SCALE;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || (lse && !aligned4(lse)) ||
+      (seqlens_k && !aligned4(seqlens_k)))
+    return FA_ERR_MISALIGNED;
+  return FA_OK;
+}
+
+// Key-split forward with its fp32 partials in `workspace` (checked by the caller: large enough,
+// 16-byte aligned). Every partial the merge reads is written by the split kernel first.
+fa_status_t launch_kvsplit(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int Nq,
+                           int Nk, int d, float scale, int causal, const int32_t* seqlens_k, int num_splits,
+                           void* workspace, int dtype, void* stream) {
+  int tps = 0;
+  const int s = kvsplit_plan(B * H, Nq, Nk, num_splits, &tps);
+  const size_t rows = (size_t)s * B * H * Nq;
+  float* opart = static_cast<float*>(workspace);
+  float* lsepart = reinterpret_cast<float*>(static_cast<char*>(workspace) + round256(rows * d * sizeof(float)));
+  hipError_t e = fa::launch_fwd_16_kvsplit(dtype == FA_DTYPE_FP16, q, k, v, o, lse, B * H, Nq, Nk, d, scale,
+                                           causal != 0, s, tps, opart, lsepart, seqlens_k, H,
+                                           static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
 }  // namespace
 
 extern "C" {
@@ -152,25 +209,26 @@ fa_status_t flash_attn_fwd_masked(const void* q, const void* k, const void* v, v
 fa_status_t flash_attn_fwd_kvsplit(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                                    int Nq, int Nk, int d, float scale, int causal, const int32_t* seqlens_k,
                                    int num_splits, void* workspace, size_t workspace_bytes, int dtype, void* stream) {
-  if (!q || !k || !v || !o) return FA_ERR_NULL_POINTER;
-  fa_status_t st = check_kvsplit_shape(B, H, Nq, Nk, d, num_splits);
+  fa_status_t st = check_kvsplit_args(q, k, v, o, lse, B, H, Nq, Nk, d, scale, seqlens_k, num_splits, dtype);
   if (st != FA_OK) return st;
-  if (!is_16bit(dtype) || !supported_d(d)) return FA_ERR_UNSUPPORTED;
-  if (!isfinite(scale)) return FA_ERR_BAD_SCALE;
-  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || (lse && !aligned4(lse)))
-    return FA_ERR_MISALIGNED;
   if (!workspace || workspace_bytes < flash_attn_fwd_kvsplit_workspace_size(B, H, Nq, Nk, d, num_splits, dtype))
     return FA_ERR_WORKSPACE;
-  if (!aligned16(workspace) || (seqlens_k && !aligned4(seqlens_k))) return FA_ERR_MISALIGNED;
-  int tps = 0;
-  const int s = kvsplit_plan(B * H, Nq, Nk, num_splits, &tps);
-  const size_t rows = (size_t)s * B * H * Nq;
-  float* opart = static_cast<float*>(workspace);
-  float* lsepart = reinterpret_cast<float*>(static_cast<char*>(workspace) + round256(rows * d * sizeof(float)));
-  hipError_t e = fa::launch_fwd_16_kvsplit(dtype == FA_DTYPE_FP16, q, k, v, o, lse, B * H, Nq, Nk, d, scale,
-                                           causal != 0, s, tps, opart, lsepart, seqlens_k, H,
-                                           static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+  if (!aligned16(workspace)) return FA_ERR_MISALIGNED;
+  return launch_kvsplit(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, seqlens_k, num_splits, workspace, dtype,
+                        stream);
+}
+
+fa_status_t flash_attn_fwd_kvsplit_noalloc(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                                           int H, int Nq, int Nk, int d, float scale, int causal,
+                                           const int32_t* seqlens_k, int num_splits, int dtype, void* stream) {
+  fa_status_t st = check_kvsplit_args(q, k, v, o, lse, B, H, Nq, Nk, d, scale, seqlens_k, num_splits, dtype);
+  if (st != FA_OK) return st;
+  if (flash_attn_fwd_kvsplit_workspace_size(B, H, Nq, Nk, d, num_splits, dtype) > FA_NOALLOC_SCRATCH_BYTES)
+    return FA_ERR_SCRATCH_LIMIT;
+  void* ws = nullptr;
+  st = scratch_of_current_device(&ws);
+  if (st != FA_OK) return st;
+  return launch_kvsplit(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, seqlens_k, num_splits, ws, dtype, stream);
 }
 
 size_t flash_attn_bwd_workspace_size(int B, int H, int N, int d, int dtype) {
@@ -299,6 +357,9 @@ const char* flash_attn_status_string(int status) {
     case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace missing or smaller than flash_attn_bwd_workspace_size()";
     case FA_ERR_HIP: return "FA_ERR_HIP: the HIP runtime reported a launch error";
     case FA_ERR_BAD_DROPOUT: return "FA_ERR_BAD_DROPOUT: dropout_p must be finite and in [0, 511/512]";
+    case FA_ERR_SCRATCH_LIMIT:
+      return "FA_ERR_SCRATCH_LIMIT: the call needs more scratch than FA_NOALLOC_SCRATCH_BYTES; use the entry point "
+             "that takes a workspace";
     default: return "unknown flash_attn status";
   }
 }

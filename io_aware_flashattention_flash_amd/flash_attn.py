@@ -45,8 +45,11 @@ SIGNATURES = {
     "flash_attn_bwd_masked": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _size,
                                      _int, _int, _int, _int, _float, _int, _vp, _vp, _float, _u64, _int, _vp]),
     "flash_attn_dropout_mask": (_int, [_vp, _int, _int, _int, _int, _float, _u64, _vp]),
+    "flash_attn_fwd_kvsplit_noalloc": (_int, [_vp, _vp, _vp, _vp, _vp, _int, _int, _int, _int, _int, _float, _int,
+                                              _vp, _int, _int, _vp]),
     "flash_attn_status_string": (ctypes.c_char_p, [_int]),
 }
+FA_NOALLOC_SCRATCH_BYTES = 16 << 20  # the library's fixed scratch per GPU (include/flash_attn.h)
 
 _lib_handle = None
 
@@ -269,6 +272,34 @@ def flash_attn_fwd_kvsplit(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, sc
     st = load_library().flash_attn_fwd_kvsplit(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Nq, Nk, d,
                                                scale, int(bool(causal)), _ptr(seqlens_k), int(num_splits),
                                                _ptr(workspace), ws_bytes, dt, _stream_handle(q))
+    _check(st)
+    return out, lse
+
+
+def flash_attn_fwd_kvsplit_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
+                                   lse: Optional[torch.Tensor] = None, scale: Optional[float] = None,
+                                   causal: bool = False, num_splits: int = 0,
+                                   seqlens_k: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """flash_attn_fwd_kvsplit with its partials in the library's fixed scratch array instead of a
+    workspace: the caller passes the outputs (out [B, H, Nq, d], optional lse [B, H, Nq]), and neither
+    this function nor the library allocates anything. Calls that may overlap on one GPU race on the
+    shared scratch."""
+    _check_tensor("q", q)
+    _check_tensor("k", k)
+    _check_tensor("v", v, k)
+    _check_tensor("out", out, q)
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    if k.shape[0] != B or k.shape[1] != H or k.shape[3] != d or k.dtype != q.dtype or k.device != q.device:
+        raise ValueError("k and v must be [B, H, Nk, d] with q's B, H, d, dtype and device")
+    if lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, Nq) or not lse.is_contiguous()
+                            or lse.device != q.device):
+        raise ValueError("lse must be a contiguous float32 [B, H, Nq] tensor on q's device")
+    _check_seqlens("seqlens_k", seqlens_k, B, q)
+    scale = float(d) ** -0.5 if scale is None else float(scale)
+    st = load_library().flash_attn_fwd_kvsplit_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(lse), B, H, Nq, Nk,
+                                                       d, scale, int(bool(causal)), _ptr(seqlens_k), int(num_splits),
+                                                       _DTYPES[q.dtype], _stream_handle(q))
     _check(st)
     return out, lse
 

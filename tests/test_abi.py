@@ -15,7 +15,7 @@ from io_aware_flashattention_flash_amd import flash_attn as fa
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "flash_attn.h")
 
-OK, NULLP, SHAPE, UNSUP, SCALE, ALIGN, WS, HIP, DROP = range(9)
+OK, NULLP, SHAPE, UNSUP, SCALE, ALIGN, WS, HIP, DROP, SCRATCH = range(10)
 A = 0x10000  # a 16-byte-aligned fake address; never dereferenced (validation fails first)
 
 
@@ -52,7 +52,7 @@ def test_exports_have_c_linkage():
 
 
 def test_status_strings(lib):
-    for s in range(9):
+    for s in range(10):
         txt = fa.flash_attn_status_string(s)
         assert txt.startswith("FA_"), txt
     assert "unknown" in fa.flash_attn_status_string(99)
@@ -353,3 +353,35 @@ def test_binding_rejects_a_bad_workspace_before_any_library_call(monkeypatch, en
         else:
             lse = torch.zeros(1, 2, 8)
             fa.flash_attn_bwd_masked(q, q, q, q, q, lse, workspace=ws)
+
+
+def _kvs_na(lib, q=A, k=A, v=A, o=A, lse=A, B=1, H=1, Nq=1, Nk=8, d=64, scale=0.125, causal=0, splits=0, dtype=1,
+            seqlens_k=None):
+    return lib.flash_attn_fwd_kvsplit_noalloc(q, k, v, o, lse, B, H, Nq, Nk, d, scale, causal, seqlens_k, splits,
+                                              dtype, None)
+
+
+def test_kvsplit_noalloc_validation(lib):
+    """The no-allocation key-split forward checks its arguments like flash_attn_fwd_kvsplit (before
+    anything else), and a call whose partials would not fit the fixed scratch is refused with
+    FA_ERR_SCRATCH_LIMIT before any HIP call."""
+    assert _kvs_na(lib, q=None) == NULLP
+    assert _kvs_na(lib, Nq=9, Nk=8) == SHAPE
+    assert _kvs_na(lib, splits=65) == SHAPE
+    assert _kvs_na(lib, dtype=0) == UNSUP
+    assert _kvs_na(lib, d=80) == UNSUP
+    assert _kvs_na(lib, scale=math.inf) == SCALE
+    assert _kvs_na(lib, k=A + 8) == ALIGN
+    assert _kvs_na(lib, seqlens_k=A + 2) == ALIGN
+    limit = fa.FA_NOALLOC_SCRATCH_BYTES
+    # 64 splits of B*H*Nq = 1024 rows of d = 128: 64 * 1024 * 129 * 4 bytes > 16 MiB
+    B, H, Nq, Nk, d, S = 8, 32, 4, 8192, 128, 64
+    assert lib.flash_attn_fwd_kvsplit_workspace_size(B, H, Nq, Nk, d, S, 1) > limit
+    assert _kvs_na(lib, B=B, H=H, Nq=Nq, Nk=Nk, d=d, splits=S) == SCRATCH
+    assert "SCRATCH" in fa.flash_attn_status_string(SCRATCH)
+
+
+def test_noalloc_scratch_limit_matches_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define FA_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == fa.FA_NOALLOC_SCRATCH_BYTES

@@ -190,8 +190,169 @@ __global__ __launch_bounds__(256 * KH) void fwd_fp32_kernel(FwdF32Params p) {
   }
 }
 
+// Small problems (few 128-row tiles in all): one workgroup per 32-row query group, so the work
+// spreads over more compute units. Its KH waves take the key tiles j = kh, kh + KH, ... and merge
+// their partial (m, l, O) at the end with the online softmax's block merge. Each tile is read by
+// one wave only, so operands come straight from global memory into registers (no LDS staging);
+// the next tile's loads are issued before the current tile is computed. The dot product runs over
+// the columns in a permuted order that both Q and K use: k-step kk of lane half hf takes column
+// (D / 2) hf + kk, so each lane reads whole 16-byte chunks of its row.
+template <int D, bool CAUSAL, int KH>
+__global__ __launch_bounds__(64 * KH) void fwd_fp32_split_kernel(FwdF32Params p) {
+  constexpr int BC = 32, NDB = D / 32, NK = D / 2;
+  constexpr int REC = 2 + 16 * NDB;  // merge record per lane: m, l, O accumulator
+  __shared__ float rec[(KH > 1 ? KH - 1 : 1) * 64 * REC];
+  const int l = threadIdx.x & 63, lq = l & 31, hf = l >> 5;
+  const int kh = threadIdx.x >> 6;
+  const int N = p.N;
+  int head, qt;
+  map_workgroup(blockIdx.x, p.n_qt, p.nh, CAUSAL ? Order::kLongestFirst : Order::kHeadMajor, true, head, qt);
+  const size_t base = (size_t)head * N * D;
+  const int q0 = qt * 32, q = q0 + lq;
+
+  // Q^T operand: lane (q, hf) holds Q[q][NK hf + kk]; rows >= N read as zero.
+  float qreg[NK];
+#pragma unroll
+  for (int c = 0; c < NK; c += 4) {
+    const f32x4 t = q < N ? *reinterpret_cast<const f32x4*>(p.q + base + (size_t)q * D + NK * hf + c) : f32x4{};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) qreg[c + e] = t[e];
+  }
+  int n_kv = (N + BC - 1) / BC;
+  if (CAUSAL) n_kv = min(n_kv, (min(N, q0 + 32) - 1) / BC + 1);
+
+  // Tile j's operands: K^T rows (lane (key lq, hf): K[key][NK hf + kk]) and V columns (lane (col lq, hf):
+  // V[key(t, hf)][32 db + lq] for the 16 keys t of its half), keys >= N as zero.
+  float kreg[NK], vreg[NDB][16];
+  auto fetch = [&](int j) __attribute__((always_inline)) {
+    const int key = j * BC + lq;
+#pragma unroll
+    for (int c = 0; c < NK; c += 4) {
+      const f32x4 t = key < N ? *reinterpret_cast<const f32x4*>(p.k + base + (size_t)key * D + NK * hf + c) : f32x4{};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) kreg[c + e] = t[e];
+    }
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      const int kv = j * BC + (t >> 2) * 8 + 4 * hf + (t & 3);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) vreg[db][t] = kv < N ? p.v[base + (size_t)kv * D + 32 * db + lq] : 0.f;
+    }
+  };
+
+  f32x16 acc_o[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) acc_o[db] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;
+  if (kh < n_kv) fetch(kh);
+  for (int j = kh; j < n_kv; j += KH) {
+    f32x16 s = f32x16{};
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) s = mfma_f32_32x32x2(kreg[kk], qreg[kk], s);
+    float vt[NDB][16];
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int t = 0; t < 16; ++t) vt[db][t] = vreg[db][t];
+    if (j + KH < n_kv) fetch(j + KH);  // next tile's loads overlap this tile's softmax and P V
+    const int key0 = j * BC;
+    const bool need_mask = (key0 + BC > N) || (CAUSAL && key0 + BC - 1 > q0);
+    float mx = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float x = s[r] * p.c;
+      if (need_mask) {
+        const int key = key0 + (r >> 2) * 8 + 4 * hf + (r & 3);
+        if (key >= N || (CAUSAL && key > q)) x = -INFINITY;
+      }
+      s[r] = x;
+      mx = fmaxf(mx, x);
+    }
+    mx = half_swap_max(mx);
+    const float m_new = fmaxf(m_run, mx);
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = fast_exp2(m_run - m_use);
+    m_run = m_new;
+    float rs = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      s[r] = fast_exp2(s[r] - m_use);
+      rs += s[r];
+    }
+    l_run = l_run * alpha + rs;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      acc_o[db] *= alpha;
+#pragma unroll
+      for (int t = 0; t < 16; ++t) acc_o[db] = mfma_f32_32x32x2(vt[db][t], s[t], acc_o[db]);
+    }
+  }
+
+  // Block merge of the KH partials of each row: waves 1 .. KH-1 publish (m, l, O accumulator);
+  // wave 0 rescales all of them to the common maximum and writes the result.
+  if constexpr (KH > 1) {
+    if (kh > 0) {
+      float* r = rec + ((kh - 1) * 64 + l) * REC;
+      r[0] = m_run;
+      r[1] = l_run;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) r[2 + 16 * db + e] = acc_o[db][e];
+    }
+    __syncthreads();
+    if (kh > 0) return;
+    for (int w = 1; w < KH; ++w) {
+      const float* r = rec + ((w - 1) * 64 + l) * REC;
+      const float m1 = r[0], l1 = r[1];
+      const float m_new = fmaxf(m_run, m1);
+      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+      const float a0 = fast_exp2(m_run - m_use), a1 = fast_exp2(m1 - m_use);
+      l_run = l_run * a0 + l1 * a1;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc_o[db][e] = acc_o[db][e] * a0 + r[2 + 16 * db + e] * a1;
+      m_run = m_new;
+    }
+  }
+  const float l_tot = half_swap_sum(l_run);
+  const float inv = 1.0f / l_tot;
+  if (q < N) {
+    float* Oq = p.o + base + (size_t)q * D;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        f32x4 t;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) t[e] = acc_o[db][4 * g + e] * inv;
+        *reinterpret_cast<f32x4*>(Oq + 32 * db + 8 * g + 4 * hf) = t;
+      }
+    }
+    if (hf == 0 && p.lse) p.lse[(size_t)head * N + q] = (m_run + __log2f(l_tot)) * kLn2;
+  }
+}
+
+// Problems with fewer 128-row tiles in all than this run as 32-row workgroups (the split kernel).
+constexpr int kSmallTiles = 64;
+
 template <int D, bool CAUSAL>
 static hipError_t launch_cfg(const FwdF32Params& prm, hipStream_t stream) {
+  const int n_tiles128 = prm.n_qt * prm.nh;
+  if (prm.N <= 512 && n_tiles128 < kSmallTiles) {
+    FwdF32Params sp = prm;
+    sp.n_qt = (prm.N + 31) / 32;
+    const int n_kv = (prm.N + 31) / 32;
+    const dim3 grid(sp.n_qt * sp.nh);
+    if (n_kv >= 4)
+      hipLaunchKernelGGL((fwd_fp32_split_kernel<D, CAUSAL, 4>), grid, dim3(256), 0, stream, sp);
+    else if (n_kv >= 2)
+      hipLaunchKernelGGL((fwd_fp32_split_kernel<D, CAUSAL, 2>), grid, dim3(128), 0, stream, sp);
+    else
+      hipLaunchKernelGGL((fwd_fp32_split_kernel<D, CAUSAL, 1>), grid, dim3(64), 0, stream, sp);
+    return hipGetLastError();
+  }
   // two key halves pay from about eight key tiles per row (measured: N = 128 is 10% faster with
   // one, N = 1000 16% faster with two)
   if (prm.N > 256)

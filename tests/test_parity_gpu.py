@@ -206,12 +206,28 @@ def test_fwd_bf16_ragged(N, causal, d):
 
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
-@pytest.mark.parametrize("N", [1, 17, 100, 129, 257, 300, 333])
+@pytest.mark.parametrize("N", [1, 17, 50, 96, 100, 129, 257, 300, 333])
 def test_fwd_fp32_ragged(N, causal, d):
-    """Rows up to 256 keys run one wave per 32-row group; longer rows two (even / odd key tiles,
-    merged). 257 and 333 give an odd key-tile count, so the last stage has no odd tile."""
+    """Small problems (here three heads) run as 32-row workgroups whose waves split the key tiles
+    (1, 2 or 4 waves: N = 17, 50, 96 give 1, 2, 3 tiles) and merge their partials; causal groups
+    whose waves have no tile exercise the merge of empty partials."""
     w = inputs.Workload("t", "fp32", 1, 3, N, d, causal, False)
     x = inputs.make_inputs(w, seed=7 * N + d)
+    o, lse = gpu_fwd(x, w)
+    O, L = attn_fwd(x["q"], x["k"], x["v"], w.scale, causal)
+    assert np.abs(host(o) - O).max() <= FP32_O
+    assert np.abs(host(lse) - L).max() <= FP32_LSE
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("B,H,N", [(2, 16, 200), (4, 16, 300), (1, 2, 600), (1, 1, 1000)])
+def test_fwd_fp32_tiled_path(B, H, N, causal, d):
+    """Larger problems run 128-row workgroups that share K/V tiles through LDS: rows up to 256 keys
+    one wave per 32-row group (N = 200), longer rows two (even / odd key tiles, merged; N = 300
+    with an odd tile count, 600, 1000)."""
+    w = inputs.Workload("t", "fp32", B, H, N, d, causal, False)
+    x = inputs.make_inputs(w, seed=3 * N + d + B)
     o, lse = gpu_fwd(x, w)
     O, L = attn_fwd(x["q"], x["k"], x["v"], w.scale, causal)
     assert np.abs(host(o) - O).max() <= FP32_O

@@ -40,23 +40,41 @@ def _run(cmd):
     return out
 
 
-def build(verbose: bool = False, extra_flags=()) -> str:
-    """Compile every HIP source and link libflashattn.so; returns its path."""
+# Library variants: (file name, extra compiler flags). The race-guard variant puts a full wait and a
+# workgroup barrier after every pipeline stage (FA_DEBUG_SYNC in csrc/fa_device.h); tests require
+# its results to equal the main library's bit for bit.
+VARIANTS = {
+    "main": ("libflashattn.so", ()),
+    "debugsync": ("libflashattn_debugsync.so", ("-DFA_DEBUG_SYNC=1",)),
+}
+DEBUGSYNC_LIB_PATH = os.path.join(PKG, VARIANTS["debugsync"][0])
+
+
+def build(verbose: bool = False, extra_flags=(), variants=("main", "debugsync")) -> str:
+    """Compile every HIP source for each library variant and link them; returns the main library's
+    path. All objects of all variants compile in one pool."""
     hipcc = _hipcc()
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    objs = []
-    cmds = []
-    for src in SOURCES:
-        obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-        objs.append(obj)
-        cmds.append([hipcc, *HIPCC_FLAGS, *extra_flags, "-c", os.path.join(CSRC, src), "-o", obj])
-    with concurrent.futures.ThreadPoolExecutor(max_workers=min(4, len(cmds))) as ex:
+    cmds, links = [], []
+    for name in variants:
+        lib_name, vflags = VARIANTS[name]
+        bdir = BUILD_DIR if name == "main" else BUILD_DIR + "_" + name
+        os.makedirs(bdir, exist_ok=True)
+        objs = []
+        for src in SOURCES:
+            obj = os.path.join(bdir, os.path.splitext(src)[0] + ".o")
+            objs.append(obj)
+            cmds.append([hipcc, *HIPCC_FLAGS, *vflags, *extra_flags, "-c", os.path.join(CSRC, src), "-o", obj])
+        links.append((os.path.join(PKG, lib_name), objs))
+    # the largest sources first, so the pool's tail is short
+    cmds.sort(key=lambda c: -os.path.getsize(c[-3]))
+    with concurrent.futures.ThreadPoolExecutor(max_workers=min(8, len(cmds))) as ex:
         for out in ex.map(_run, cmds):
             if verbose and out.strip():
                 print(out)
-    tmp = LIB_PATH + ".tmp"
-    _run([hipcc, "--offload-arch=" + ARCH, "-shared", "-fPIC", *objs, "-o", tmp])
-    os.replace(tmp, LIB_PATH)
+    for path, objs in links:
+        tmp = path + ".tmp"
+        _run([hipcc, "--offload-arch=" + ARCH, "-shared", "-fPIC", *objs, "-o", tmp])
+        os.replace(tmp, path)
     build_abi_roundtrip(hipcc)
     return LIB_PATH
 

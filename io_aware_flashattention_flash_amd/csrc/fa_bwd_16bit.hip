@@ -360,13 +360,17 @@ __global__ __launch_bounds__(NW * 64, (dkdv_waves_per_simd<D, PART, CAUSAL, MASK
   static_assert((BKV / BQ) % 2 == 0, "the diagonal section must keep the buffer parity");
   auto pair = [&](auto diag_tag, int u) __attribute__((always_inline)) {
     if (u + 1 < n_t) dma(tile(u + 1), sq1, so1);
+    debug_stage_sync();
     compute(diag_tag, tile(u), sq0, so0, sr0);
+    debug_stage_sync();
     wait_vmem();
     stage_rows(sr1);
     __syncthreads();
     if (u + 1 < n_t) {
       if (u + 2 < n_t) dma(tile(u + 2), sq0, so0);
+      debug_stage_sync();
       compute(diag_tag, tile(u + 1), sq1, so1, sr1);
+      debug_stage_sync();
       wait_vmem();
       stage_rows(sr0);
       __syncthreads();
@@ -689,12 +693,16 @@ __global__ __launch_bounds__(NW * 64, D > 128 ? 1 : 2) void bwd_dq_kernel(BwdPar
   };
   auto pair = [&](auto mask_tag, int u, int u_end) __attribute__((always_inline)) {
     if (u + 1 < n_t) dma(tile(u + 1), sk1, sv1);
+    debug_stage_sync();
     run(mask_tag, tile(u), sk0, sv0);
+    debug_stage_sync();
     wait_vmem();
     __syncthreads();
     if (u + 1 < u_end) {
       if (u + 2 < n_t) dma(tile(u + 2), sk0, sv0);
+      debug_stage_sync();
       run(mask_tag, tile(u + 1), sk1, sv1);
+      debug_stage_sync();
       wait_vmem();
       __syncthreads();
     }

@@ -224,6 +224,22 @@ __device__ __forceinline__ void buf_load16_to_lds(__amdgpu_buffer_rsrc_t r, char
 // Wait until this wave's outstanding vector-memory operations (including LDS DMA) have completed.
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Race-guard build (compiled with -DFA_DEBUG_SYNC=1): every pipeline stage of the tiled kernels
+// ends with all of the wave's memory operations complete (global, LDS and LDS DMA) and a workgroup
+// barrier, so no stage overlaps another and every tile load is complete before any wave reads it.
+// The stages compute exactly what they compute in the normal build, so both builds must give
+// bitwise-equal results; a difference would expose a missing wait or barrier (a read racing the
+// write that fills or overwrites a buffer). In the normal build this is nothing.
+#ifndef FA_DEBUG_SYNC
+#define FA_DEBUG_SYNC 0
+#endif
+__device__ __forceinline__ void debug_stage_sync() {
+  if constexpr (FA_DEBUG_SYNC != 0) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+  }
+}
+
 template <typename E>
 __device__ __forceinline__ typename Half16<E>::x8 lds_read16(const char* base, int off) {
   return *reinterpret_cast<const typename Half16<E>::x8*>(base + off);

@@ -476,7 +476,9 @@ __global__ __launch_bounds__(NW * 64, D > 128 ? 1 : 2) void fwd16_kernel(Fwd16Pa
   wait_vmem();
   __syncthreads();
   s_half(s0, sk0, 0);
+  debug_stage_sync();
   phase_a(j_first, sk0, sv1, no{});
+  debug_stage_sync();
 #pragma unroll 1
   for (int t = 0; t < n_eff - 2; t += 2) {
     const int j0 = tile(t), j1 = tile(t + 1), j2 = tile(t + 2);
@@ -484,14 +486,20 @@ __global__ __launch_bounds__(NW * 64, D > 128 ? 1 : 2) void fwd16_kernel(Fwd16Pa
     __syncthreads();
     if (t + 2 < n_t) dma(Kh, j2, sk0);
     dma(Vh, j1, sv1);
+    debug_stage_sync();
     phase_b(j0, sk1, sv0, yes{});
+    debug_stage_sync();
     phase_a(j1, sk1, sv0, yes{});
+    debug_stage_sync();
     wait_vmem();
     __syncthreads();
     if (t + 3 < n_t) dma(Kh, tile(t + 3), sk1);
     dma(Vh, j2, sv0);
+    debug_stage_sync();
     phase_b(j1, sk0, sv1, yes{});
+    debug_stage_sync();
     phase_a(j2, sk0, sv1, yes{});
+    debug_stage_sync();
   }
   {  // the last two tiles: the same steps without scoring a tile past the end
     const int t = n_eff - 2;
@@ -499,11 +507,15 @@ __global__ __launch_bounds__(NW * 64, D > 128 ? 1 : 2) void fwd16_kernel(Fwd16Pa
     wait_vmem();
     __syncthreads();
     dma(Vh, j1, sv1);
+    debug_stage_sync();
     phase_b(j0, sk1, sv0, yes{});
+    debug_stage_sync();
     phase_a(j1, sk1, sv0, yes{});
+    debug_stage_sync();
     wait_vmem();
     __syncthreads();
     phase_b(j1, sk0, sv1, no{});
+    debug_stage_sync();
     pv_only(sv1, 1, p1);
   }
 

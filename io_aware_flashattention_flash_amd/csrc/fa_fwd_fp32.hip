@@ -139,7 +139,9 @@ __global__ __launch_bounds__(256 * KH) void fwd_fp32_kernel(FwdF32Params p) {
         }
       }
     }
+    debug_stage_sync();
     if (i + 1 < n_st) deposit((i + 1) & 1);
+    debug_stage_sync();
   }
 
   // KH = 2: merge the two key halves of each query group. The odd-tile wave publishes its running

@@ -52,14 +52,14 @@ def parse():
     return ap.parse_args()
 
 
-def traffic_for(kernel: str):
+def traffic_for(workload: str, kernel: str):
     """HBM bytes per launch from the committed counter summary, if it matches the current source."""
     from io_aware_flashattention_flash_amd.profiling import source_digest
 
     try:
         with open(TRAFFIC_FILE) as f:
-            rec = json.load(f).get(kernel)
-    except (OSError, ValueError):
+            rec = json.load(f).get("workloads", {}).get(workload, {}).get(kernel)
+    except (OSError, ValueError, AttributeError):
         return None
     if not rec or rec.get("source_digest") != source_digest(kernel):
         return None
@@ -436,7 +436,7 @@ def main():
     else:
         achieved, peak, unit = kbytes[dom] / (kern_ms[dom] * 1e-3) / 1e9, 8000.0, "GB/s"
     roofline = {"kernel": dom, "bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
-                "frac": round(achieved / peak, 4), "traffic": traffic_for(dom),
+                "frac": round(achieved / peak, 4), "traffic": traffic_for(HEADLINE, dom),
                 "algorithmic_flops_per_launch": kflops[dom], "algorithmic_bytes_per_launch": kbytes[dom],
                 "avg_launch_us": round(kern_ms[dom] * 1e3, 2)}
     kernels = {n: {"avg_us": round(kern_ms[n] * 1e3, 2),

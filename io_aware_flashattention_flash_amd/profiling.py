@@ -3,12 +3,20 @@
   python -m io_aware_flashattention_flash_amd.profiling trace STATS_CSV OUT_MD "COMMAND" "TITLE"
       kernel-trace summary (calls, average / min / max duration, share) of this library's kernels
 
-  python -m io_aware_flashattention_flash_amd.profiling traffic --fetch DIR --write DIR \
-      --copy-fetch DIR --copy-write DIR --copy-bytes N --out-json JSON --out-md MD --commands "..."
-      HBM traffic per launch of each attention kernel from FETCH_SIZE / WRITE_SIZE (KiB per
-      dispatch), each scaled by what the same counter reports for a plain device copy of N bytes
-      (bench.py --copy-calibration), stored with a digest of the kernel's source so that a stale
-      figure is never reported for a changed kernel.
+  python -m io_aware_flashattention_flash_amd.profiling traffic --copy-fetch DIR --copy-write DIR \
+      --copy-bytes N --run WORKLOAD FETCH_DIR WRITE_DIR KERNEL_STATS_CSV [--run ...] \
+      --out-json JSON --out-md MD --commands "..."
+      HBM traffic per launch of each attention kernel of each workload from FETCH_SIZE / WRITE_SIZE
+      (KiB per dispatch), each scaled by what the same counter reports for a plain device copy of N
+      bytes (bench.py --copy-calibration); set against the kernel's algorithmic bytes (each tensor
+      moved once: the ratio of fetched to algorithmic read bytes is the re-read factor of K/V tiles
+      that reach past L2) and, with the kernel's average duration from the same workload's kernel
+      trace, as GB/s. Stored with a digest of the kernel's source so that a stale figure is never
+      reported for a changed kernel.
+
+  python -m io_aware_flashattention_flash_amd.profiling counters --run LABEL DIR WORKLOAD ... \
+      --out-md MD --commands "..."
+      MFMA / VALU / LDS counter summary, one counter pass per workload
 """
 from __future__ import annotations
 
@@ -22,8 +30,10 @@ import re
 from collections import defaultdict
 
 CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
-KERNEL_SOURCES = {"fwd": "fa_fwd_16bit.hip", "bwd_dq": "fa_bwd_16bit.hip", "bwd_dkdv": "fa_bwd_16bit.hip"}
-KERNEL_PREFIX = {"fwd": "fa::fwd16_kernel", "bwd_dq": "fa::bwd_dq_kernel", "bwd_dkdv": "fa::bwd_dkdv_kernel"}
+KERNEL_SOURCES = {"fwd": "fa_fwd_16bit.hip", "fwd_fp32": "fa_fwd_fp32.hip", "bwd_dq": "fa_bwd_16bit.hip",
+                  "bwd_dkdv": "fa_bwd_16bit.hip"}
+KERNEL_PREFIX = {"fwd": ("fa::fwd16_kernel",), "fwd_fp32": ("fa::fwd_fp32_kernel", "fa::fwd_fp32_split_kernel"),
+                 "bwd_dq": ("fa::bwd_dq_kernel",), "bwd_dkdv": ("fa::bwd_dkdv_kernel",)}
 
 
 def source_digest(kernel: str) -> str:
@@ -63,10 +73,44 @@ def readable_name(name: str) -> str:
 
 def kernel_key(name: str):
     short = readable_name(name)
-    for key, prefix in KERNEL_PREFIX.items():
-        if short.startswith(prefix + "<"):
+    for key, prefixes in KERNEL_PREFIX.items():
+        if any(short.startswith(prefix + "<") for prefix in prefixes):
             return key
     return None
+
+
+def algorithmic_bytes(w, kernel: str):
+    """(read, write) bytes of one launch of `kernel` on workload w when every tensor crosses HBM once:
+    forward reads Q, K, V and writes O and LSE; dQ reads Q, K, V, O, dO, LSE and writes dQ and delta;
+    dK/dV reads Q, K, V, dO, LSE, delta and writes dK, dV."""
+    s = 4 if w.dtype == "fp32" else 2
+    t, r = w.B * w.H * w.N * w.d * s, w.B * w.H * w.N * 4
+    return {"fwd": (3 * t, t + r), "fwd_fp32": (3 * t, t + r), "bwd_dq": (5 * t + r, t + r),
+            "bwd_dkdv": (4 * t + 2 * r, 2 * t)}[kernel]
+
+
+def kernel_names(directory: str) -> dict:
+    """Kernel key -> the set of readable kernel names (template instances) in a counter pass."""
+    path = glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True)
+    names = defaultdict(set)
+    for row in csv.DictReader(open(path[0])):
+        k = kernel_key(row["Kernel_Name"])
+        if k is not None:
+            names[k].add(readable_name(row["Kernel_Name"]))
+    return names
+
+
+def kernel_avg_us(stats_csv: str, only=None) -> dict:
+    """Average duration per attention kernel key from a --kernel-trace --stats kernel_stats.csv
+    (calls-weighted over the instances of a key; with `only` (key -> names), over those instances)."""
+    tot, calls = defaultdict(float), defaultdict(int)
+    for r in csv.DictReader(open(stats_csv)):
+        k = kernel_key(r["Name"])
+        if k is None or (only is not None and readable_name(r["Name"]) not in only.get(k, ())):
+            continue
+        tot[k] += float(r["TotalDurationNs"])
+        calls[k] += int(r["Calls"])
+    return {k: tot[k] / calls[k] / 1e3 for k in tot}
 
 
 def counter_per_dispatch(directory: str, counter: str, match) -> dict:
@@ -103,6 +147,8 @@ def trace(stats_csv: str, out_md: str, command: str, title: str) -> str:
 
 
 def traffic(a) -> dict:
+    from . import inputs
+
     # the runtime's device-to-device blit kernel that a same-device torch copy launches
     copy = lambda n: "copy" if "copybuffer" in n.lower() else None
     cf = counter_per_dispatch(a.copy_fetch, "FETCH_SIZE", copy).get("copy")
@@ -111,37 +157,56 @@ def traffic(a) -> dict:
         raise RuntimeError("copy calibration kernel not found in the counter output")
     # a copy of N bytes fetches N and writes N: KiB reported per byte moved
     f_scale, w_scale = cf * 1024.0 / a.copy_bytes, cw * 1024.0 / a.copy_bytes
-    fetch = counter_per_dispatch(a.fetch, "FETCH_SIZE", kernel_key)
-    write = counter_per_dispatch(a.write, "WRITE_SIZE", kernel_key)
     out = {"_calibration": {"copy_bytes": a.copy_bytes, "fetch_kib_per_dispatch": cf, "write_kib_per_dispatch": cw,
-                            "fetch_scale": f_scale, "write_scale": w_scale}}
-    for k in sorted(set(fetch) & set(write)):
-        fb, wb = fetch[k] * 1024.0 / f_scale, write[k] * 1024.0 / w_scale
-        out[k] = {"source_digest": source_digest(k), "fetch_bytes_per_launch": round(fb),
-                  "write_bytes_per_launch": round(wb), "bytes_per_launch": round(fb + wb)}
-    with open(a.out_json, "w") as f:
-        json.dump(out, f, indent=1)
-        f.write("\n")
-    lines = ["# HBM traffic per launch (rocprofv3 FETCH_SIZE / WRITE_SIZE, copy-calibrated)", "",
+                            "fetch_scale": f_scale, "write_scale": w_scale}, "workloads": {}}
+    lines = ["# HBM traffic per launch (rocprofv3 FETCH_SIZE / WRITE_SIZE, copy-calibrated), every workload", "",
              "Commands (run from the repository root on one MI355X; one counter per pass):", "", "```",
              a.commands, "```", "",
              f"Calibration: a device copy of {a.copy_bytes} bytes reads FETCH_SIZE {cf:.0f} KiB and WRITE_SIZE "
              f"{cw:.0f} KiB per dispatch, i.e. {f_scale:.4f} / {w_scale:.4f} of the bytes moved; kernel figures "
-             "below are divided by these factors.", "",
-             "| kernel | fetch MB / launch | write MB / launch | total MB / launch |", "|---|---|---|---|"]
-    for k, v in out.items():
-        if k.startswith("_"):
-            continue
-        lines.append(f"| {k} | {v['fetch_bytes_per_launch'] / 1e6:.2f} | {v['write_bytes_per_launch'] / 1e6:.2f} | "
-                     f"{v['bytes_per_launch'] / 1e6:.2f} |")
+             "below are divided by these factors. FETCH_SIZE counts L2 misses sent to the fabric, some of which "
+             "the 256 MB Infinity Cache serves, so it bounds HBM reads from above. Algorithmic bytes move every "
+             "tensor once; fetched / algorithmic read bytes is the factor by which K/V (and Q/dO) tiles are "
+             "re-read past L2. GB/s divide the bytes by the kernel's average duration in the same workload's "
+             "kernel trace.", "",
+             "| workload | kernel | fetch MB | write MB | algorithmic read / write MB | fetch / algorithmic read | "
+             "avg µs | counter GB/s | algorithmic GB/s |", "|---|---|---|---|---|---|---|---|---|"]
+    for wname, fdir, wdir, stats in a.run:
+        w = inputs.WORKLOADS[wname]
+        fetch = counter_per_dispatch(fdir, "FETCH_SIZE", kernel_key)
+        write = counter_per_dispatch(wdir, "WRITE_SIZE", kernel_key)
+        # the trace's averages over the same kernel instances the counter pass ran
+        avg = kernel_avg_us(stats, kernel_names(fdir)) if stats != "-" else {}
+        entry = {}
+        for k in sorted(set(fetch) & set(write)):
+            fb, wb = fetch[k] * 1024.0 / f_scale, write[k] * 1024.0 / w_scale
+            ar, aw = algorithmic_bytes(w, k)
+            e = {"source_digest": source_digest(k), "fetch_bytes_per_launch": round(fb),
+                 "write_bytes_per_launch": round(wb), "bytes_per_launch": round(fb + wb),
+                 "algorithmic_read_bytes": ar, "algorithmic_write_bytes": aw,
+                 "fetch_over_algorithmic_read": round(fb / ar, 3)}
+            us = avg.get(k)
+            if us:
+                e.update({"avg_us": round(us, 2), "counter_gbps": round((fb + wb) / (us * 1e-6) / 1e9, 1),
+                          "algorithmic_gbps": round((ar + aw) / (us * 1e-6) / 1e9, 1)})
+            entry[k] = e
+            lines.append(f"| {wname} | {k} | {fb / 1e6:.2f} | {wb / 1e6:.2f} | {ar / 1e6:.2f} / {aw / 1e6:.2f} | "
+                         f"{fb / ar:.2f} | {e.get('avg_us', '–')} | {e.get('counter_gbps', '–')} | "
+                         f"{e.get('algorithmic_gbps', '–')} |")
+        out["workloads"][wname] = entry
+    with open(a.out_json, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
     with open(a.out_md, "w") as f:
         f.write("\n".join(lines) + "\n")
     return out
 
 
-# One counter pass per workload (at most 8 SQ and 2 GRBM counters, so they fit a single pass).
+# One counter pass per workload (at most 8 SQ and 2 GRBM counters, so they fit a single pass). The
+# fp32 workload counts SQ_INSTS_VALU_MFMA_MOPS_F32 in place of the bf16 matrix-op counter.
 COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_INSTS_VALU SQ_INSTS_MFMA SQ_INSTS_LDS "
             "SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_WAVE_CYCLES GRBM_GUI_ACTIVE")
+COUNTERS_FP32 = COUNTERS.replace("SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_VALU_MFMA_MOPS_F32")
 N_XCD, N_SIMD = 8, 1024  # MI355X: GRBM_GUI_ACTIVE is summed over the 8 XCDs; 256 CUs x 4 SIMDs
 
 
@@ -167,7 +232,7 @@ def counter_summary(directory: str, formula_flops: dict) -> list:
     for key in sorted(total):
         c = {n: v / len(dispatches[key]) for n, v in total[key].items()}
         cycles = c["GRBM_GUI_ACTIVE"] / N_XCD
-        mfma_flops = 512.0 * c["SQ_INSTS_VALU_MFMA_MOPS_BF16"]
+        mfma_flops = 512.0 * (c.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) + c.get("SQ_INSTS_VALU_MFMA_MOPS_F32", 0.0))
         out.append({
             "kernel": key,
             "dispatches": len(dispatches[key]),
@@ -214,9 +279,11 @@ def main():
     t.add_argument("command")
     t.add_argument("title")
     r = sub.add_parser("traffic")
-    for name in ("--fetch", "--write", "--copy-fetch", "--copy-write", "--out-json", "--out-md", "--commands"):
+    for name in ("--copy-fetch", "--copy-write", "--out-json", "--out-md", "--commands"):
         r.add_argument(name, required=True)
     r.add_argument("--copy-bytes", type=int, required=True)
+    r.add_argument("--run", nargs=4, action="append", required=True,
+                   metavar=("WORKLOAD", "FETCH_DIR", "WRITE_DIR", "KERNEL_STATS_CSV"))
     c = sub.add_parser("counters", help="MFMA / VALU / LDS counter summary; --run LABEL DIR WORKLOAD per workload")
     c.add_argument("--run", nargs=3, action="append", required=True, metavar=("LABEL", "DIR", "WORKLOAD"))
     c.add_argument("--out-md", required=True)
@@ -230,7 +297,7 @@ def main():
         for label, directory, wname in a.run:
             w = inputs.WORKLOADS[wname]
             f = w.fwd_flops()
-            runs.append((label, directory, {"fwd": f, "bwd_dq": 0.5 * f, "bwd_dkdv": 2.0 * f}))
+            runs.append((label, directory, {"fwd": f, "fwd_fp32": f, "bwd_dq": 0.5 * f, "bwd_dkdv": 2.0 * f}))
         print(counters_md(runs, a.out_md, a.commands))
     else:
         print(json.dumps(traffic(a), indent=1))

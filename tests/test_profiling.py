@@ -10,7 +10,9 @@ def test_mangled_and_demangled_names_classify_alike():
             ("fa::bwd_dq_kernel<f16, 64, 64, 4, true>", "bwd_dq"),
         "_ZN2fa15bwd_dkdv_kernelIDF16bLi64ELi4ELi64ELb0EEEvNS_9BwdParamsIT_EE":
             ("fa::bwd_dkdv_kernel<bf16, 64, 4, 64, false>", "bwd_dkdv"),
-        "void fa::fwd_fp32_kernel<64, false>(fa::FwdF32Params)": ("fa::fwd_fp32_kernel<64, false>", None),
+        "void fa::fwd_fp32_kernel<64, false>(fa::FwdF32Params)": ("fa::fwd_fp32_kernel<64, false>", "fwd_fp32"),
+        "void fa::fwd_fp32_split_kernel<64, false, 4>(fa::FwdF32Params)": ("fa::fwd_fp32_split_kernel<64, false, 4>",
+                                                                            "fwd_fp32"),
         "_ZN2fa20kvsplit_merge_kernelIDF16bLi128EEEvPKfS2_PT_Pfii": ("fa::kvsplit_merge_kernel<bf16, 128>", None),
         "__amd_rocclr_copyBuffer": ("__amd_rocclr_copyBuffer", None),
     }
@@ -18,3 +20,15 @@ def test_mangled_and_demangled_names_classify_alike():
         assert readable_name(raw) == pretty
         assert kernel_key(raw) == key
     assert kernel_key("void fa::fwd16_kernel<__bf16, 64, 64, 4, true, false>(fa::Fwd16Params<__bf16>)") == "fwd"
+
+
+def test_algorithmic_bytes_move_each_tensor_once():
+    from io_aware_flashattention_flash_amd import inputs
+    from io_aware_flashattention_flash_amd.profiling import algorithmic_bytes
+    w = inputs.WORKLOADS["fwdbwd_bf16_b4h16n2048d64_causal"]
+    t = 4 * 16 * 2048 * 64 * 2
+    r = 4 * 16 * 2048 * 4
+    assert algorithmic_bytes(w, "fwd") == (3 * t, t + r)
+    assert sum(algorithmic_bytes(w, "bwd_dkdv")) == 6 * t + 2 * r == sum(algorithmic_bytes(w, "bwd_dq"))
+    c1 = inputs.WORKLOADS["fwd_fp32_b1h1n128d64"]
+    assert sum(algorithmic_bytes(c1, "fwd_fp32")) == 4 * 128 * 64 * 4 + 128 * 4

@@ -454,6 +454,46 @@ def test_fwd_bf16_rising_scores(d, causal):
     assert lerr <= BF16_LSE
 
 
+def _rising_row_inputs(N, d, rise_log2, at, seed):
+    """Q, K, V where every score of keys >= `at` exceeds the first 32 keys' maximum by about
+    `rise_log2` log2 units: all queries point along e1 with length a, keys 0 .. at-1 have e1
+    component 1, later keys 1 + delta, where a * delta * scale * log2(e) = rise_log2 (scale 1/sqrt(d));
+    small noise elsewhere keeps rows and keys distinct."""
+    rng = np.random.default_rng(seed)
+    scale = d ** -0.5
+    a = np.sqrt(rise_log2 / (scale * np.log2(np.e)))
+    q = 0.05 * rng.standard_normal((1, 2, N, d)).astype(np.float32)
+    k = 0.05 * rng.standard_normal((1, 2, N, d)).astype(np.float32)
+    q[..., 0] = a
+    k[..., 0] = 1.0
+    k[..., at:, 0] = 1.0 + a
+    v = rng.standard_normal((1, 2, N, d)).astype(np.float32)
+    return {"q": inputs.round_to_bf16(q), "k": inputs.round_to_bf16(k), "v": inputs.round_to_bf16(v)}
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("rise", [100.0, 200.0])
+def test_fwd_bf16_scores_far_above_the_first_half(rise, d, causal):
+    """Every score from key 333 on exceeds the first 32 keys' maximum by ~100 or ~200 log2 units. The
+    running reference maximum starts at the first half's and must move by that much mid-row: without
+    the overflow guard the later probabilities would be ~2^100 (finite) or overflow exp2's fp32 range
+    (~2^200). Both must match the oracle, causal (rows before key 333 never see the climb) or not.
+"""
+    N = 700
+    w = inputs.Workload("t", "bf16", 1, 2, N, d, causal, False)
+    x = _rising_row_inputs(N, d, rise, at=333, seed=int(rise) + d)
+    o, lse = gpu_fwd(x, w)
+    O, L = attn_fwd(x["q"], x["k"], x["v"], w.scale, causal)
+    oh, lh = host(o), host(lse)
+    assert np.isfinite(oh).all() and np.isfinite(lh).all()
+    err, beyond = float(np.abs(oh - O).max()), beyond_rounding(oh, O)
+    lerr = float(np.abs(lh - L).max())
+    print(f"rise {rise} d {d} causal {causal}: O err {err:.3e}, beyond output rounding {beyond:.3e}, LSE err {lerr:.3e}")
+    assert beyond <= BF16_O
+    assert lerr <= BF16_LSE
+
+
 def test_zero_scale_is_mean_of_visible_values():
     """scale = 0 makes every visible score equal: O_i = mean of V_0..V_i (causal), LSE_i = ln(i+1)."""
     w = inputs.Workload("t", "fp32", 1, 1, 257, 64, True, False)

@@ -26,6 +26,7 @@ from __future__ import annotations
 
 import argparse
 import contextlib
+import itertools
 import json
 import os
 import sys
@@ -141,6 +142,39 @@ def extra_workload(name):
     return inputs.Workload(name, "fp16", base.B, base.H, base.N, base.d, base.causal, base.backward, base.q_mult)
 
 
+SETTLE_MS = 30.0  # GPU time of untimed calls enqueued right before every timed run
+
+
+def timed_calls(call, reps, warmup, clock=None):
+    """Average ms per call of `reps` back-to-back calls between two HIP events (reps=None: about
+    0.3 s of calls). Before them, untimed calls covering SETTLE_MS of GPU time are enqueued with no
+    host synchronisation in between: after an idle gap of >= 5 ms the GPU runs its first ~10 ms of
+    work in a slower transient, which the timed calls would otherwise include. Returns (ms, reps)."""
+    import torch
+
+    for _ in range(warmup):
+        call()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    call()
+    b.record()
+    torch.cuda.synchronize()
+    one = max(a.elapsed_time(b), 1e-3)
+    if reps is None:
+        reps = int(min(2000, max(20, 300.0 / one)))
+    settle = int(min(5000, max(1, SETTLE_MS / one)))
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    with (clock if clock is not None else contextlib.nullcontext()):
+        for _ in range(settle):
+            call()
+        a.record()
+        for _ in range(reps):
+            call()
+        b.record()
+        torch.cuda.synchronize()
+    return a.elapsed_time(b) / reps, reps
+
+
 def time_forward(name, reps, warmup, dev, to_dev, wl=None, cold=False, clock=None):
     """Forward-only timing of one workload (HIP events around `reps` back-to-back launches; the
     shader clock is sampled over them when a ClockSampler is given)."""
@@ -154,24 +188,11 @@ def time_forward(name, reps, warmup, dev, to_dev, wl=None, cold=False, clock=Non
     qi, ki, vi = (to_dev(xi[n], dt) for n in ("q", "k", "v"))
     oi = torch.empty_like(qi)
     li = torch.empty(wl.B, wl.H, wl.N, device=dev)
-    for _ in range(warmup):
+    def call():
         flash_attn_fwd(qi, ki, vi, wl.scale, wl.causal, out=oi, lse=li)
-    if reps is None:  # about 0.3 s of back-to-back launches, so clocks settle
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        flash_attn_fwd(qi, ki, vi, wl.scale, wl.causal, out=oi, lse=li)
-        b.record()
-        torch.cuda.synchronize()
-        reps = int(min(2000, max(20, 300.0 / max(a.elapsed_time(b), 1e-3))))
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    with (clock if clock is not None else contextlib.nullcontext()):
-        a.record()
-        for _ in range(reps):
-            flash_attn_fwd(qi, ki, vi, wl.scale, wl.causal, out=oi, lse=li)
-        b.record()
-        torch.cuda.synchronize()
-    us = a.elapsed_time(b) / reps * 1e3
+
+    ms, reps = timed_calls(call, reps, warmup, clock)
+    us = ms * 1e3
     tf = wl.fwd_flops() / (us * 1e-6) / 1e12
     peak = PEAK_FP32_TFLOPS if wl.dtype == "fp32" else PEAK_BF16_TFLOPS  # fp16 dense MFMA peak = bf16's
     nbytes = wl.B * wl.H * (4 * wl.N * wl.d * (4 if wl.dtype == "fp32" else 2) + 4 * wl.N)
@@ -179,9 +200,6 @@ def time_forward(name, reps, warmup, dev, to_dev, wl=None, cold=False, clock=Non
            "pct_of_peak": round(100 * tf / peak, 2), "gbps_algorithmic": round(nbytes / (us * 1e-6) / 1e9, 1)}
     if clock is not None:
         out["shader_clock"] = clock.summary()
-
-    def call():
-        flash_attn_fwd(qi, ki, vi, wl.scale, wl.causal, out=oi, lse=li)
 
     # per-call distribution: each of 50 calls bracketed by its own events (warm caches)
     p10, p50, p90 = percentiles_us(call, 50)
@@ -230,16 +248,9 @@ def time_decode(B, H, Nk, d, reps, dev):
     o = torch.empty_like(q)
     lse = torch.empty(B, H, 1, device=dev)
     ws = torch.empty(flash_attn_fwd_kvsplit_workspace_size(B, H, 1, Nk, d, 0, 1), dtype=torch.uint8, device=dev)
-    for _ in range(10):
-        flash_attn_fwd_kvsplit(q, k, v, None, False, 0, out=o, lse=lse, workspace=ws)
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    a.record()
-    for _ in range(reps):
-        flash_attn_fwd_kvsplit(q, k, v, None, False, 0, out=o, lse=lse, workspace=ws)
-    b.record()
-    torch.cuda.synchronize()
-    us = a.elapsed_time(b) / reps * 1e3
+    ms, reps = timed_calls(lambda: flash_attn_fwd_kvsplit(q, k, v, None, False, 0, out=o, lse=lse, workspace=ws),
+                           reps, 10)
+    us = ms * 1e3
     nbytes = B * H * (2 * Nk * d * 2 + 2 * d * 2 + 4)
     return {"workload": f"decode_bf16_b{B}h{H}nq1nk{Nk}d{d}", "pass": "fwd (key-split + merge)", "reps": reps,
             "us": round(us, 2), "gbps_algorithmic": round(nbytes / (us * 1e-6) / 1e9, 1),
@@ -275,16 +286,9 @@ def time_masked_forward(kind, B, H, N, d, dev, reps=100):
         sl = torch.from_numpy(lens).to(dev)
     o = torch.empty_like(q)
     lse = torch.empty(B, H, N, device=dev)
-    for _ in range(10):
-        flash_attn_fwd_masked(q, k, v, None, True, seqlens=sl, block_mask=bm, out=o, lse=lse)
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    a.record()
-    for _ in range(reps):
-        flash_attn_fwd_masked(q, k, v, None, True, seqlens=sl, block_mask=bm, out=o, lse=lse)
-    b.record()
-    torch.cuda.synchronize()
-    us = a.elapsed_time(b) / reps * 1e3
+    ms, reps = timed_calls(lambda: flash_attn_fwd_masked(q, k, v, None, True, seqlens=sl, block_mask=bm, out=o,
+                                                         lse=lse), reps, 10)
+    us = ms * 1e3
     tf = 4.0 * d * pairs / (us * 1e-6) / 1e12
     return {"workload": f"fwd_bf16_b{B}h{H}n{N}d{d}_causal_{kind}", "pass": "fwd (masked)", "reps": reps,
             "us": round(us, 2), "visible_pairs": pairs, "tflops_visible": round(tf, 1),
@@ -310,16 +314,9 @@ def time_dropout_step(B, H, N, d, p, dev, reps=50):
         flash_attn_bwd_masked(do, q, k, v, o, lse, None, True, dq=grads[0], dk=grads[1], dv=grads[2], workspace=ws,
                               dropout_p=p, seed=seed)
 
-    for s in range(5):
-        step(s)
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    a.record()
-    for s in range(reps):
-        step(100 + s)
-    b.record()
-    torch.cuda.synchronize()
-    us = a.elapsed_time(b) / reps * 1e3
+    seeds = itertools.count()
+    ms, reps = timed_calls(lambda: step(next(seeds)), reps, 5)
+    us = ms * 1e3
     flops = 3.5 * 4.0 * B * H * N * N * d / 2
     return {"workload": f"fwdbwd_bf16_b{B}h{H}n{N}d{d}_causal_dropout{p}", "pass": "fwd+bwd (dropout)", "reps": reps,
             "us": round(us, 2), "tflops": round(flops / (us * 1e-6) / 1e12, 1)}
@@ -356,8 +353,8 @@ def prepare_fwdbwd(w, x, dev, to_dev):
     return step
 
 
-def auto_steps(step, warmup, seconds=0.3):
-    """Steps of `step` that take about `seconds` (after `warmup` untimed ones)."""
+def one_step_ms(step, warmup):
+    """GPU time of one call of `step` (events around it), after `warmup` untimed calls."""
     import torch
 
     for _ in range(warmup):
@@ -367,7 +364,12 @@ def auto_steps(step, warmup, seconds=0.3):
     step()
     b.record()
     torch.cuda.synchronize()
-    return int(min(3000, max(20, seconds * 1e3 / max(a.elapsed_time(b), 1e-3))))
+    return max(a.elapsed_time(b), 1e-3)
+
+
+def auto_steps(step, warmup, seconds=0.3):
+    """Steps of `step` that take about `seconds` (after `warmup` untimed ones)."""
+    return int(min(3000, max(20, seconds * 1e3 / one_step_ms(step, warmup))))
 
 
 class TimedSteps:
@@ -408,17 +410,16 @@ class TimedSteps:
 
 
 def run_fwdbwd(step, steps, warmup, clock=None, sample_every=1):
-    """Times `steps` steps after `warmup` untimed ones, synchronising before and after the timed
-    steps. Returns (ms per step, {stage: average ms}); steps=None times about 0.3 s of steps."""
-    import torch
-
+    """Times `steps` steps (steps=None: about 0.3 s of steps) after `warmup` untimed ones and
+    SETTLE_MS of untimed steps enqueued right before them (see timed_calls). Returns (ms per step,
+    {stage: average ms})."""
+    one_ms = one_step_ms(step, warmup)
     if steps is None:
-        steps = auto_steps(step, warmup)
+        steps = int(min(3000, max(20, 300.0 / one_ms)))
     timed = TimedSteps(step, steps, sample_every)
     with (clock if clock is not None else contextlib.nullcontext()):
-        for _ in range(warmup):
+        for _ in range(int(min(2000, max(1, SETTLE_MS / one_ms)))):
             step()
-        torch.cuda.synchronize()
         timed.enqueue()
         return timed.result()
 

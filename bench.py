@@ -74,7 +74,17 @@ def traffic_for(workload: str, kernel: str):
 class ClockSampler:
     """Samples the GPU's current shader (gfx) clock in MHz from a host thread while a timed region
     runs (amdsmi's read-only clock query, every 10 ms). The device is matched to torch's by PCI bus
-    id. If the query is unavailable the summary is None; nothing else depends on it."""
+    id. If the query is unavailable the summary is None; nothing else depends on it.
+
+    The figure is the one the power-management firmware reports, not a clock measured on the
+    engines. It reads 2.0-2.4 GHz during the long workloads and the headline step, but the idle
+    level (~170 MHz) throughout the short d = 64 and fp32 workloads, even over 0.2-0.3 s of
+    back-to-back launches whose throughput shows the engines running at full clock. The summary uses
+    only samples taken at least SKIP_S after the window opened, and timed_calls keeps the GPU loaded
+    for at least WINDOW_MS while a sampler is open."""
+
+    WINDOW_MS = 300.0
+    SKIP_S = 0.15
 
     def __init__(self, props):
         self.samples, self._stop, self._thread, self._handle = [], None, None, None
@@ -105,10 +115,12 @@ class ClockSampler:
             return self
         self._stop = threading.Event()
 
+        t0 = time.perf_counter()
+
         def run():
             while not self._stop.is_set():
                 try:
-                    self.samples.append(self._read())
+                    self.samples.append((time.perf_counter() - t0, self._read()))
                 except Exception:
                     return
                 self._stop.wait(0.01)
@@ -124,10 +136,11 @@ class ClockSampler:
         return False
 
     def summary(self):
-        if not self.samples:
+        t = sorted(mhz for when, mhz in self.samples if when >= self.SKIP_S)
+        if not t:
             return None
-        t = sorted(self.samples)
-        return {"median_mhz": t[len(t) // 2], "min_mhz": t[0], "max_mhz": t[-1], "samples": len(t)}
+        return {"median_mhz": t[len(t) // 2], "min_mhz": t[0], "max_mhz": t[-1], "samples": len(t),
+                "window_s": round(self.samples[-1][0], 3)}
 
 
 TORCH_DTYPE = {"bf16": "bfloat16", "fp16": "float16", "fp32": "float32"}
@@ -162,7 +175,10 @@ def timed_calls(call, reps, warmup, clock=None):
     one = max(a.elapsed_time(b), 1e-3)
     if reps is None:
         reps = int(min(2000, max(20, 300.0 / one)))
-    settle = int(min(5000, max(1, SETTLE_MS / one)))
+    settle_ms = SETTLE_MS
+    if clock is not None:  # the sampler needs a longer loaded window than short workloads' timed calls
+        settle_ms = max(settle_ms, ClockSampler.WINDOW_MS - reps * one)
+    settle = int(min(50000, max(1, settle_ms / one)))
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     with (clock if clock is not None else contextlib.nullcontext()):
         for _ in range(settle):
@@ -489,19 +505,22 @@ def main():
     # warm-up steps follow it on the GPU without an idle gap)
     extras = {}
     fp16 = None
+    fp16_step = None
     if not args.no_workloads:
         name = "fwdbwd_fp16_b4h16n2048d64_causal"
         wl16 = extra_workload(name)
         fp16_step = prepare_fwdbwd(wl16, inputs.make_inputs(wl16), dev, to_dev)
-        fp16 = TimedSteps(fp16_step, auto_steps(fp16_step, 10))
-        fp16.enqueue()
 
     # ------------------------------------------------------------------ headline: fwd + bwd
     # W untimed warm-up steps, a synchronisation, then exactly K timed steps between two events and
     # a final synchronisation. Every 5th timed step also times its three kernels (the roofline's
-    # kernel durations, measured inside the timed region).
+    # kernel durations, measured inside the timed region). The clock sampler opens before the fp16
+    # line, whose ~0.3 s of steps keep the GPU loaded up to the headline (see ClockSampler).
     timed = TimedSteps(headline_step, args.steps, sample_every=5)
     with clock:
+        if fp16_step is not None:
+            fp16 = TimedSteps(fp16_step, auto_steps(fp16_step, 10))
+            fp16.enqueue()
         for _ in range(args.warmup):
             headline_step()
         torch.cuda.synchronize()

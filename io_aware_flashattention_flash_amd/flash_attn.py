@@ -84,17 +84,20 @@ def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
 
 
 def _check_tensor(name: str, t: torch.Tensor, like: Optional[torch.Tensor] = None) -> None:
+    # (cheap accessors only: these checks run on every call, in front of microsecond kernels)
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
-    if t.device.type != "cuda":
+    if not t.is_cuda:
         raise ValueError(f"{name} must be a GPU tensor, got {t.device}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous [B, H, N, d]")
-    if t.dim() != 4:
-        raise ValueError(f"{name} must be 4-D [B, H, N, d], got {tuple(t.shape)}")
-    if t.dtype not in _DTYPES:
-        raise ValueError(f"{name} must be bfloat16, float16 or float32, got {t.dtype}")
-    if like is not None and (t.shape != like.shape or t.dtype != like.dtype or t.device != like.device):
+    if like is None:
+        if t.dim() != 4:
+            raise ValueError(f"{name} must be 4-D [B, H, N, d], got {tuple(t.shape)}")
+        if t.dtype not in _DTYPES:
+            raise ValueError(f"{name} must be bfloat16, float16 or float32, got {t.dtype}")
+    elif t.shape != like.shape or t.dtype != like.dtype or t.get_device() != like.get_device():
+        # (like has passed these checks itself: matching it makes t 4-D with a supported dtype)
         raise ValueError(f"{name} must match q in shape, dtype and device")
 
 
@@ -109,7 +112,7 @@ def _check_workspace(workspace: torch.Tensor, q: torch.Tensor) -> int:
 
 
 def _stream_handle(t: torch.Tensor) -> int:
-    return torch.cuda.current_stream(t.device).cuda_stream
+    return torch.cuda.current_stream(t.get_device()).cuda_stream
 
 
 def flash_attn_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, scale: Optional[float] = None,

@@ -388,11 +388,58 @@ def auto_steps(step, warmup, seconds=0.3):
     return int(min(3000, max(20, seconds * 1e3 / one_step_ms(step, warmup))))
 
 
+class KernelEvent:
+    """A HIP timing event created with hipEventDisableSystemFence, for the events between kernels:
+    recording a default event performs a system-scope cache write-back and invalidation, which
+    holds the next kernel back and adds ~2 us to each duration measured between such events.
+    Same interface as torch.cuda.Event (record on torch's current stream, elapsed_time in ms). The
+    calls go to the HIP runtime torch has loaded (a second copy of the runtime would not know torch's
+    streams). The events live until the process ends."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000
+    _hip = None
+
+    @classmethod
+    def runtime(cls):
+        if cls._hip is None:
+            import ctypes
+
+            with open("/proc/self/maps") as f:
+                paths = [ln.split()[-1] for ln in f if "libamdhip64" in ln and "/" in ln]
+            if not paths:
+                raise RuntimeError("the HIP runtime is not loaded in this process")
+            cls._hip = ctypes.CDLL(paths[0])
+        return cls._hip
+
+    def __init__(self):
+        import ctypes
+
+        self._h = ctypes.c_void_p()
+        if self.runtime().hipEventCreateWithFlags(ctypes.byref(self._h), ctypes.c_uint(self.DISABLE_SYSTEM_FENCE)):
+            raise RuntimeError("hipEventCreateWithFlags failed")
+
+    def record(self):
+        import ctypes
+
+        import torch
+
+        if self.runtime().hipEventRecord(self._h, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)):
+            raise RuntimeError("hipEventRecord failed")
+
+    def elapsed_time(self, other):
+        import ctypes
+
+        ms = ctypes.c_float()
+        if self.runtime().hipEventElapsedTime(ctypes.byref(ms), self._h, other._h):
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+
 class TimedSteps:
     """K steps of a fwd+bwd step between two HIP events on the stream, enqueued without waiting.
-    Every `sample_every`-th step also records events between its three kernels (forward, dQ, dK/dV);
-    such events hold the next kernel back by ~5 us, so sampling a subset keeps that cost off most
-    steps while still timing each kernel inside the timed region."""
+    Every `sample_every`-th step also records fence-free events (KernelEvent) between its three
+    kernels (forward, dQ, dK/dV); each still costs the next kernel a little, so sampling a subset
+    keeps that off most steps while timing each kernel inside the timed region."""
 
     NAMES = ("fwd", "bwd_dq", "bwd_dkdv")
 
@@ -401,7 +448,7 @@ class TimedSteps:
 
         self.step, self.steps = step, steps
         self.sampled = [i for i in range(steps) if i % sample_every == sample_every - 1] or [steps - 1]
-        self.kev = {i: [torch.cuda.Event(enable_timing=True) for _ in range(4)] for i in self.sampled}
+        self.kev = {i: [KernelEvent() for _ in range(4)] for i in self.sampled}
         self.t0 = torch.cuda.Event(enable_timing=True)
         self.t1 = torch.cuda.Event(enable_timing=True)
 
@@ -553,8 +600,8 @@ def main():
                 "frac": round(achieved / peak, 4), "traffic": traffic_for(HEADLINE, dom),
                 "algorithmic_flops_per_launch": kflops[dom], "algorithmic_bytes_per_launch": kbytes[dom],
                 "avg_launch_us": round(kern_ms[dom] * 1e3, 2),
-                "launch_timing": f"HIP events around each kernel on {len(timed.sampled)} of the {args.steps} timed "
-                                 "steps (every 5th)"}
+                "launch_timing": f"HIP events (hipEventDisableSystemFence) around each kernel on "
+                                 f"{len(timed.sampled)} of the {args.steps} timed steps (every 5th)"}
     kernels = {n: {"avg_us": round(kern_ms[n] * 1e3, 2),
                    "tflops": round(kflops[n] / (kern_ms[n] * 1e-3) / 1e12, 1) if kflops[n] else None,
                    "gbps_algorithmic": round(kbytes[n] / (kern_ms[n] * 1e-3) / 1e9, 1)} for n in names}

@@ -1,7 +1,9 @@
 """Turn rocprofv3 output into the short text summaries kept under profiles/.
 
-  python -m io_aware_flashattention_flash_amd.profiling trace STATS_CSV OUT_MD "COMMAND" "TITLE"
-      kernel-trace summary (calls, average / min / max duration, share) of this library's kernels
+  python -m io_aware_flashattention_flash_amd.profiling trace STATS_CSV OUT_MD "COMMAND" "TITLE" [--bench-json F]
+      kernel-trace summary (calls, average / min / max duration, share) of this library's kernels;
+      with --bench-json, the traced bench.py run's own output line is appended for comparison, and
+      with --plain-json that of the same command run without the profiler
 
   python -m io_aware_flashattention_flash_amd.profiling traffic --copy-fetch DIR --copy-write DIR \
       --copy-bytes N --run WORKLOAD FETCH_DIR WRITE_DIR KERNEL_STATS_CSV [--run ...] \
@@ -130,7 +132,31 @@ def counter_per_dispatch(directory: str, counter: str, match) -> dict:
     return {k: total[k] / len(dispatches[k]) for k in total}
 
 
-def trace(stats_csv: str, out_md: str, command: str, title: str) -> str:
+def _bench_line(bench_json: str) -> str:
+    with open(bench_json) as f:
+        d = json.loads(f.read().strip().splitlines()[-1])
+    r = d["roofline"]
+    kern = ", ".join(f"{n} {k['avg_us']:.2f} µs" for n, k in d["kernels"].items())
+    return (f"value {d['value']} {d['unit']}, {d['ms_per_step']} ms per step; per-kernel event averages "
+            f"({r.get('launch_timing', 'HIP events')}): {kern}; roofline kernel {r['kernel']}, {r['achieved']} "
+            f"{r['unit']} of {r['peak']}, frac {r['frac']}.")
+
+
+def bench_line_section(bench_json: str, plain_json: str = None) -> list:
+    """The bench line printed by the traced run itself and, if given, that of the same command run
+    without the profiler just before on the same box: throughput, per-kernel event averages and
+    roofline fraction, for comparison with the trace's durations."""
+    lines = ["", "## The traced run's bench line", "", _bench_line(bench_json), "",
+             "An event pair around one kernel also spans that launch's dispatch gap after the previous kernel, "
+             "which the profiler lengthens (it adds work to every dispatch); the trace's durations are the kernels' "
+             "own. The trace's averages of the headline's kernel instances also include its warm-up steps."]
+    if plain_json:
+        lines += ["", "## The same command without the profiler (same box, just before)", "", _bench_line(plain_json)]
+    return lines
+
+
+def trace(stats_csv: str, out_md: str, command: str, title: str, bench_json: str = None,
+          plain_json: str = None) -> str:
     rows = list(csv.DictReader(open(stats_csv)))
     lines = [f"# {title}", "", "Command (run from the repository root on one MI355X):", "", "```", command, "```", "",
              "| kernel | calls | avg µs | min µs | max µs | share of GPU time |", "|---|---|---|---|---|---|"]
@@ -140,6 +166,8 @@ def trace(stats_csv: str, out_md: str, command: str, title: str) -> str:
             continue
         lines.append(f"| `{short}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | {float(r['MinNs']) / 1e3:.2f} | "
                      f"{float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.2f}% |")
+    if bench_json:
+        lines += bench_line_section(bench_json, plain_json)
     text = "\n".join(lines) + "\n"
     with open(out_md, "w") as f:
         f.write(text)
@@ -278,6 +306,8 @@ def main():
     t.add_argument("out_md")
     t.add_argument("command")
     t.add_argument("title")
+    t.add_argument("--bench-json", help="the traced bench.py run's output line, appended as a section")
+    t.add_argument("--plain-json", help="the same bench.py command's line without the profiler")
     r = sub.add_parser("traffic")
     for name in ("--copy-fetch", "--copy-write", "--out-json", "--out-md", "--commands"):
         r.add_argument(name, required=True)
@@ -290,7 +320,7 @@ def main():
     c.add_argument("--commands", required=True)
     a = ap.parse_args()
     if a.cmd == "trace":
-        print(trace(a.stats_csv, a.out_md, a.command, a.title))
+        print(trace(a.stats_csv, a.out_md, a.command, a.title, a.bench_json, a.plain_json))
     elif a.cmd == "counters":
         from . import inputs
         runs = []

@@ -159,7 +159,13 @@ __global__ __launch_bounds__(NW * 64, D > 128 ? 1 : 2) void fwd16_kernel(Fwd16Pa
   const int Nk = KV_SPLIT ? p.Nk : p.N;      // key rows
 
   int head, qt;
-  map_workgroup(blockIdx.x, p.n_qt, p.nh, CAUSAL ? Order::kLongestFirst : Order::kHeadMajor, true, head, qt);
+  // Masked launches with lengths: tiles with work first, padding tiles last (map_workgroup_varlen);
+  // the padding tiles' zero rows are then written by the head's tiles with work, spread over the
+  // launch, and the padding workgroups themselves exit at once.
+  const bool vmapped = MASKED && p.seqlens &&
+                       map_workgroup_varlen(blockIdx.x, p.n_qt, p.nh, p.heads, p.seqlens, p.N, BR, CAUSAL, head, qt);
+  if (!vmapped)
+    map_workgroup(blockIdx.x, p.n_qt, p.nh, CAUSAL ? Order::kLongestFirst : Order::kHeadMajor, true, head, qt);
   // Valid query rows Lq and keys Lk of this head's sequence.
   int Lq = N, Lk = Nk;
   if ((KV_SPLIT || MASKED) && p.seqlens) {
@@ -175,17 +181,27 @@ __global__ __launch_bounds__(NW * 64, D > 128 ? 1 : 2) void fwd16_kernel(Fwd16Pa
   const int q_w0 = qt * BR + 32 * w;
   const int q = q_w0 + lq;
 
-  // Rows of this tile that see no key at all (padding rows, empty map rows): O = 0, LSE = -inf.
-  auto write_empty_rows = [&]() __attribute__((always_inline)) {
-    if (q < N) {
+  // Rows that see no key at all (padding rows, empty map rows): O = 0, LSE = -inf. This lane's
+  // row of tile t.
+  auto write_empty_row = [&](int t) __attribute__((always_inline)) {
+    const int row = t * BR + 32 * w + lq;
+    if (row < N) {
       const __amdgpu_buffer_rsrc_t ro = make_rsrc(p.o + base, head_bytes);
 #pragma unroll
-      for (int i = 0; i < D / 16; ++i) buf_store16(ro, (q * D + 8 * (2 * i + hf)) * 2, u32x4{0, 0, 0, 0});
-      if (p.lse && hf == 0) p.lse[(size_t)head * N + q] = -INFINITY;
+      for (int i = 0; i < D / 16; ++i) buf_store16(ro, (row * D + 8 * (2 * i + hf)) * 2, u32x4{0, 0, 0, 0});
+      if (p.lse && hf == 0) p.lse[(size_t)head * N + row] = -INFINITY;
     }
   };
+  auto write_empty_rows = [&]() __attribute__((always_inline)) { write_empty_row(qt); };
+  // A tile with work also writes the padding tiles T + qt, 2T + qt, ... of its head (T = the tiles
+  // with work), when the padding workgroups leave them to it (vmapped).
+  auto write_carried_rows = [&]() __attribute__((always_inline)) {
+    const int T = (Lq + BR - 1) / BR;
+    if (MASKED && vmapped && T > 0)
+      for (int pt = T + qt; pt < p.n_qt; pt += T) write_empty_row(pt);
+  };
   if (MASKED && qt * BR >= Lq) {  // a tile of padding rows only (uniform over the workgroup)
-    write_empty_rows();
+    if (!vmapped || Lq == 0) write_empty_rows();  // else a tile with work of this head writes them
     return;
   }
 
@@ -240,6 +256,7 @@ __global__ __launch_bounds__(NW * 64, D > 128 ? 1 : 2) void fwd16_kernel(Fwd16Pa
     __syncthreads();
     if (cnt == 0) {
       write_empty_rows();
+      write_carried_rows();
       return;
     }
     n_t = 2 * cnt;
@@ -568,6 +585,7 @@ __global__ __launch_bounds__(NW * 64, D > 128 ? 1 : 2) void fwd16_kernel(Fwd16Pa
     const __amdgpu_buffer_rsrc_t rl = make_rsrc(p.lse + (size_t)head * N, N * 4);
     buf_store4(rl, q * 4, lse_row);
   }
+  write_carried_rows();
 }
 
 template <typename E, int D, int BC, int NW, bool CAUSAL, int MODE>

@@ -125,4 +125,62 @@ __device__ __forceinline__ void map_workgroup(int wg, int n_tiles, int nh, Order
   tile = last_is_longest ? n_tiles - 1 - rank : rank;
 }
 
+// Work decomposition with per-sequence lengths (sequence b = head / heads, valid rows L_b; a tile
+// of BR rows is padding when it starts at or past L_b). map_workgroup would interleave padding
+// tiles, which finish at once, with long ones; the hardware dispatches a launch's workgroups in
+// order and lets CUs idle behind such a mix (measured: a quarter of the slots on a length mix of
+// [N/4, N]). Here every XCD takes the same heads as in map_workgroup (head = xcd + 8 t), runs all
+// its tiles with work first, in the same order (longest-first: by tile index, descending, over its
+// heads; head-major: tiles of one head after another), and then all its padding tiles.
+// Applies when heads % 8 == 0 and there are at most 64 sequences (lane b of the wave holds
+// sequence b's tile count); returns false otherwise, and the caller uses map_workgroup.
+// Wave-uniform; every wave of the workgroup computes the same result.
+__device__ __forceinline__ bool map_workgroup_varlen(int wg, int n_tiles, int nh, int heads, const int* seqlens,
+                                                     int N, int BR, bool longest_first, int& head, int& tile) {
+  const int nseq = nh / heads;
+  if ((heads & 7) != 0 || nseq > 64) return false;
+  const int lane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0));
+  int t_lane = 0;  // tiles with work of sequence `lane`
+  if (lane < nseq) t_lane = (min(max(seqlens[lane], 0), N) + BR - 1) / BR;
+  auto tiles_of = [&](int b) __attribute__((always_inline)) { return __builtin_amdgcn_readlane(t_lane, b); };
+  const int x = wg & 7, hp8 = heads >> 3;  // heads of each sequence on this XCD: b*heads + x + 8j, j < hp8
+  int pos = wg >> 3;
+  if (longest_first) {
+    for (int q = n_tiles - 1; q >= 0; --q) {
+      const uint64_t m = __builtin_amdgcn_ballot_w64(lane < nseq && t_lane > q);
+      const int c = hp8 * __builtin_popcountll(m);
+      if (pos < c) {
+        int k = pos / hp8;
+        uint64_t mm = m;
+        for (; k > 0; --k) mm &= mm - 1;  // drop the k lowest sequences that have tile q
+        head = __builtin_ctzll(mm) * heads + x + 8 * (pos % hp8);
+        tile = q;
+        return true;
+      }
+      pos -= c;
+    }
+  } else {
+    for (int b = 0; b < nseq; ++b) {
+      const int tb = tiles_of(b), c = hp8 * tb;
+      if (pos < c) {
+        head = b * heads + x + 8 * (pos / tb);
+        tile = pos % tb;
+        return true;
+      }
+      pos -= c;
+    }
+  }
+  for (int b = 0; b < nseq; ++b) {  // padding tiles
+    const int pb = n_tiles - tiles_of(b), c = hp8 * pb;
+    if (pos < c) {
+      head = b * heads + x + 8 * (pos / pb);
+      tile = n_tiles - pb + pos % pb;
+      return true;
+    }
+    pos -= c;
+  }
+  head = tile = 0;  // not reached: the grid holds n_tiles * nh workgroups
+  return true;
+}
+
 }  // namespace fa

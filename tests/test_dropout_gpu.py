@@ -71,6 +71,12 @@ def test_dropout_with_padding_and_block_map():
     _case(2, 2, N, 128, True, 0.2, seed=77, seqlens=[900, 555], bmap=bmap, in_seed=3)
 
 
+def test_dropout_with_padding_eight_heads():
+    """Lengths with eight heads per sequence (the forward's tiles with work run first and write the
+    padding rows)."""
+    _case(3, 8, 500, 64, True, 0.2, seed=11, seqlens=[500, 0, 333], in_seed=13)
+
+
 def test_dropout_fp16():
     _case(1, 4, 600, 128, True, 0.25, seed=5, dtype="fp16", in_seed=9)
 

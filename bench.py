@@ -448,7 +448,14 @@ class TimedSteps:
 
         self.step, self.steps = step, steps
         self.sampled = [i for i in range(steps) if i % sample_every == sample_every - 1] or [steps - 1]
-        self.kev = {i: [KernelEvent() for _ in range(4)] for i in self.sampled}
+        try:
+            make = KernelEvent
+            make()
+            self.event_kind = "HIP events (hipEventDisableSystemFence)"
+        except (RuntimeError, OSError, AttributeError):  # the HIP runtime's entry points are not reachable
+            make = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+            self.event_kind = "HIP events (torch, default flags)"
+        self.kev = {i: [make() for _ in range(4)] for i in self.sampled}
         self.t0 = torch.cuda.Event(enable_timing=True)
         self.t1 = torch.cuda.Event(enable_timing=True)
 
@@ -600,7 +607,7 @@ def main():
                 "frac": round(achieved / peak, 4), "traffic": traffic_for(HEADLINE, dom),
                 "algorithmic_flops_per_launch": kflops[dom], "algorithmic_bytes_per_launch": kbytes[dom],
                 "avg_launch_us": round(kern_ms[dom] * 1e3, 2),
-                "launch_timing": f"HIP events (hipEventDisableSystemFence) around each kernel on "
+                "launch_timing": f"{timed.event_kind} around each kernel on "
                                  f"{len(timed.sampled)} of the {args.steps} timed steps (every 5th)"}
     kernels = {n: {"avg_us": round(kern_ms[n] * 1e3, 2),
                    "tflops": round(kflops[n] / (kern_ms[n] * 1e-3) / 1e12, 1) if kflops[n] else None,

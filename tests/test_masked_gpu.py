@@ -97,6 +97,20 @@ def test_fwd_padded_eight_heads_with_block_map():
     _check_fwd(o, lse, O, L, beyond_output_rounding=True)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("B,H,N", [(64, 8, 100), (3, 16, 333), (2, 24, 257)])
+def test_fwd_padded_head_layouts(B, H, N, causal):
+    """The padding-last order at its limits: exactly 64 sequences (one per lane of a wave), 16 and
+    24 heads per sequence; non-causal launches take its head-major branch. Lengths include 0 and N."""
+    rng = np.random.default_rng(B * H + N)
+    seqlens = [int(v) for v in rng.integers(0, N + 1, size=B)]
+    seqlens[0], seqlens[-1] = N, 0
+    x = _inputs(B, H, N, 64, seed=B + H + N)
+    o, lse = _fwd(x, 0.125, causal, seqlens, None)
+    O, L = attn_fwd_masked(x["q"], x["k"], x["v"], 0.125, padded_batch_visible(B, H, N, causal, seqlens))
+    _check_fwd(o, lse, O, L, beyond_output_rounding=True)
+
+
 def test_fwd_padded_many_sequences():
     """65 sequences of eight heads (more than one wave's lanes): the launch keeps the plain tile
     order, still correct."""

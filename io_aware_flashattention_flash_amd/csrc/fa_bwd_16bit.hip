@@ -181,7 +181,10 @@ __global__ __launch_bounds__(NW * 64, (dkdv_waves_per_simd<D, PART, CAUSAL, MASK
   const int l = tid & 63, lq = l & 31, hf = l >> 5;
   const int N = p.N;
   int head, kt;
-  map_workgroup(blockIdx.x, p.n_tiles, p.nh, CAUSAL ? Order::kLongestFirst : Order::kHeadMajor, false, head, kt);  // causal: key tile 0 has the most work
+  // causal: key tile 0 has the most work; with sequence lengths, padding key tiles run last
+  if (!(MASKED && p.seqlens &&
+        map_workgroup_varlen(blockIdx.x, p.n_tiles, p.nh, p.heads, p.seqlens, p.N, BKV, CAUSAL, false, head, kt)))
+    map_workgroup(blockIdx.x, p.n_tiles, p.nh, CAUSAL ? Order::kLongestFirst : Order::kHeadMajor, false, head, kt);
   const size_t base = (size_t)head * N * D;
   const size_t rbase = (size_t)head * N;
   const int head_bytes = N * D * 2;
@@ -443,8 +446,11 @@ __global__ __launch_bounds__(NW * 64, D > 128 ? 1 : 2) void bwd_dq_kernel(BwdPar
   // then tiles are dispatched longest-first.)
   const bool paired = CAUSAL && p.n_units != p.n_tiles;
   int head, unit;
-  map_workgroup(blockIdx.x, p.n_units, p.nh, paired ? Order::kHeadMajor : (CAUSAL ? Order::kLongestFirst : Order::kHeadMajor),
-                !paired, head, unit);
+  // (with sequence lengths the host leaves pairing off, and padding tiles run last)
+  if (!(MASKED && p.seqlens && !paired &&
+        map_workgroup_varlen(blockIdx.x, p.n_units, p.nh, p.heads, p.seqlens, p.N, BR, CAUSAL, true, head, unit)))
+    map_workgroup(blockIdx.x, p.n_units, p.nh, paired ? Order::kHeadMajor : (CAUSAL ? Order::kLongestFirst : Order::kHeadMajor),
+                  !paired, head, unit);
   const int n_items = (paired && p.n_tiles - 1 - unit != unit) ? 2 : 1;
   const int Lb = valid_rows<MASKED>(p, head);  // rows >= Lb of every input read as zero
 #pragma unroll 1
@@ -794,8 +800,11 @@ hipError_t dkdv_d(BwdParams<E> prm, hipStream_t stream) {
 template <typename E, int D, bool CAUSAL, bool MASKED = false, bool DROPOUT = false>
 hipError_t dq_d(BwdParams<E> prm, hipStream_t stream) {
   prm.n_tiles = (prm.N + 32 * kDqNW - 1) / (32 * kDqNW);
-  // Pair causal tiles when there are at least four workgroups per CU to begin with.
-  prm.n_units = (CAUSAL && (long)prm.n_tiles * prm.nh >= 4L * device_cu_count()) ? (prm.n_tiles + 1) / 2 : prm.n_tiles;
+  // Pair causal tiles when there are at least four workgroups per CU to begin with, except where
+  // the kernel orders tiles by sequence length instead (map_workgroup_varlen's conditions).
+  const bool by_length = MASKED && prm.seqlens && prm.heads % 8 == 0 && prm.nh / prm.heads <= 64;
+  prm.n_units = (CAUSAL && !by_length && (long)prm.n_tiles * prm.nh >= 4L * device_cu_count()) ? (prm.n_tiles + 1) / 2
+                                                                                              : prm.n_tiles;
   hipLaunchKernelGGL((bwd_dq_kernel<E, D, dq_bc<D>(), kDqNW, CAUSAL, MASKED, DROPOUT>), dim3(prm.n_units * prm.nh),
                      dim3(kDqNW * 64), 0, stream, prm);
   return hipGetLastError();

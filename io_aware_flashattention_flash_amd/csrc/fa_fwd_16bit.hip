@@ -163,7 +163,7 @@ __global__ __launch_bounds__(NW * 64, D > 128 ? 1 : 2) void fwd16_kernel(Fwd16Pa
   // the padding tiles' zero rows are then written by the head's tiles with work, spread over the
   // launch, and the padding workgroups themselves exit at once.
   const bool vmapped = MASKED && p.seqlens &&
-                       map_workgroup_varlen(blockIdx.x, p.n_qt, p.nh, p.heads, p.seqlens, p.N, BR, CAUSAL, head, qt);
+                       map_workgroup_varlen(blockIdx.x, p.n_qt, p.nh, p.heads, p.seqlens, p.N, BR, CAUSAL, true, head, qt);
   if (!vmapped)
     map_workgroup(blockIdx.x, p.n_qt, p.nh, CAUSAL ? Order::kLongestFirst : Order::kHeadMajor, true, head, qt);
   // Valid query rows Lq and keys Lk of this head's sequence.

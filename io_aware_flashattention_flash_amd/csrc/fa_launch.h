@@ -130,13 +130,15 @@ __device__ __forceinline__ void map_workgroup(int wg, int n_tiles, int nh, Order
 // tiles, which finish at once, with long ones; the hardware dispatches a launch's workgroups in
 // order and lets CUs idle behind such a mix (measured: a quarter of the slots on a length mix of
 // [N/4, N]). Here every XCD takes the same heads as in map_workgroup (head = xcd + 8 t), runs all
-// its tiles with work first, in the same order (longest-first: by tile index, descending, over its
-// heads; head-major: tiles of one head after another), and then all its padding tiles.
+// its tiles with work first, in the same order (longest-first: by tile index over its heads,
+// descending when tile n_tiles-1 carries the most work, ascending when tile 0 does; head-major:
+// tiles of one head after another), and then all its padding tiles.
 // Applies when heads % 8 == 0 and there are at most 64 sequences (lane b of the wave holds
 // sequence b's tile count); returns false otherwise, and the caller uses map_workgroup.
 // Wave-uniform; every wave of the workgroup computes the same result.
 __device__ __forceinline__ bool map_workgroup_varlen(int wg, int n_tiles, int nh, int heads, const int* seqlens,
-                                                     int N, int BR, bool longest_first, int& head, int& tile) {
+                                                     int N, int BR, bool longest_first, bool last_is_longest,
+                                                     int& head, int& tile) {
   const int nseq = nh / heads;
   if ((heads & 7) != 0 || nseq > 64) return false;
   const int lane = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0));
@@ -146,7 +148,8 @@ __device__ __forceinline__ bool map_workgroup_varlen(int wg, int n_tiles, int nh
   const int x = wg & 7, hp8 = heads >> 3;  // heads of each sequence on this XCD: b*heads + x + 8j, j < hp8
   int pos = wg >> 3;
   if (longest_first) {
-    for (int q = n_tiles - 1; q >= 0; --q) {
+    for (int i = 0; i < n_tiles; ++i) {
+      const int q = last_is_longest ? n_tiles - 1 - i : i;
       const uint64_t m = __builtin_amdgcn_ballot_w64(lane < nseq && t_lane > q);
       const int c = hp8 * __builtin_popcountll(m);
       if (pos < c) {

@@ -196,6 +196,45 @@ def test_bwd_block_sparse(N, density, padded, causal, d):
     _bwd_case(B, H, N, d, causal, [N - 37, N - 300] if padded else None, bmap, seed=N + d)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N,seqlens", [(300, [300, 1, 0, 129]), (700, [700, 455, 0, 64, 699])])
+def test_bwd_padded_eight_heads(N, seqlens, causal, d):
+    """Eight heads per sequence: dQ and dK/dV run their padding tiles after every tile with work
+    (gradients start as NaN, so a tile left unwritten fails)."""
+    _bwd_case(len(seqlens), 8, N, d, causal, seqlens, None, seed=N + d + 7)
+
+
+def test_bwd_padded_large_causal_launch():
+    """B8 H16 N1024 d64 causal with lengths: a launch that large pairs dQ's tiles when it has no
+    lengths; with them every tile runs on its own, padding tiles last. Every gradient is written
+    (NaN-filled beforehand, exact zeros for rows and keys that see nothing); three heads are
+    checked against the oracle."""
+    B, H, N, d = 8, 16, 1024, 64
+    seqlens = [int(v) for v in np.random.default_rng(8).integers(N // 4, N + 1, size=B)]
+    seqlens[3] = 0
+    x = _inputs(B, H, N, d, seed=81, with_do=True)
+    q, k, v, do = (dev(x[n], torch.bfloat16) for n in ("q", "k", "v", "do"))
+    sl = torch.tensor(seqlens, dtype=torch.int32, device=DEV)
+    scale = d ** -0.5
+    o, lse = flash_attn_fwd_masked(q, k, v, scale, True, seqlens=sl)
+    dq, dk, dv = (torch.full_like(q, float("nan")) for _ in range(3))
+    flash_attn_bwd_masked(do, q, k, v, o, lse, scale, True, seqlens=sl, dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    gq, gk, gv = host(dq), host(dk), host(dv)
+    assert np.isfinite(gq).all() and np.isfinite(gk).all() and np.isfinite(gv).all()
+    for b in range(B):  # padding rows and keys of every sequence are exactly zero
+        for g in (gq, gk, gv):
+            assert (g[b, :, seqlens[b]:] == 0).all()
+    for b, h in ((0, 0), (3, 5), (B - 1, H - 1)):
+        sl_ = (slice(b, b + 1), slice(h, h + 1))
+        vis = padded_batch_visible(1, 1, N, True, [seqlens[b]])
+        ref = attn_bwd_masked(x["q"][sl_], x["k"][sl_], x["v"][sl_], x["do"][sl_], scale, vis)
+        for name, g, r in (("dQ", gq, ref[0]), ("dK", gk, ref[1]), ("dV", gv, ref[2])):
+            e_inf, e_fro = grad_errors(g[sl_], r)
+            assert e_inf <= GRAD and e_fro <= GRAD, (name, b, h, e_inf, e_fro)
+
+
 def test_bwd_masked_fp16():
     bmap = _random_map(2, 2, 600, seed=3, density=0.6)
     _bwd_case(2, 2, 600, 128, True, [600, 333], bmap, seed=11, tdt=torch.float16, dtype="fp16")

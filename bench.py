@@ -547,14 +547,13 @@ def main():
     # ------------------------------------------------------------------ headline inputs
     # Everything the headline needs is built before the fp16 line runs, so the GPU goes from that
     # line straight into the headline. After an idle gap (host work) the GPU runs a few fast steps,
-    # then 10-17% slower ones for ~50 steps, then settles (measured on this step); the driver's
+    # then 10-17% slower ones for ~50 steps, then settles (measured on this step); a short run of
     # 5 warm-up + 20 timed steps would sit in that transient.
     w = inputs.WORKLOADS[HEADLINE]
     x = inputs.make_inputs(w)
     headline_step = prepare_fwdbwd(w, x, dev, to_dev)
 
     # ------------------------------------------------------------------ fp16 fwd+bwd extra line
-    # (the headline's shape on fp16 storage, timed over ~0.3 s right before the headline)
     # (the headline's shape on fp16 storage, about 0.3 s of steps, enqueued so that the headline's
     # warm-up steps follow it on the GPU without an idle gap)
     extras = {}

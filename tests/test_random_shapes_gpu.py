@@ -52,3 +52,107 @@ def test_random_shape_fwd_bwd(i, B, H, N, d, causal, dtype, scale):
         assert np.isfinite(g).all(), name
         e_inf, e_fro = grad_errors(g, r)
         assert e_inf <= GRAD and e_fro <= GRAD, (name, e_inf, e_fro)
+
+
+def _masked_configs(n=64, seed=77):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        d = int(rng.choice([32, 64, 96, 128, 256]))
+        B = int(rng.integers(1, 5))
+        H = int(rng.choice([1, 2, 8, 16]))  # 8 and 16: the length-ordered launch
+        N = int(rng.choice([1, 64, 129, 300, 513]))
+        causal = bool(rng.integers(0, 2))
+        dtype = str(rng.choice(["bf16", "fp16"]))
+        kind = str(rng.choice(["lengths", "map", "both"]))
+        out.append((i, B, H, N, d, causal, dtype, kind))
+    return out
+
+
+@pytest.mark.parametrize("i,B,H,N,d,causal,dtype,kind", _masked_configs())
+def test_random_masked_fwd_bwd(i, B, H, N, d, causal, dtype, kind):
+    """Padded lengths (0 and N included), block maps of random density, or both; forward and backward
+    against the masked oracle; rows and keys that see nothing give exact zeros (and LSE = -inf)."""
+    from io_aware_flashattention_flash_amd import flash_attn_bwd_masked, flash_attn_fwd_masked
+    from oracle import attn_bwd_masked, attn_fwd_masked, padded_batch_visible
+
+    rng = np.random.default_rng(5000 + i)
+    seqlens = bmap = None
+    if kind in ("lengths", "both"):
+        seqlens = [int(v) for v in rng.integers(0, N + 1, size=B)]
+        seqlens[0] = N
+    if kind in ("map", "both"):
+        nb = -(-N // 128)
+        bmap = (rng.random((B, H, nb, nb)) < rng.uniform(0.2, 0.9)).astype(np.uint8)
+    x = {n: inputs.random_tensor((B, H, N, d), 3000 + 10 * i + j, dtype) for j, n in enumerate(("q", "k", "v", "do"))}
+    q, k, v, do = (dev(x[n], TDT[dtype]) for n in ("q", "k", "v", "do"))
+    sl = None if seqlens is None else torch.tensor(seqlens, dtype=torch.int32, device=q.device)
+    bm = None if bmap is None else torch.from_numpy(bmap).to(q.device)
+    scale = d ** -0.5
+    o = torch.full_like(q, float("nan"))
+    lse = torch.full((B, H, N), float("nan"), device=q.device)
+    flash_attn_fwd_masked(q, k, v, scale, causal, seqlens=sl, block_mask=bm, out=o, lse=lse)
+    dq, dk, dv = (torch.full_like(q, float("nan")) for _ in range(3))
+    flash_attn_bwd_masked(do, q, k, v, o, lse, scale, causal, seqlens=sl, block_mask=bm, dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    vis = padded_batch_visible(B, H, N, causal, seqlens, bmap, 128)
+    O, L = attn_fwd_masked(x["q"], x["k"], x["v"], scale, vis)
+    ho, hl = host(o), host(lse)
+    full = np.isfinite(L)
+    assert np.isfinite(ho).all()
+    assert (ho[~full] == 0).all() and np.isneginf(hl[~full]).all()
+    if full.any():
+        assert beyond_rounding(ho[full], O[full]) <= BF16_O
+        assert np.abs(hl[full] - L[full]).max() <= BF16_LSE
+    dQ, dK, dV, _ = attn_bwd_masked(x["q"], x["k"], x["v"], x["do"], scale, vis)
+    rows_seen, keys_seen = vis.any(axis=-1), vis.any(axis=-2)
+    for name, g, r, live in (("dQ", dq, dQ, rows_seen), ("dK", dk, dK, keys_seen), ("dV", dv, dV, keys_seen)):
+        g = host(g)
+        assert np.isfinite(g).all(), name
+        assert (g[~live] == 0).all(), name
+        e_inf, e_fro = grad_errors(g, r)
+        assert e_inf <= GRAD and e_fro <= GRAD, (name, e_inf, e_fro)
+
+
+def _kv_configs(n=48, seed=91):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        d = int(rng.choice([32, 64, 96, 128, 256]))
+        B = int(rng.integers(1, 4))
+        H = int(rng.choice([1, 2, 8]))
+        Nk = int(rng.choice([1, 65, 500, 1000, 2049]))
+        Nq = int(min(Nk, rng.choice([1, 1, 2, 17, 64, 200])))
+        causal = bool(rng.integers(0, 2))
+        splits = int(rng.choice([0, 1, 2, 3, 7]))
+        lengths = bool(rng.integers(0, 2))
+        out.append((i, B, H, Nq, Nk, d, causal, splits, lengths))
+    return out
+
+
+@pytest.mark.parametrize("i,B,H,Nq,Nk,d,causal,splits,lengths", _kv_configs())
+def test_random_kvsplit(i, B, H, Nq, Nk, d, causal, splits, lengths):
+    """Key-split forward: Nq queries as the last positions of Nk keys (or of each sequence's cache
+    length), automatic or given split counts; rows that see no key give O = 0, LSE = -inf."""
+    from io_aware_flashattention_flash_amd import flash_attn_fwd_kvsplit
+    from oracle import attn_fwd_masked, kv_cache_visible
+
+    rng = np.random.default_rng(7000 + i)
+    lens = [int(v) for v in rng.integers(0, Nk + 1, size=B)] if lengths else None
+    x = {"q": inputs.random_tensor((B, H, Nq, d), 4000 + 10 * i, "bf16"),
+         "k": inputs.random_tensor((B, H, Nk, d), 4001 + 10 * i, "bf16"),
+         "v": inputs.random_tensor((B, H, Nk, d), 4002 + 10 * i, "bf16")}
+    q, k, v = (dev(x[n], torch.bfloat16) for n in ("q", "k", "v"))
+    o = torch.full_like(q, float("nan"))
+    lse = torch.full((B, H, Nq), float("nan"), device=q.device)
+    sl = None if lens is None else torch.tensor(lens, dtype=torch.int32, device=q.device)
+    flash_attn_fwd_kvsplit(q, k, v, d ** -0.5, causal, splits, out=o, lse=lse, seqlens_k=sl)
+    torch.cuda.synchronize()
+    O, L = attn_fwd_masked(x["q"], x["k"], x["v"], d ** -0.5, kv_cache_visible(B, H, Nq, Nk, causal, lens))
+    ho, hl = host(o), host(lse)
+    full = np.isfinite(L)
+    assert np.isfinite(ho).all()
+    assert (ho[~full] == 0).all() and np.isneginf(hl[~full]).all()
+    if full.any():
+        assert beyond_rounding(ho[full], O[full]) <= BF16_O
+        assert np.abs(hl[full] - L[full]).max() <= BF16_LSE

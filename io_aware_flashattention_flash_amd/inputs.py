@@ -117,3 +117,15 @@ def random_tensor(shape, seed: int, dtype: str = "bf16", mult: float = 1.0) -> n
     rng = np.random.default_rng(seed)
     t = (rng.standard_normal(shape) * mult).astype(np.float32)
     return round_to(t, dtype)
+
+
+GRID_STEP = 1.0 / 64.0
+
+
+def grid_codes(shape, seed: int) -> np.ndarray:
+    """Integer codes c, uniform on [-128, 128), as int8; the tensor's values are c * GRID_STEP,
+    uniform on [-2, 2) in steps of 1/64. Every such value is exact in bf16 and fp16 (at most 8
+    significant bits), so the codes can be widened on either side without rounding. One byte per
+    element and no float draws: cheap enough for tensors of ~2^31 elements (the size-limit tests),
+    where standard-normal draws would dominate the run."""
+    return np.random.default_rng(seed).integers(-128, 128, size=shape, dtype=np.int8)

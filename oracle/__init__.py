@@ -23,12 +23,13 @@ Every function cites the passage of the pages it follows. Parity pins (closed
 forms, invariants, brute force, library special cases, finite differences)
 live in tests/test_oracle.py, tests/test_oracle_masked.py and tests/test_oracle_dropout.py.
 """
-from .attention import attn_bwd, attn_fwd, attn_fwd_kv, attn_fwd_rows, softmax_rows
+from .attention import attn_bwd, attn_bwd_keys, attn_bwd_rows, attn_fwd, attn_fwd_kv, attn_fwd_rows, softmax_rows
 from .brute import brute_fwd
 from .dropout import attn_bwd_dropout, attn_fwd_dropout, keep_mask, keep_threshold, philox4x32_10, random_bytes
 from .masked import attn_bwd_masked, attn_fwd_masked, kv_cache_visible, padded_batch_visible
 from .online import online_fwd
 
-__all__ = ["attn_fwd", "attn_fwd_kv", "attn_fwd_rows", "attn_bwd", "softmax_rows", "brute_fwd", "online_fwd",
+__all__ = ["attn_fwd", "attn_fwd_kv", "attn_fwd_rows", "attn_bwd", "attn_bwd_rows", "attn_bwd_keys", "softmax_rows",
+           "brute_fwd", "online_fwd",
            "attn_fwd_masked", "attn_bwd_masked", "padded_batch_visible", "kv_cache_visible",
            "attn_fwd_dropout", "attn_bwd_dropout", "keep_mask", "keep_threshold", "philox4x32_10", "random_bytes"]

@@ -114,6 +114,47 @@ def attn_fwd_rows(q, k, v, scale: float, causal: bool, b: int, h: int, rows):
     return P @ vh, lse
 
 
+def attn_bwd_rows(q, k, v, do, scale: float, causal: bool, b: int, h: int, rows):
+    """dQ of the backward below restricted to some query rows of one (b, h): returns
+    (dQ_rows [len(rows), d], D_rows). Row i of dQ = scale * sum_j dS_ij K_j needs only row i's
+    probabilities, dP_ij = dO_i . V_j and D_i = sum_j P_ij dP_ij, all formed from its own query
+    and gradient row, so this is a sample of attn_bwd's dQ."""
+    rows = np.asarray(rows, dtype=np.int64)
+    kh, vh = _f64(k[b, h]), _f64(v[b, h])
+    S = _scores(_f64(q[b, h, rows]), kh, scale, causal, rows)
+    P, _, _, _ = softmax_rows(S)
+    dP = _f64(do[b, h, rows]) @ vh.T
+    Dr = np.sum(P * dP, axis=1)
+    dS = P * (dP - Dr[:, None])
+    return scale * (dS @ kh), Dr
+
+
+def attn_bwd_keys(q, k, v, do, scale: float, causal: bool, b: int, h: int, keys):
+    """dK and dV of the backward below restricted to some key rows of one (b, h): returns
+    (dK_keys, dV_keys), each [len(keys), d]. Column j of P and dS involves every query row that
+    sees key j, and each such row's softmax needs its whole row of scores, so every such row is
+    formed in full (in chunks) and only the selected columns are kept:
+    dV_j = sum_i P_ij dO_i, dK_j = scale * sum_i dS_ij Q_i. Under the causal mask only rows
+    i >= min(keys) see any selected key, so the cost falls with the keys' position."""
+    keys = np.asarray(keys, dtype=np.int64)
+    qh, kh, vh, doh = _f64(q[b, h]), _f64(k[b, h]), _f64(v[b, h]), _f64(do[b, h])
+    N, d = qh.shape
+    dK = np.zeros((len(keys), d))
+    dV = np.zeros((len(keys), d))
+    r_first = int(keys.min()) if causal else 0
+    for r0 in range(r_first, N, _ROW_CHUNK):
+        rows = np.arange(r0, min(N, r0 + _ROW_CHUNK))
+        S = _scores(qh[rows], kh, scale, causal, rows)
+        P, _, _, _ = softmax_rows(S)
+        dP = doh[rows] @ vh.T
+        Dr = np.sum(P * dP, axis=1)
+        Pk = P[:, keys]
+        dSk = Pk * (dP[:, keys] - Dr[:, None])
+        dV += Pk.T @ doh[rows]
+        dK += scale * (dSk.T @ qh[rows])
+    return dK, dV
+
+
 def attn_bwd(q, k, v, do, scale: float, causal: bool):
     """Analytic backward of O = softmax(scale*Q K^T + mask) V for the loss sum(O * dO).
 

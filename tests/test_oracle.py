@@ -7,7 +7,7 @@ import numpy as np
 import pytest
 
 import oracle
-from oracle import attn_bwd, attn_fwd, attn_fwd_rows, online_fwd
+from oracle import attn_bwd, attn_bwd_keys, attn_bwd_rows, attn_fwd, attn_fwd_rows, online_fwd
 from io_aware_flashattention_flash_amd import inputs
 from tests import oracle_pins as pins
 
@@ -48,6 +48,25 @@ def test_row_sampler_is_a_slice_of_the_full_forward():
         Or, Lr = attn_fwd_rows(q, k, v, 0.3, causal, 1, 1, rows)
         np.testing.assert_array_equal(Or, O[1, 1, rows])
         np.testing.assert_array_equal(Lr, L[1, 1, rows])
+
+
+def test_backward_samplers_are_slices_of_the_full_backward(monkeypatch):
+    """dQ of some query rows and dK, dV of some keys equal the same rows of the full backward
+    (which its own pins tie to autograd, brute force and finite differences), with the key
+    sampler's row chunks smaller than the sequence so chunk boundaries are crossed."""
+    rng = np.random.default_rng(74)
+    q, k, v, do = (rng.standard_normal((2, 2, 37, 8)) for _ in range(4))
+    monkeypatch.setattr(oracle.attention, "_ROW_CHUNK", 5)
+    for causal in (False, True):
+        dQ, dK, dV, D = attn_bwd(q, k, v, do, 0.3, causal)
+        rows = [0, 5, 17, 36]
+        dQr, Dr = attn_bwd_rows(q, k, v, do, 0.3, causal, 1, 0, rows)
+        np.testing.assert_allclose(dQr, dQ[1, 0, rows], rtol=0, atol=1e-13)
+        np.testing.assert_allclose(Dr, D[1, 0, rows], rtol=0, atol=1e-13)
+        for keys in ([0, 1, 36], [20, 33, 35, 36], [36]):
+            dKk, dVk = attn_bwd_keys(q, k, v, do, 0.3, causal, 0, 1, keys)
+            np.testing.assert_allclose(dKk, dK[0, 1, keys], rtol=0, atol=1e-13)
+            np.testing.assert_allclose(dVk, dV[0, 1, keys], rtol=0, atol=1e-13)
 
 
 def test_row_chunking_does_not_change_results(monkeypatch):
@@ -177,3 +196,14 @@ def test_kv_oracle_equal_keys_give_the_mean_of_values():
         O, L = attn_fwd_kv(q, k, v, 1.3, causal)
         np.testing.assert_allclose(O[0, 0, 0], v[0, 0].mean(axis=0), atol=1e-13)
         np.testing.assert_allclose(L[0, 0, 0], 1.3 * float(q[0, 0, 0] @ k[0, 0, 0]) + math.log(Nk), atol=1e-13)
+
+
+def test_grid_codes_widen_exactly_to_16_bit():
+    """The size-limit tests' inputs: codes / 64 are exact in bf16 and fp16, and cover the grid."""
+    import torch
+    c = inputs.grid_codes((4096,), 5)
+    assert c.dtype == np.int8 and c.min() == -128 and c.max() == 127
+    v = c.astype(np.float64) * inputs.GRID_STEP
+    for dt in (torch.bfloat16, torch.float16):
+        t = torch.from_numpy(c).to(dt).mul_(inputs.GRID_STEP)
+        np.testing.assert_array_equal(t.double().numpy(), v)

@@ -40,11 +40,13 @@ def _f64(x):
     return np.asarray(x, dtype=np.float64)
 
 
-def padded_batch_visible(B, H, N, causal, seqlens=None, block_mask=None, block=BLOCK):
-    """visible[b, h, i, j] for a padded batch of square problems (see the module readings)."""
-    i = np.arange(N)[:, None]
+def padded_batch_visible(B, H, N, causal, seqlens=None, block_mask=None, block=BLOCK, rows=None):
+    """visible[b, h, i, j] for a padded batch of square problems (see the module readings).
+    With `rows`, only those query rows i (visible[b, h, r, j] for the r-th entry of rows); every
+    row's visibility depends on its own index alone, so this is a slice of the full array."""
+    i = (np.arange(N) if rows is None else np.asarray(rows, dtype=np.int64))[:, None]
     j = np.arange(N)[None, :]
-    vis = np.ones((B, H, N, N), dtype=bool)
+    vis = np.ones((B, H, i.shape[0], N), dtype=bool)
     if causal:
         vis &= (j <= i)[None, None]
     if seqlens is not None:

@@ -316,3 +316,55 @@ def test_autograd_wrapper_routes_masks_and_dropout():
     assert torch.equal(out.detach(), o)
     for g, r in zip((qa.grad, ka.grad, va.grad), ref):
         assert torch.equal(g, r)
+
+
+def test_block_map_at_capacity():
+    """N = 131072: 1024 key blocks per map row, the most a map may hold. Causal, one full-length and
+    one shorter sequence, a random map (30% of blocks) in which one head's last query tile has
+    all 1024 blocks enabled and another head has an empty map row. The full N x N oracle is out of
+    reach on the host, so it runs on sampled rows alone: O, LSE and dQ of query rows at the start,
+    in the empty map row, around the shorter sequence's end and at the end; dK and dV of each
+    sequence's last block of keys (and the padding keys after it), which under the causal mask only
+    that sequence's last query block sees, so the oracle on those rows gives them exactly. Every
+    output element must come back finite (they start as NaN)."""
+    B, H, N, d = 2, 2, 131072, 64
+    seqlens = [N, 100000]
+    print(f"block map at capacity: B{B} H{H} N{N} d{d}, lengths {seqlens}", flush=True)
+    bmap = _random_map(B, H, N, 950, 0.3)
+    assert bmap.shape[-1] == 1024
+    bmap[0, 0, -1, :] = 1  # head (0, 0): the last query tile walks every block
+    bmap[0, 1, 5, :] = 0   # head (0, 1): rows 640..767 see no key
+    x = _inputs(B, H, N, d, seed=951, with_do=True)
+    scale = d ** -0.5
+    o, lse = _fwd(x, scale, True, seqlens, bmap)
+    q, k, v, do = (dev(x[n], torch.bfloat16) for n in ("q", "k", "v", "do"))
+    sl = torch.tensor(seqlens, dtype=torch.int32, device=DEV)
+    bm = torch.from_numpy(bmap).to(DEV)
+    dq, dk, dv = (torch.full_like(q, float("nan")) for _ in range(3))
+    flash_attn_bwd_masked(do, q, k, v, o, lse, scale, True, seqlens=sl, block_mask=bm, dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    for name, t in (("dQ", dq), ("dK", dk), ("dV", dv)):
+        assert bool(torch.isfinite(t).all()), name
+    rows = [0, 1, 127, 128, 640, 700, 767, 50000, 99967, 99968, 99999, 100000, 100001, N - 129, N - 128, N - 1]
+    vis = padded_batch_visible(B, H, N, True, seqlens, bmap, rows=rows)
+    O, L = attn_fwd_masked(x["q"][:, :, rows], x["k"], x["v"], scale, vis)
+    _check_fwd(o[:, :, rows], lse[:, :, rows], O, L, beyond_output_rounding=True)
+    dQ = attn_bwd_masked(x["q"][:, :, rows], x["k"], x["v"], x["do"][:, :, rows], scale, vis)[0]
+    g = host(dq[:, :, rows])
+    seen = vis.any(axis=-1)
+    assert (g[~seen] == 0).all()
+    e_inf, e_fro = grad_errors(g, dQ)
+    print(f"dQ rows: {e_inf:.2e} / {e_fro:.2e}")
+    assert e_inf <= GRAD and e_fro <= GRAD
+    for b, Lb in enumerate(seqlens):
+        r0 = (Lb - 1) // BLK * BLK  # the last query block with valid rows; it alone sees keys >= r0
+        R = np.arange(r0, Lb)
+        vr = padded_batch_visible(B, H, N, True, seqlens, bmap, rows=R)
+        _, dK, dV, _ = attn_bwd_masked(x["q"][:, :, R], x["k"], x["v"], x["do"][:, :, R], scale, vr)
+        for name, t, ref in (("dK", dk, dK), ("dV", dv, dV)):
+            gk = host(t[b, :, r0:])
+            rk = ref[b, :, r0:]
+            assert (gk[:, Lb - r0:] == 0).all(), (b, name)  # padding keys
+            e_inf, e_fro = grad_errors(gk, rk)
+            print(f"sequence {b} {name}, keys {r0}..{N - 1}: {e_inf:.2e} / {e_fro:.2e}")
+            assert e_inf <= GRAD and e_fro <= GRAD, (b, name)

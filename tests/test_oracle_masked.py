@@ -182,6 +182,29 @@ def test_kv_cache_pin():
     pin_kv_cache_lengths(om.kv_cache_visible, om.attn_fwd_masked)
 
 
+def test_row_restricted_visibility_is_a_slice():
+    """The builder's `rows` option (used where the full N x N array is too large) returns exactly
+    those rows of the full array, and the masked forward and dQ of those rows alone equal the
+    full results' rows."""
+    B, H, N, d = 2, 2, 300, 8
+    q, k, v = _qkv(B, H, N, d, 80)
+    do = RNG(81).standard_normal((B, H, N, d))
+    bm = _random_block_mask(B, H, 3, 82, 0.6)
+    rows = [0, 1, 127, 128, 200, 255, 256, 299]
+    for causal in (False, True):
+        for seqlens, bmap in ((None, None), ([300, 130], None), (None, bm), ([255, 299], bm)):
+            full = om.padded_batch_visible(B, H, N, causal, seqlens, bmap)
+            part = om.padded_batch_visible(B, H, N, causal, seqlens, bmap, rows=rows)
+            np.testing.assert_array_equal(part, full[:, :, rows])
+            O, L = om.attn_fwd_masked(q, k, v, 0.4, full)
+            Or, Lr = om.attn_fwd_masked(q[:, :, rows], k, v, 0.4, part)
+            np.testing.assert_allclose(Or, O[:, :, rows], rtol=0, atol=1e-13)  # BLAS order only
+            np.testing.assert_allclose(Lr, L[:, :, rows], rtol=0, atol=1e-13)
+            dQ = om.attn_bwd_masked(q, k, v, do, 0.4, full)[0]
+            dQr = om.attn_bwd_masked(q[:, :, rows], k, v, do[:, :, rows], 0.4, part)[0]
+            np.testing.assert_allclose(dQr, dQ[:, :, rows], rtol=0, atol=1e-13)
+
+
 # ---------------------------------------------------------------------------------------------
 # backward
 # ---------------------------------------------------------------------------------------------

@@ -52,6 +52,9 @@ def parse():
     ap.add_argument("--workload", default=None,
                     help="time only this workload (any name in inputs.WORKLOADS) and print its own JSON line; "
                          "used to profile one kernel at a time")
+    ap.add_argument("--decode", action="store_true",
+                    help="time only the key-split decoding line (B8 H32, 1 query x 8192 keys, d128) for --steps "
+                         "calls and print its JSON line; used to profile the HBM-bound kernel")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run --steps plain device copies of 256 MiB (reference for the HBM byte counters)")
     return ap.parse_args()
@@ -527,6 +530,9 @@ def main():
         print(json.dumps({"copy_bytes_per_launch": nbytes, "launches": max(1, args.steps)}))
         return
 
+    if args.decode:
+        print(json.dumps(time_decode(8, 32, 8192, 128, args.steps, dev)))
+        return
     if args.workload is not None and args.workload != HEADLINE:
         print(json.dumps(time_forward(args.workload, args.steps, args.warmup, dev, to_dev)))
         return

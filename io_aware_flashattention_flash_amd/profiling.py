@@ -33,9 +33,28 @@ from collections import defaultdict
 
 CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
 KERNEL_SOURCES = {"fwd": "fa_fwd_16bit.hip", "fwd_fp32": "fa_fwd_fp32.hip", "bwd_dq": "fa_bwd_16bit.hip",
-                  "bwd_dkdv": "fa_bwd_16bit.hip"}
+                  "bwd_dkdv": "fa_bwd_16bit.hip", "fwd_kvsplit": "fa_fwd_16bit.hip",
+                  "kvsplit_merge": "fa_fwd_16bit.hip"}
 KERNEL_PREFIX = {"fwd": ("fa::fwd16_kernel",), "fwd_fp32": ("fa::fwd_fp32_kernel", "fa::fwd_fp32_split_kernel"),
-                 "bwd_dq": ("fa::bwd_dq_kernel",), "bwd_dkdv": ("fa::bwd_dkdv_kernel",)}
+                 "bwd_dq": ("fa::bwd_dq_kernel",), "bwd_dkdv": ("fa::bwd_dkdv_kernel",),
+                 "kvsplit_merge": ("fa::kvsplit_merge_kernel",)}
+KSPLIT_MODE = 1  # the forward kernel's last template argument in key-split launches
+
+
+class Decode:
+    """A key-split forward workload (Nq queries against Nk keys), as bench.py --decode times it."""
+
+    def __init__(self, B, H, Nq, Nk, d):
+        self.B, self.H, self.Nq, self.Nk, self.d = B, H, Nq, Nk, d
+
+
+DECODE = {"decode_bf16_b8h32nq1nk8192d128": Decode(8, 32, 1, 8192, 128)}
+
+
+def workload(name: str):
+    from . import inputs
+
+    return DECODE[name] if name in DECODE else inputs.WORKLOADS[name]
 
 
 def source_digest(kernel: str) -> str:
@@ -75,6 +94,8 @@ def readable_name(name: str) -> str:
 
 def kernel_key(name: str):
     short = readable_name(name)
+    if short.startswith("fa::fwd16_kernel<") and short.endswith(f", {KSPLIT_MODE}>"):
+        return "fwd_kvsplit"
     for key, prefixes in KERNEL_PREFIX.items():
         if any(short.startswith(prefix + "<") for prefix in prefixes):
             return key
@@ -84,7 +105,11 @@ def kernel_key(name: str):
 def algorithmic_bytes(w, kernel: str):
     """(read, write) bytes of one launch of `kernel` on workload w when every tensor crosses HBM once:
     forward reads Q, K, V and writes O and LSE; dQ reads Q, K, V, O, dO, LSE and writes dQ and delta;
-    dK/dV reads Q, K, V, dO, LSE, delta and writes dK, dV."""
+    dK/dV reads Q, K, V, dO, LSE, delta and writes dK, dV. A key-split forward reads Q, K and V (its
+    fp32 partials are scratch, not counted) and its merge writes O and LSE."""
+    if isinstance(w, Decode):
+        return {"fwd_kvsplit": (w.B * w.H * (w.Nq + 2 * w.Nk) * w.d * 2, 0),
+                "kvsplit_merge": (0, w.B * w.H * w.Nq * (w.d * 2 + 4))}[kernel]
     s = 4 if w.dtype == "fp32" else 2
     t, r = w.B * w.H * w.N * w.d * s, w.B * w.H * w.N * 4
     return {"fwd": (3 * t, t + r), "fwd_fp32": (3 * t, t + r), "bwd_dq": (5 * t + r, t + r),
@@ -132,9 +157,16 @@ def counter_per_dispatch(directory: str, counter: str, match) -> dict:
     return {k: total[k] / len(dispatches[k]) for k in total}
 
 
-def _bench_line(bench_json: str) -> str:
+def _bench_json(bench_json: str) -> dict:
     with open(bench_json) as f:
-        d = json.loads(f.read().strip().splitlines()[-1])
+        return json.loads(f.read().strip().splitlines()[-1])
+
+
+def _bench_line(bench_json: str) -> str:
+    d = _bench_json(bench_json)
+    if "roofline" not in d:  # a single timed line (bench.py --decode)
+        return (f"{d['workload']}: {d['us']} µs per call ({d['reps']} calls back to back between two events), "
+                f"{d['gbps_algorithmic']} GB/s algorithmic = {d['pct_of_hbm_peak']}% of the 8 TB/s HBM peak.")
     r = d["roofline"]
     kern = ", ".join(f"{n} {k['avg_us']:.2f} µs" for n, k in d["kernels"].items())
     return (f"value {d['value']} {d['unit']}, {d['ms_per_step']} ms per step; per-kernel event averages "
@@ -146,10 +178,15 @@ def bench_line_section(bench_json: str, plain_json: str = None) -> list:
     """The bench line printed by the traced run itself and, if given, that of the same command run
     without the profiler just before on the same box: throughput, per-kernel event averages and
     roofline fraction, for comparison with the trace's durations."""
-    lines = ["", "## The traced run's bench line", "", _bench_line(bench_json), "",
-             "An event pair around one kernel also spans that launch's dispatch gap after the previous kernel, "
-             "which the profiler lengthens (it adds work to every dispatch); the trace's durations are the kernels' "
-             "own. The trace's averages of the headline's kernel instances also include its warm-up steps."]
+    lines = ["", "## The traced run's bench line", "", _bench_line(bench_json)]
+    if "roofline" in _bench_json(bench_json):
+        lines += ["", "An event pair around one kernel also spans that launch's dispatch gap after the previous "
+                  "kernel, which the profiler lengthens (it adds work to every dispatch); the trace's durations are "
+                  "the kernels' own. The trace's averages of the headline's kernel instances also include its "
+                  "warm-up steps."]
+    else:
+        lines += ["", "The events span both launches of each call (key-split forward and merge) and the gaps "
+                  "between them, which the profiler lengthens."]
     if plain_json:
         lines += ["", "## The same command without the profiler (same box, just before)", "", _bench_line(plain_json)]
     return lines
@@ -175,8 +212,6 @@ def trace(stats_csv: str, out_md: str, command: str, title: str, bench_json: str
 
 
 def traffic(a) -> dict:
-    from . import inputs
-
     # the runtime's device-to-device blit kernel that a same-device torch copy launches
     copy = lambda n: "copy" if "copybuffer" in n.lower() else None
     cf = counter_per_dispatch(a.copy_fetch, "FETCH_SIZE", copy).get("copy")
@@ -200,7 +235,7 @@ def traffic(a) -> dict:
              "| workload | kernel | fetch MB | write MB | algorithmic read / write MB | fetch / algorithmic read | "
              "avg µs | counter GB/s | algorithmic GB/s |", "|---|---|---|---|---|---|---|---|---|"]
     for wname, fdir, wdir, stats in a.run:
-        w = inputs.WORKLOADS[wname]
+        w = workload(wname)
         fetch = counter_per_dispatch(fdir, "FETCH_SIZE", kernel_key)
         write = counter_per_dispatch(wdir, "WRITE_SIZE", kernel_key)
         # the trace's averages over the same kernel instances the counter pass ran
@@ -212,14 +247,15 @@ def traffic(a) -> dict:
             e = {"source_digest": source_digest(k), "fetch_bytes_per_launch": round(fb),
                  "write_bytes_per_launch": round(wb), "bytes_per_launch": round(fb + wb),
                  "algorithmic_read_bytes": ar, "algorithmic_write_bytes": aw,
-                 "fetch_over_algorithmic_read": round(fb / ar, 3)}
+                 "fetch_over_algorithmic_read": round(fb / ar, 3) if ar else None}
             us = avg.get(k)
             if us:
                 e.update({"avg_us": round(us, 2), "counter_gbps": round((fb + wb) / (us * 1e-6) / 1e9, 1),
                           "algorithmic_gbps": round((ar + aw) / (us * 1e-6) / 1e9, 1)})
             entry[k] = e
+            ratio = f"{fb / ar:.2f}" if ar else "–"
             lines.append(f"| {wname} | {k} | {fb / 1e6:.2f} | {wb / 1e6:.2f} | {ar / 1e6:.2f} / {aw / 1e6:.2f} | "
-                         f"{fb / ar:.2f} | {e.get('avg_us', '–')} | {e.get('counter_gbps', '–')} | "
+                         f"{ratio} | {e.get('avg_us', '–')} | {e.get('counter_gbps', '–')} | "
                          f"{e.get('algorithmic_gbps', '–')} |")
         out["workloads"][wname] = entry
     with open(a.out_json, "w") as f:

@@ -92,6 +92,10 @@ struct Fwd16Params {
   // Key-split launches only: nonzero when each head has a single query tile, so every K/V tile is
   // read by exactly one workgroup; its loads then carry the non-temporal cache hint.
   int kv_once;
+  // Key-split launches only: nonzero when there is a single split (and split_direct_ok(D)). Its
+  // workgroups then write the final O and LSE themselves (what the merge would produce with one
+  // split: weight exactly 1), and no partials are written or merged.
+  int kv_direct;
   // Per-sequence lengths (sequence = head / heads), or null: kMasked, the valid rows of Q and K/V;
   // kSplit, the valid keys of the cache. Values are clamped to [0, N] (kSplit: [0, Nk]).
   const int* seqlens;
@@ -114,6 +118,10 @@ struct Fwd16Params {
 template <typename E>
 constexpr float kOverflowSum = std::is_same<E, f16>::value ? 32768.0f : 65536.0f;
 constexpr float kInitMax = -1e30f;
+
+// Head dims whose key-split kernel writes O and LSE itself when there is one split. At d = 256 the
+// second epilogue costs registers the kernel does not have (it would spill), so it keeps the merge.
+__host__ __device__ constexpr bool split_direct_ok(int d) { return d <= 128; }
 
 // buf_load16_to_lds with the non-temporal cache policy (bit 1 of the cache-policy operand, "nt"):
 // for data that no other workgroup reads again.
@@ -236,6 +244,10 @@ __global__ __launch_bounds__(NW * 64, D > 128 ? 1 : 2) void fwd16_kernel(Fwd16Pa
     jb = blockIdx.y * p.tiles_per_split;
     je = min(n_kv, jb + p.tiles_per_split);
     if (jb >= je) {  // no visible key in this split: empty partials (uniform over the workgroup)
+      if (split_direct_ok(D) && p.kv_direct) {
+        write_empty_rows();
+        return;
+      }
       if (q < N) {
         const size_t row = ((size_t)blockIdx.y * p.nh + head) * N + q;
         if (hf == 0) p.lsepart[row] = -INFINITY;
@@ -559,7 +571,7 @@ __global__ __launch_bounds__(NW * 64, D > 128 ? 1 : 2) void fwd16_kernel(Fwd16Pa
   // by 16 bytes) and written back as whole rows of 16-byte chunks. Rows >= N fall outside the
   // buffer descriptors and are dropped.
   const float l_tot = half_swap_sum(l_run);
-  if (KV_SPLIT) {
+  if (KV_SPLIT && !(split_direct_ok(D) && p.kv_direct)) {
     // fp32 partial: O_s = O_acc / l~ and LSE_s; a row with no visible key in this split (l~ = 0)
     // gets O_s = 0, LSE_s = -inf, so the merge gives it no weight. Lane (q, hf) holds columns
     // 32*db + 8*g + 4*hf .. +3 of row q.
@@ -585,8 +597,9 @@ __global__ __launch_bounds__(NW * 64, D > 128 ? 1 : 2) void fwd16_kernel(Fwd16Pa
   }
   float inv = 1.0f / half_swap_sum(lr_run);
   float lse_row = (m_run + __log2f(l_tot)) * kLn2;
-  if (MASKED) {
+  if (MASKED || KV_SPLIT) {
     // padding rows, and rows whose visible keys all fell in disabled blocks or the causal mask
+    // (key-split: a cache shorter than the row's position)
     const bool empty = q >= Lq || half_swap_sum(lr_run) == 0.f;
     if (DROPOUT) inv *= p.drop_scale;
     inv = empty ? 0.f : inv;
@@ -650,6 +663,7 @@ static hipError_t launch_typed(const void* q, const void* k, const void* v, void
   // Measured on decoding and chunked-prefill shapes (d = 128, 8192 keys): one query tile per head
   // gains 11-15% from non-temporal K/V loads, two to four are neutral, eight or more lose 3-15%.
   prm.kv_once = MODE == kSplit && prm.n_qt == 1;
+  prm.kv_direct = MODE == kSplit && x.n_splits == 1 && split_direct_ok(d);
   prm.seqlens = x.masks.seqlens;
   prm.block_mask = x.masks.block_mask;
   prm.heads = x.masks.heads;
@@ -734,7 +748,7 @@ template <typename E>
 static hipError_t launch_split_typed(const void* q, const void* k, const void* v, void* o, float* lse, int BH, int N,
                                      int d, float scale, bool causal, const FwdExtra& x, hipStream_t stream) {
   hipError_t e = launch_typed<E, kSplit>(q, k, v, o, lse, BH, N, d, scale, causal, x, stream);
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || (x.n_splits == 1 && split_direct_ok(d))) return e;  // one split writes O and LSE itself
   const int n_splits = x.n_splits;
   float* opart = x.opart;
   float* lsepart = x.lsepart;

@@ -150,7 +150,9 @@ fa_status_t flash_attn_dropout_mask(uint8_t* keep, int B, int H, int Nq, int Nk,
  * the rule the online softmax uses for consecutive blocks (52jiny.com
  * FlashAttention explainer, "key ideas" part 2; codechina.net article,
  * section 4.2): LSE = ln sum_s exp(LSE_s), O = sum_s exp(LSE_s - LSE) O_s.
- * O and LSE equal those of the plain softmax over all Nk keys.
+ * O and LSE equal those of the plain softmax over all Nk keys. When the launch has a
+ * single split (d <= 128) its workgroups write O and LSE directly, which is what the
+ * merge would produce with one split; the workspace is then left untouched.
  * workspace: device scratch of at least flash_attn_fwd_kvsplit_workspace_size()
  * bytes for the same shape and num_splits (16-byte aligned); its contents on
  * entry are ignored. Deterministic.

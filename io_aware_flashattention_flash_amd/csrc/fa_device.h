@@ -117,8 +117,11 @@ __device__ __forceinline__ void philox4x32_10(uint32_t c0, uint32_t c1, uint32_t
   for (int r = 0; r < 10; ++r) {
     const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
     const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
-    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
-    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    // Three-way xor. In the first two rounds parts of the counter may still be wave-uniform, and
+    // the compiler folds those into scalar instructions; later rounds use one v_bitop3 (truth
+    // table 0x96 = a ^ b ^ c) in place of two vector xors.
+    const uint32_t n0 = r < 2 ? (uint32_t)(p1 >> 32) ^ c1 ^ k0 : __builtin_amdgcn_bitop3_b32((uint32_t)(p1 >> 32), c1, k0, 0x96);
+    const uint32_t n2 = r < 2 ? (uint32_t)(p0 >> 32) ^ c3 ^ k1 : __builtin_amdgcn_bitop3_b32((uint32_t)(p0 >> 32), c3, k1, 0x96);
     c1 = (uint32_t)p1;
     c3 = (uint32_t)p0;
     c0 = n0;

@@ -281,7 +281,10 @@ def test_masked_deterministic():
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("Nq,Nk,lens,splits", [(1, 4097, [4097, 1, 0, 2000], 0), (1, 1000, [999, 64, 65, 500], 3),
-                                               (200, 1000, [1000, 150, 200, 901], 0), (64, 640, [640, 0, 10, 300], 4)])
+                                               (200, 1000, [1000, 150, 200, 901], 0), (64, 640, [640, 0, 10, 300], 4),
+                                               # one split: the workgroups write O and LSE themselves (no merge),
+                                               # including rows before a short cache's first key and an empty cache
+                                               (200, 1000, [1000, 150, 0, 901], 1), (1, 700, [700, 0, 1, 333], 1)])
 def test_kvsplit_cache_lengths(Nq, Nk, lens, splits, causal, d):
     B, H = len(lens), 2
     x = {"q": inputs.random_tensor((B, H, Nq, d), Nq + d, "bf16"),
@@ -295,6 +298,24 @@ def test_kvsplit_cache_lengths(Nq, Nk, lens, splits, causal, d):
     torch.cuda.synchronize()
     O, L = attn_fwd_masked(x["q"], x["k"], x["v"], d ** -0.5, kv_cache_visible(B, H, Nq, Nk, causal, lens))
     _check_fwd(o, lse, O, L)
+
+
+@pytest.mark.parametrize("d", [32, 96, 256])
+def test_kvsplit_single_split_head_dims(d):
+    """One split at every other head dim (d = 256 keeps the merge kernel; the others write O and LSE
+    in the split kernel), causal, with cache lengths that leave some rows and one sequence empty."""
+    B, H, Nq, Nk, lens = 3, 2, 130, 777, [777, 100, 0]
+    x = {"q": inputs.random_tensor((B, H, Nq, d), 50 + d, "bf16"),
+         "k": inputs.random_tensor((B, H, Nk, d), 51 + d, "bf16"),
+         "v": inputs.random_tensor((B, H, Nk, d), 52 + d, "bf16")}
+    q, k, v = (dev(x[n], torch.bfloat16) for n in ("q", "k", "v"))
+    o = torch.full_like(q, float("nan"))
+    lse = torch.full(q.shape[:3], float("nan"), device=DEV)
+    sl = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    o, lse = flash_attn_fwd_kvsplit(q, k, v, d ** -0.5, True, 1, out=o, lse=lse, seqlens_k=sl)
+    torch.cuda.synchronize()
+    O, L = attn_fwd_masked(x["q"], x["k"], x["v"], d ** -0.5, kv_cache_visible(B, H, Nq, Nk, True, lens))
+    _check_fwd(o, lse, O, L, beyond_output_rounding=True)
 
 
 def test_autograd_wrapper_routes_masks_and_dropout():

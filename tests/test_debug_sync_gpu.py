@@ -103,7 +103,11 @@ def test_masked_dropout_and_keysplit_match_the_race_guard_build(debug_lib):
         g = fa.flash_attn_bwd_masked(do, q, k, v, o, lse, None, True, seqlens=lens, block_mask=bmap,
                                      dropout_p=0.2, seed=9)
         o2, lse2 = fa.flash_attn_fwd_kvsplit(q[:, :, -3:].contiguous(), k, v, None, True, 0)
-        return (o, lse, *g, o2, lse2)
+        # one split: the split kernel writes O and LSE itself (with a single query tile per head its
+        # K/V loads also carry the non-temporal hint)
+        o3, lse3 = fa.flash_attn_fwd_kvsplit(q[:, :, -3:].contiguous(), k, v, None, True, 1)
+        o4, lse4 = fa.flash_attn_fwd_kvsplit(q[:, :, -300:].contiguous(), k, v, None, True, 1, seqlens_k=lens)
+        return (o, lse, *g, o2, lse2, o3, lse3, o4, lse4)
 
     a, b = both(debug_lib, run)
     assert_bitwise(a, b)

@@ -334,6 +334,46 @@ def counters_md(runs: list, out_md: str, commands: str) -> str:
     return text
 
 
+STALL_COUNTERS = ("SQ_WAVE_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_WAIT_INST_LDS SQ_ACTIVE_INST_VALU SQ_ACTIVE_INST_LDS "
+                  "SQ_ACTIVE_INST_ANY SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE")
+
+
+def stall_md(directory: str, out_md: str, title: str, commands: str) -> str:
+    """Where each kernel's wave-cycles go, from one counter pass: waiting at s_waitcnt for memory
+    or LDS results (SQ_WAIT_ANY), ready but not issued because other waves hold the issue slots
+    (SQ_WAIT_INST_ANY; of which waiting to issue an LDS instruction: SQ_WAIT_INST_LDS), and issuing
+    (SQ_ACTIVE_INST_ANY; of which VALU and LDS). The three parts add up to the wave-cycles."""
+    path = glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True)
+    if not path:
+        raise FileNotFoundError(f"no counter_collection.csv under {directory}")
+    tot, disp = defaultdict(lambda: defaultdict(float)), defaultdict(set)
+    for row in csv.DictReader(open(path[0])):
+        k = kernel_key(row["Kernel_Name"])
+        if k is None:
+            continue
+        tot[k][row["Counter_Name"]] += float(row["Counter_Value"])
+        disp[k].add(row["Dispatch_Id"])
+    lines = [f"# {title}", "", "Command (run from the repository root on one MI355X; one counter pass):", "", "```",
+             commands, "```", "",
+             "Shares of each kernel's wave-cycles (SQ_WAVE_CYCLES): waiting at `s_waitcnt` for memory or LDS "
+             "results (SQ_WAIT_ANY); ready but not issued while other waves use the issue slots "
+             "(SQ_WAIT_INST_ANY, of which LDS instructions: SQ_WAIT_INST_LDS); issuing (SQ_ACTIVE_INST_ANY, "
+             "of which VALU and LDS). The first, second and fourth columns add up to 1. MFMA busy: "
+             "SQ_VALU_MFMA_BUSY_CYCLES over GRBM_GUI_ACTIVE (summed over the 8 XCDs) times the 1024 SIMDs.", "",
+             "| kernel | dispatches | waiting at s_waitcnt | ready, not issued | (LDS) | issuing | (VALU) | (LDS) | MFMA busy |",
+             "|---|---|---|---|---|---|---|---|---|"]
+    for k in sorted(tot):
+        c, wc = tot[k], tot[k]["SQ_WAVE_CYCLES"]
+        busy = c["SQ_VALU_MFMA_BUSY_CYCLES"] / (c["GRBM_GUI_ACTIVE"] / N_XCD * N_SIMD) if c["GRBM_GUI_ACTIVE"] else 0.0
+        lines.append(f"| {k} | {len(disp[k])} | {c['SQ_WAIT_ANY'] / wc:.3f} | {c['SQ_WAIT_INST_ANY'] / wc:.3f} | "
+                     f"{c['SQ_WAIT_INST_LDS'] / wc:.3f} | {c['SQ_ACTIVE_INST_ANY'] / wc:.3f} | "
+                     f"{c['SQ_ACTIVE_INST_VALU'] / wc:.3f} | {c['SQ_ACTIVE_INST_LDS'] / wc:.3f} | {100 * busy:.1f}% |")
+    text = "\n".join(lines) + "\n"
+    with open(out_md, "w") as f:
+        f.write(text)
+    return text
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -350,6 +390,11 @@ def main():
     r.add_argument("--copy-bytes", type=int, required=True)
     r.add_argument("--run", nargs=4, action="append", required=True,
                    metavar=("WORKLOAD", "FETCH_DIR", "WRITE_DIR", "KERNEL_STATS_CSV"))
+    st = sub.add_parser("stalls", help="wave-cycle breakdown (waiting / ready / issuing) from one counter pass")
+    st.add_argument("directory")
+    st.add_argument("out_md")
+    st.add_argument("title")
+    st.add_argument("command")
     c = sub.add_parser("counters", help="MFMA / VALU / LDS counter summary; --run LABEL DIR WORKLOAD per workload")
     c.add_argument("--run", nargs=3, action="append", required=True, metavar=("LABEL", "DIR", "WORKLOAD"))
     c.add_argument("--out-md", required=True)
@@ -357,6 +402,8 @@ def main():
     a = ap.parse_args()
     if a.cmd == "trace":
         print(trace(a.stats_csv, a.out_md, a.command, a.title, a.bench_json, a.plain_json))
+    elif a.cmd == "stalls":
+        print(stall_md(a.directory, a.out_md, a.title, a.command))
     elif a.cmd == "counters":
         from . import inputs
         runs = []

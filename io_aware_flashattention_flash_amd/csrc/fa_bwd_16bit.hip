@@ -293,11 +293,30 @@ __global__ __launch_bounds__(NW * 64, (dkdv_waves_per_simd<D, PART, CAUSAL, MASK
           for (int e = 0; e < 4; ++e) dp[4 * g + e] = nd4[e];
         }
       }
+      if constexpr (D >= 128) {
+        // one wave per SIMD (or the d = 128 parts): the next k-step's Q / dO fragments are read one
+        // step ahead, as no other wave hides the LDS latency in front of each product
+        e16x8 qn = lds_read16<E>(qbuf, T::chunk_off(32 * qb + lq, hf)), on;
+        if (WANT_DK) on = lds_read16<E>(obuf, T::chunk_off(32 * qb + lq, hf));
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
-        const int off = T::chunk_off(32 * qb + lq, 2 * kk + hf);
-        s = H::mfma(lds_read16<E>(qbuf, off), kreg[kk], s);
-        if (WANT_DK) dp = H::mfma(lds_read16<E>(obuf, off), vreg[kk], dp);
+        for (int kk = 0; kk < NKK; ++kk) {
+          const e16x8 qc = qn, oc = on;
+          if (kk + 1 < NKK) {
+            const int off = T::chunk_off(32 * qb + lq, 2 * (kk + 1) + hf);
+            qn = lds_read16<E>(qbuf, off);
+            if (WANT_DK) on = lds_read16<E>(obuf, off);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          s = H::mfma(qc, kreg[kk], s);
+          if (WANT_DK) dp = H::mfma(oc, vreg[kk], dp);
+        }
+      } else {
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) {
+          const int off = T::chunk_off(32 * qb + lq, 2 * kk + hf);
+          s = H::mfma(lds_read16<E>(qbuf, off), kreg[kk], s);
+          if (WANT_DK) dp = H::mfma(lds_read16<E>(obuf, off), vreg[kk], dp);
+        }
       }
       // Register r holds query q0 + 8*(r/4) + 4*hf + r%4 against this lane's key.
       const int kmin = key - q0 - 4 * hf;  // (DIAG) query offsets below this are masked
@@ -342,17 +361,48 @@ __global__ __launch_bounds__(NW * 64, (dkdv_waves_per_simd<D, PART, CAUSAL, MASK
       }
       // dV^T += dO^T P and dK^T += Q^T dS; k-step ks covers queries
       // 32qb + 16ks + {4hf..4hf+3, 8+4hf..8+4hf+3} (registers 8ks..8ks+7).
+      if constexpr (D >= 128) {
+        // the transposed dO / Q fragments of step (db, ks) + 1 read before step (db, ks)'s products
+        auto tr_off = [&](int st, int& o0, int& o1) __attribute__((always_inline)) {
+          const int db = st >> 1, ks = st & 1;
+          const int r0 = 32 * qb + 16 * ks + tr_row_lane, col = 32 * db + tr_col_lane;
+          o0 = T::elem_off(r0, col);
+          o1 = T::elem_off(r0 + 8, col);
+        };
+        e16x8 vn, kn;
+        {
+          int o0, o1;
+          tr_off(0, o0, o1);
+          if (WANT_DV) vn = cat4<E>(lds_read_tr16<E>(obuf, o0), lds_read_tr16<E>(obuf, o1));
+          if (WANT_DK) kn = cat4<E>(lds_read_tr16<E>(qbuf, o0), lds_read_tr16<E>(qbuf, o1));
+        }
 #pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const int col = 32 * db + tr_col_lane;
+        for (int st = 0; st < 2 * NDB; ++st) {
+          const e16x8 vc = vn, kc = kn;
+          if (st + 1 < 2 * NDB) {
+            int o0, o1;
+            tr_off(st + 1, o0, o1);
+            if (WANT_DV) vn = cat4<E>(lds_read_tr16<E>(obuf, o0), lds_read_tr16<E>(obuf, o1));
+            if (WANT_DK) kn = cat4<E>(lds_read_tr16<E>(qbuf, o0), lds_read_tr16<E>(qbuf, o1));
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          const int db = st >> 1, ks = st & 1;
+          if (WANT_DV) dv[db] = H::mfma(vc, pb[ks], dv[db]);
+          if (WANT_DK) dk[db] = H::mfma(kc, dsb[ks], dk[db]);
+        }
+      } else {
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-          const int r0 = 32 * qb + 16 * ks + tr_row_lane;
-          const int o0 = T::elem_off(r0, col), o1 = T::elem_off(r0 + 8, col);
-          if (WANT_DV)
-            dv[db] = H::mfma(cat4<E>(lds_read_tr16<E>(obuf, o0), lds_read_tr16<E>(obuf, o1)), pb[ks], dv[db]);
-          if (WANT_DK)
-            dk[db] = H::mfma(cat4<E>(lds_read_tr16<E>(qbuf, o0), lds_read_tr16<E>(qbuf, o1)), dsb[ks], dk[db]);
+        for (int db = 0; db < NDB; ++db) {
+          const int col = 32 * db + tr_col_lane;
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks) {
+            const int r0 = 32 * qb + 16 * ks + tr_row_lane;
+            const int o0 = T::elem_off(r0, col), o1 = T::elem_off(r0 + 8, col);
+            if (WANT_DV)
+              dv[db] = H::mfma(cat4<E>(lds_read_tr16<E>(obuf, o0), lds_read_tr16<E>(obuf, o1)), pb[ks], dv[db]);
+            if (WANT_DK)
+              dk[db] = H::mfma(cat4<E>(lds_read_tr16<E>(qbuf, o0), lds_read_tr16<E>(qbuf, o1)), dsb[ks], dk[db]);
+          }
         }
       }
     }
@@ -653,11 +703,20 @@ __global__ __launch_bounds__(NW * 64, D > 128 ? 1 : 2) void bwd_dq_kernel(BwdPar
         s[kb] = f32x16{};
         // FOLD_DELTA: dP starts from -delta (the lane's query), giving dP - delta directly
         dp[kb] = FOLD_DELTA ? ndlt : f32x16{};
+        // (d >= 128, one 32-key block per tile) the next k-step's K / V fragments read one step ahead
+        e16x8 kn = lds_read16<E>(kbuf, T::chunk_off(32 * kb + lq, hf));
+        e16x8 vn = lds_read16<E>(vbuf, T::chunk_off(32 * kb + lq, hf));
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk) {
-          const int off = T::chunk_off(32 * kb + lq, 2 * kk + hf);
-          s[kb] = H::mfma(lds_read16<E>(kbuf, off), qreg[kk], s[kb]);
-          dp[kb] = H::mfma(lds_read16<E>(vbuf, off), oreg[kk], dp[kb]);
+          const e16x8 kc = kn, vc = vn;
+          if (kk + 1 < NKK) {
+            const int off = T::chunk_off(32 * kb + lq, 2 * (kk + 1) + hf);
+            kn = lds_read16<E>(kbuf, off);
+            vn = lds_read16<E>(vbuf, off);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          s[kb] = H::mfma(kc, qreg[kk], s[kb]);
+          dp[kb] = H::mfma(vc, oreg[kk], dp[kb]);
         }
       }
       if constexpr (DROPOUT) {
@@ -667,6 +726,7 @@ __global__ __launch_bounds__(NW * 64, D > 128 ? 1 : 2) void bwd_dq_kernel(BwdPar
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
         e16x8 dsb;
+        e16x8 fn = frag_dq(ks, 0);  // read before the elementwise work, which covers its latency
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int r = (ks & 1) * 8 + e;
@@ -679,9 +739,15 @@ __global__ __launch_bounds__(NW * 64, D > 128 ? 1 : 2) void bwd_dq_kernel(BwdPar
           if constexpr (DROPOUT) dpr = dropout_keep(kw[ks >> 1][r >> 2], r & 3, p.drop_thr) ? dpr * p.drop_scale : 0.f;
           dsb[e] = (E)(FOLD_DELTA ? pr * dpr : pr * (dpr - dlt));
         }
-        // dQ^T += K^T dS^T; k-step ks covers keys 16ks + {4hf..4hf+3, 8+4hf..8+4hf+3}.
+        // dQ^T += K^T dS^T; k-step ks covers keys 16ks + {4hf..4hf+3, 8+4hf..8+4hf+3}. The next
+        // output block's fragment is read one product ahead.
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) dq[db] = H::mfma(frag_dq(ks, db), dsb, dq[db]);
+        for (int db = 0; db < NDB; ++db) {
+          const e16x8 fc = fn;
+          if (db + 1 < NDB) fn = frag_dq(ks, db + 1);
+          __builtin_amdgcn_sched_barrier(0);
+          dq[db] = H::mfma(fc, dsb, dq[db]);
+        }
       }
     }
   };

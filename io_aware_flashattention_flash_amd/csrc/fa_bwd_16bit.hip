@@ -296,7 +296,7 @@ __global__ __launch_bounds__(NW * 64, (dkdv_waves_per_simd<D, PART, CAUSAL, MASK
       if constexpr (D >= 128) {
         // one wave per SIMD (or the d = 128 parts): the next k-step's Q / dO fragments are read one
         // step ahead, as no other wave hides the LDS latency in front of each product
-        e16x8 qn = lds_read16<E>(qbuf, T::chunk_off(32 * qb + lq, hf)), on;
+        e16x8 qn = lds_read16<E>(qbuf, T::chunk_off(32 * qb + lq, hf)), on{};  // on: unused in the dV-only part
         if (WANT_DK) on = lds_read16<E>(obuf, T::chunk_off(32 * qb + lq, hf));
 #pragma unroll
         for (int kk = 0; kk < NKK; ++kk) {
@@ -369,7 +369,7 @@ __global__ __launch_bounds__(NW * 64, (dkdv_waves_per_simd<D, PART, CAUSAL, MASK
           o0 = T::elem_off(r0, col);
           o1 = T::elem_off(r0 + 8, col);
         };
-        e16x8 vn, kn;
+        e16x8 vn{}, kn{};  // each unused in the part that does not compute it
         {
           int o0, o1;
           tr_off(0, o0, o1);

@@ -18,11 +18,13 @@
 //     the untransposed score block S = Q K^T, so a lane holds one key and the
 //     registers run over queries: P and dS, rounded to the 16-bit type, are directly the
 //     B operands of dV^T += dO^T P and dK^T += Q^T dS, whose A operands
-//     (dO^T, Q^T) come from the LDS transpose read.
+//     (dO^T, Q^T) come from the LDS transpose read. In small causal launches the longest key
+//     tiles run as two workgroups of 64 keys each (split_rank).
 //  3. dQ kernel (query-outer): the forward's layout (S^T = K Q^T, a lane holds
 //     one query); computes its rows' delta from O and dO (and publishes it for
 //     kernel 2), recomputes P and dP, forms dS^T and accumulates
 //     dQ^T += K^T dS^T with K^T from the LDS transpose read.
+#include <algorithm>
 #include <type_traits>
 
 #include "fa_device.h"
@@ -46,6 +48,10 @@ struct BwdParams {
   int nh;
   int n_tiles;
   int n_units;  // workgroups per head (dQ: n_tiles, or (n_tiles + 1) / 2 when causal tiles are paired)
+  // Split dK/dV launches (small dense causal ones): the first n_split key tiles of each head run as
+  // two half-size workgroups; n_long orders a head's workgroups (see split_rank).
+  int n_split;
+  int n_long;
   float c;      // scale * log2(e)
   float scale;
   // Masked launches only: per-sequence valid rows (sequence = head / heads; clamped to [0, N]) and
@@ -142,12 +148,32 @@ __global__ __launch_bounds__(256) void bwd_delta_kernel(BwdParams<E> p) {
 // Waves per SIMD: 2 where the registers fit 256 per lane (d <= 64, d = 96, the parts at d = 128),
 // else 1. The dense causal d = 64 kernel fits 168 registers and runs 3 (measured 2.4% faster; the
 // non-causal one was 2.4% slower at 3, and the masked ones spill there).
+// Split launches. Key tile kt of a causal head sees n_qt - 2 kt query tiles of 64 rows, so when a
+// launch's workgroups all fit on the chip at once, the launch lasts as long as key tile 0. Its
+// first n_split key tiles then run as two workgroups each, one per 64-key half (hs = 0, 1): wave w
+// takes the 32 keys of group w & 1 against query block w >> 1 of every query tile, and the two waves
+// of a key group add their partial sums through LDS at the end. A head's workgroups run longest
+// first: key tiles n_split .. n_long - 1 (longer than any half), the halves, then the rest.
+__device__ __forceinline__ void split_rank(int r, int n_split, int n_long, int& kt, int& hs) {
+  if (r < n_long - n_split) {
+    kt = n_split + r;
+    hs = -1;
+  } else if (r < n_long + n_split) {
+    const int j = r - (n_long - n_split);
+    kt = j >> 1;
+    hs = j & 1;
+  } else {
+    kt = r - n_split;
+    hs = -1;
+  }
+}
+
 template <int D, int PART, bool CAUSAL, bool MASKED>
 constexpr int dkdv_waves_per_simd() {
   return (D > 128 || (D == 128 && PART == 0)) ? 1 : ((D == 64 && CAUSAL && !MASKED) ? 3 : 2);
 }
 
-template <typename E, int D, int NW, int BQ, bool CAUSAL, bool MASKED, bool DROPOUT, int PART>
+template <typename E, int D, int NW, int BQ, bool CAUSAL, bool MASKED, bool DROPOUT, int PART, bool QSPLIT = false>
 __global__ __launch_bounds__(NW * 64, (dkdv_waves_per_simd<D, PART, CAUSAL, MASKED>())) void bwd_dkdv_kernel(BwdParams<E> p) {
   constexpr bool WANT_DV = PART != 2, WANT_DK = PART != 1;
   using H = Half16<E>;
@@ -166,6 +192,8 @@ __global__ __launch_bounds__(NW * 64, (dkdv_waves_per_simd<D, PART, CAUSAL, MASK
   // accumulator, one VALU operation less per score (not in the one-wave d = 128 kernel, whose
   // registers are full: measured slower there).
   constexpr bool FOLD_DELTA = !DROPOUT && !(D == 128 && PART == 0);
+  static_assert(!QSPLIT || (CAUSAL && !MASKED && PART == 0 && NW == 4 && BQ == 64),
+                "split launches: dense causal dK and dV, 2 key groups x 2 query blocks of 32");
 
   __shared__ __attribute__((aligned(16))) char sq0[TILE_BYTES];
   __shared__ __attribute__((aligned(16))) char so0[TILE_BYTES];
@@ -180,15 +208,22 @@ __global__ __launch_bounds__(NW * 64, (dkdv_waves_per_simd<D, PART, CAUSAL, MASK
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l = tid & 63, lq = l & 31, hf = l >> 5;
   const int N = p.N;
-  int head, kt;
+  int head, kt, hs = -1;
   // causal: key tile 0 has the most work; with sequence lengths, padding key tiles run last
-  if (!(MASKED && p.seqlens &&
-        map_workgroup_varlen(blockIdx.x, p.n_tiles, p.nh, p.heads, p.seqlens, p.N, BKV, CAUSAL, false, head, kt)))
+  if constexpr (QSPLIT) {
+    int r;
+    map_workgroup(blockIdx.x, p.n_tiles + p.n_split, p.nh, Order::kLongestFirst, false, head, r);
+    split_rank(r, p.n_split, p.n_long, kt, hs);
+  } else if (!(MASKED && p.seqlens &&
+               map_workgroup_varlen(blockIdx.x, p.n_tiles, p.nh, p.heads, p.seqlens, p.N, BKV, CAUSAL, false, head, kt))) {
     map_workgroup(blockIdx.x, p.n_tiles, p.nh, CAUSAL ? Order::kLongestFirst : Order::kHeadMajor, false, head, kt);
+  }
+  const bool split = QSPLIT && hs >= 0;                  // a 64-key half (wave-uniform)
+  const int kspan0 = kt * BKV + (split ? 64 * hs : 0);  // the workgroup's first key
   const size_t base = (size_t)head * N * D;
   const size_t rbase = (size_t)head * N;
   const int head_bytes = N * D * 2;
-  const int key_w0 = kt * BKV + 32 * w;
+  const int key_w0 = kspan0 + 32 * (split ? (w & 1) : w);
   const int key = key_w0 + lq;
   const int Lb = valid_rows<MASKED>(p, head);  // rows >= Lb of every input read as zero
 
@@ -213,7 +248,7 @@ __global__ __launch_bounds__(NW * 64, (dkdv_waves_per_simd<D, PART, CAUSAL, MASK
   }
 
   const int n_qt = (Lb + BQ - 1) / BQ;
-  const int qt0 = CAUSAL ? (kt * BKV) / BQ : 0;
+  const int qt0 = CAUSAL ? kspan0 / BQ : 0;
   // Loop positions u = 0 .. n_t - 1 map to query tiles tile(u): qt0 + u, or with a block map the
   // tile pairs of the enabled 128-row blocks (causal: from the diagonal block on).
   constexpr int TPB = kMaskBlock / BQ;
@@ -280,6 +315,7 @@ __global__ __launch_bounds__(NW * 64, (dkdv_waves_per_simd<D, PART, CAUSAL, MASK
     constexpr bool DIAG = decltype(diag_tag)::value;
 #pragma unroll
     for (int qb = 0; qb < NQB; ++qb) {
+      if (split && qb != (w >> 1)) continue;  // the other wave of this key group takes the block
       const int q0 = i * BQ + 32 * qb;
       if (DIAG && q0 + 31 < key_w0) continue;  // wave-uniform: every query precedes every key
       // FOLD_DELTA: the dP product starts from -delta of each register's query, so it yields
@@ -451,6 +487,45 @@ __global__ __launch_bounds__(NW * 64, (dkdv_waves_per_simd<D, PART, CAUSAL, MASK
   // dK = scale * dK^T^T and dV, written as whole rows through this wave's idle tile buffer.
   __syncthreads();  // every wave is done reading the last Q / dO tile
   char* stage = w == 0 ? sq0 : (w == 1 ? so0 : (w == 2 ? sq1 : so1));
+  if (split) {
+    // Waves g and g + 2 hold key group g's partial sums over query blocks 0 and 1. Wave g + 2 hands
+    // its dK partial to wave g, wave g hands its dV partial to wave g + 2 (fp32, through the tile
+    // buffers: each partial is 128 * D bytes, one tile buffer); then wave g writes dK and wave
+    // g + 2 writes dV.
+    const int g = w & 1;
+    const bool fin_dk = w < 2;
+    char* xbuf_dk = g ? sq1 : sq0;
+    char* xbuf_dv = g ? so1 : so0;
+    static_assert(NDB * 4 * 64 * 16 == TILE_BYTES, "a partial fills one tile buffer");
+    auto give = [&](const f32x16(&acc)[NDB], char* buf) __attribute__((always_inline)) {
+      f32x4* out4 = reinterpret_cast<f32x4*>(buf);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          out4[(4 * db + q4) * 64 + l] = f32x4{acc[db][4 * q4], acc[db][4 * q4 + 1], acc[db][4 * q4 + 2], acc[db][4 * q4 + 3]};
+    };
+    auto take = [&](f32x16(&acc)[NDB], const char* buf) __attribute__((always_inline)) {
+      const f32x4* in4 = reinterpret_cast<const f32x4*>(buf);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const f32x4 t = in4[(4 * db + q4) * 64 + l];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[db][4 * q4 + e] += t[e];
+        }
+    };
+    if (fin_dk) give(dv, xbuf_dv);
+    else give(dk, xbuf_dk);
+    __syncthreads();
+    if (fin_dk) take(dk, xbuf_dk);
+    else take(dv, xbuf_dv);
+    __syncthreads();  // every handed-over partial is read before the staging areas are reused
+    if (fin_dk) store_rows_via_lds<E, D, TILE_BYTES>(stage, dk, p.scale, make_rsrc(p.dk + base, head_bytes), key_w0, l);
+    else store_rows_via_lds<E, D, TILE_BYTES>(stage, dv, 1.0f, make_rsrc(p.dv + base, head_bytes), key_w0, l);
+    return;
+  }
   if (WANT_DK) store_rows_via_lds<E, D, TILE_BYTES>(stage, dk, p.scale, make_rsrc(p.dk + base, head_bytes), key_w0, l);
   if (WANT_DV) store_rows_via_lds<E, D, TILE_BYTES>(stage, dv, 1.0f, make_rsrc(p.dv + base, head_bytes), key_w0, l);
 }
@@ -828,6 +903,8 @@ BwdParams<E> make_params(const void* q, const void* k, const void* v, const void
   prm.nh = BH;
   prm.n_tiles = 0;
   prm.n_units = 0;
+  prm.n_split = 0;
+  prm.n_long = 0;
   prm.c = scale * kLog2e;
   prm.scale = scale;
   prm.seqlens = nullptr;
@@ -858,6 +935,26 @@ hipError_t dkdv_d(BwdParams<E> prm, hipStream_t stream) {
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, kKvNW, kKvBQ, CAUSAL, MASKED, DROPOUT, 2>), grid, block, 0, stream, prm);
   } else {
+    if constexpr (CAUSAL && !MASKED) {
+      // Small launch (its workgroups fit on the chip at once): split about 3/8 of the key tiles, as
+      // long as the extra workgroups still fit. Halving a tile costs ~25% more time per query tile
+      // (half the work per barrier and tile load), so key tile 0's halves then last about as long
+      // as the first unsplit tile.
+      const long slots = (long)device_cu_count() * dkdv_waves_per_simd<D, 0, CAUSAL, MASKED>();
+      const long wgs = (long)prm.n_tiles * prm.nh;
+      if (prm.n_tiles >= 8 && wgs < slots) {
+        const long fit = slots / prm.nh - prm.n_tiles;
+        const int n_split = (int)std::min<long>((3 * prm.n_tiles + 4) / 8, fit);
+        if (n_split >= 3) {
+          const int n_qt = (prm.N + kKvBQ - 1) / kKvBQ;
+          prm.n_split = n_split;
+          prm.n_long = std::max(n_split, std::min(prm.n_tiles, (n_qt + 3) / 4));
+          hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, kKvNW, kKvBQ, CAUSAL, MASKED, DROPOUT, 0, true>),
+                             dim3((prm.n_tiles + n_split) * prm.nh), block, 0, stream, prm);
+          return hipGetLastError();
+        }
+      }
+    }
     hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, kKvNW, kKvBQ, CAUSAL, MASKED, DROPOUT, 0>), grid, block, 0, stream, prm);
   }
   return hipGetLastError();

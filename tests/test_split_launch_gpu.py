@@ -1,12 +1,18 @@
-"""GPU parity of small causal backward launches, where the dK/dV kernel runs the longest key tiles of
-each head as two half-size workgroups (keys 0-63 and 64-127 of the tile; each wave takes one of the
-two 32-row blocks of every query tile, and the two waves that share keys add their partial sums at
-the end). The host splits about 3/8 of a head's key tiles when the launch has at least 8 key tiles
-per head and its workgroups all fit on the chip at once (so the launch would otherwise last as long
-as key tile 0), and only as many as still fit. The shapes below cover head dims 32 to 128, bf16 and
-fp16, ragged lengths, and a launch where the fit bounds the split count (12 heads of 16 key tiles at
-d = 128, one workgroup per CU). Every element of dQ, dK and dV is compared with the float64
-oracle; outputs are poisoned with NaN beforehand."""
+"""GPU parity of small causal backward launches, where the backward kernels split their longest
+tiles across two half-size workgroups:
+  * dK/dV: the longest key tiles of each head (keys 0-63 and 64-127 of the tile); each wave takes
+    one of the two 32-row blocks of every query tile, and the two waves that share keys add their
+    partial sums at the end. The host splits about 3/8 of a head's key tiles when the launch has
+    at least 8 key tiles per head and its workgroups all fit on the chip at once (so the launch
+    would otherwise last as long as key tile 0), and only as many as still fit.
+  * dQ (d <= 64, launches that fill at most half of the chip's slots): the longest query tiles
+    (rows 0-63 and 64-127 of the tile); each wave takes one of the two 32-key blocks of every key
+    tile, and the two waves that share rows add their partial sums at the end.
+The shapes below cover head dims 32 to 128, bf16 and fp16, ragged lengths, and a launch where the
+fit bounds the dK/dV split count (12 heads of 16 key tiles at d = 128, one workgroup per CU).
+Every element of dQ, dK and dV is compared with the float64 oracle; outputs are poisoned with NaN
+beforehand."""
+import numpy as np
 import pytest
 import torch
 
@@ -47,8 +53,9 @@ def test_bwd_small_causal_launch(dtype, d, B, H, N):
 
 
 def test_bwd_small_causal_launch_deterministic_and_staged():
-    """Repeated calls give the same bits, and the staged dQ then dK/dV calls reproduce the fused
-    backward bit for bit."""
+    """Repeated calls give the same bits, the staged dQ then dK/dV calls reproduce the fused
+    backward bit for bit, and the delta rows the split dQ launch writes (one wave of each pair
+    writes them) equal rowsum(dO * O) in float64."""
     w = inputs.Workload("t", "bf16", 1, 2, 2048, 64, True, True)
     x = inputs.make_inputs(w, seed=41)
     q, k, v, do = (dev(x[n], torch.bfloat16) for n in ("q", "k", "v", "do"))
@@ -62,3 +69,5 @@ def test_bwd_small_causal_launch_deterministic_and_staged():
     dk2, dv2 = flash_attn_bwd_dkdv(q, k, v, lse, do, delta, w.scale, True)
     torch.cuda.synchronize()
     assert torch.equal(ref[0], dq2) and torch.equal(ref[1], dk2) and torch.equal(ref[2], dv2)
+    want = np.sum(host(o) * x["do"].astype(np.float64), axis=-1)
+    assert np.abs(host(delta) - want).max() <= 1e-4 * max(1.0, np.abs(want).max())

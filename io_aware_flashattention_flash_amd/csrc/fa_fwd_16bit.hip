@@ -144,7 +144,14 @@ enum FwdMode : int { kDense = 0, kSplit = 1, kMasked = 2, kMaskedDropout = 3 };
 
 // d = 256 needs more than half the register file per lane (O accumulator 128, Q operand 64): one
 // workgroup per CU, one wave per SIMD. Smaller head dims run two workgroups per CU.
-template <typename E, int D, int BC, int NW, bool CAUSAL, int MODE>
+//
+// QSPLIT (dense launches at d <= 64 whose 128-row tiles are no more than the CUs): a workgroup
+// takes 64 query rows, and its two wave pairs take the even and the odd K/V tiles: wave w runs the
+// 32 rows of group w & 1 over tiles w >> 1, (w >> 1) + 2, ..., each pair with its own double
+// buffer, and the pair of odd tiles hands its (m, l, l~, O) to the other at the end, which merges
+// them by the online-softmax rule. A wave's loop is the same as in the plain launch; the
+// workgroups are twice as many and each row's key loop half as long.
+template <typename E, int D, int BC, int NW, bool CAUSAL, int MODE, bool QSPLIT = false>
 __global__ __launch_bounds__(NW * 64, D > 128 ? 1 : 2) void fwd16_kernel(Fwd16Params<E> p) {
   constexpr bool KV_SPLIT = MODE == kSplit, DROPOUT = MODE == kMaskedDropout;
   constexpr bool MASKED = MODE == kMasked || DROPOUT;
@@ -162,11 +169,21 @@ __global__ __launch_bounds__(NW * 64, D > 128 ? 1 : 2) void fwd16_kernel(Fwd16Pa
   constexpr int NKK = D / 16;
   using T = SwizzledTile<D>;
   static_assert(!MASKED || BR == kMaskBlock, "a query tile is one row of the block map");
+  static_assert(!QSPLIT || (MODE == kDense && D <= 64 && NW == 4), "split launches: dense forward, d <= 64");
+  constexpr int RW = QSPLIT ? 64 : BR;    // query rows per workgroup
+  constexpr int DW = QSPLIT ? 2 : NW;     // waves that load one tile
+  constexpr int NLDW = BC * NCH / (64 * DW);  // their DMA instructions per tile
+  static_assert(NLDW * 64 * DW == BC * NCH, "a tile splits evenly over its loading waves");
 
   __shared__ __attribute__((aligned(16))) char sk0[TILE_BYTES];
   __shared__ __attribute__((aligned(16))) char sv0[TILE_BYTES];
   __shared__ __attribute__((aligned(16))) char sk1[TILE_BYTES];
   __shared__ __attribute__((aligned(16))) char sv1[TILE_BYTES];
+  // the odd-tile pair's buffers (split launches)
+  __shared__ __attribute__((aligned(16))) char skb0[QSPLIT ? TILE_BYTES : 16];
+  __shared__ __attribute__((aligned(16))) char svb0[QSPLIT ? TILE_BYTES : 16];
+  __shared__ __attribute__((aligned(16))) char skb1[QSPLIT ? TILE_BYTES : 16];
+  __shared__ __attribute__((aligned(16))) char svb1[QSPLIT ? TILE_BYTES : 16];
   __shared__ short blist[MASKED ? kMaxMaskBlocks : 1];  // enabled key blocks of this query tile
 
   const int tid = threadIdx.x;
@@ -195,7 +212,9 @@ __global__ __launch_bounds__(NW * 64, D > 128 ? 1 : 2) void fwd16_kernel(Fwd16Pa
   const E* Kh = p.k + kbase;
   const E* Vh = p.v + kbase;
   const int head_bytes = N * D * 2;
-  const int q_w0 = qt * BR + 32 * w;
+  const int stream = QSPLIT ? (w >> 1) : 0;  // split launches: even (0) or odd (1) K/V tiles
+  const int wl = QSPLIT ? (w & 1) : w;       // the wave's index among the waves loading its tiles
+  const int q_w0 = qt * RW + 32 * wl;
   const int q = q_w0 + lq;
 
   // Rows that see no key at all (padding rows, empty map rows): O = 0, LSE = -inf. This lane's
@@ -235,7 +254,7 @@ __global__ __launch_bounds__(NW * 64, D > 128 ? 1 : 2) void fwd16_kernel(Fwd16Pa
   }
   int n_kv = (Lk + BC - 1) / BC;
   if (CAUSAL) {
-    const int last_key = min(Lq, (qt + 1) * BR) - 1 + koff;  // the last key any row here sees
+    const int last_key = min(Lq, (qt + 1) * RW) - 1 + koff;  // the last key any row here sees
     n_kv = min(n_kv, last_key < 0 ? 0 : last_key / BC + 1);
   }
   // K/V tiles [jb, je) of this workgroup; keys at or beyond key_end are masked.
@@ -282,9 +301,17 @@ __global__ __launch_bounds__(NW * 64, D > 128 ? 1 : 2) void fwd16_kernel(Fwd16Pa
     }
     n_t = 2 * cnt;
   }
+  // Split launches: this wave pair's tiles stream, stream + 2, ...; both pairs run as many loop
+  // positions as the even tiles need (the odd pair's last one may be padding).
+  int n_loop = n_t;
+  if (QSPLIT) {
+    n_t = (n_kv - stream + 1) / 2;
+    n_loop = (n_kv + 1) / 2;
+  }
   // Tile index of loop position u. Positions past the end (the pipeline's look-ahead) map to a
   // tile beyond every key this workgroup can see: fully masked and never loaded.
   auto tile = [&](int u) __attribute__((always_inline)) -> int {
+    if (QSPLIT) return 2 * u + stream;
     if (!sparse) return jb + u;
     if (u >= n_t) return n_kv + 2;
     return 2 * __builtin_amdgcn_readfirstlane(blist[u >> 1]) + (u & 1);
@@ -293,10 +320,10 @@ __global__ __launch_bounds__(NW * 64, D > 128 ? 1 : 2) void fwd16_kernel(Fwd16Pa
   // Byte offsets (within a tile) of the 16-byte chunks this lane deposits: DMA instruction i of
   // wave w fills LDS chunk positions (w + NW*i)*64 + lane, i.e. swizzled (row, chunk) slots.
   // Tiles past the end of the head load zeros.
-  int goff[NLD];
+  int goff[NLDW];
 #pragma unroll
-  for (int i = 0; i < NLD; ++i) {
-    const int pos = (w + NW * i) * 64 + l;
+  for (int i = 0; i < NLDW; ++i) {
+    const int pos = (wl + DW * i) * 64 + l;
     const int row = pos / NCH, pc = pos % NCH;
     goff[i] = row * (D * 2) + ((pc ^ T::swz(row)) * 16);
   }
@@ -310,10 +337,10 @@ __global__ __launch_bounds__(NW * 64, D > 128 ? 1 : 2) void fwd16_kernel(Fwd16Pa
     const __amdgpu_buffer_rsrc_t r = make_rsrc(src + (size_t)min(key0, Lk) * D, rows * (D * 2));
     if (KV_SPLIT && p.kv_once) {
 #pragma unroll
-      for (int i = 0; i < NLD; ++i) buf_load16_to_lds_once(r, dst + (w + NW * i) * 1024, goff[i]);
+      for (int i = 0; i < NLDW; ++i) buf_load16_to_lds_once(r, dst + (wl + DW * i) * 1024, goff[i]);
     } else {
 #pragma unroll
-      for (int i = 0; i < NLD; ++i) buf_load16_to_lds(r, dst + (w + NW * i) * 1024, goff[i]);
+      for (int i = 0; i < NLDW; ++i) buf_load16_to_lds(r, dst + (wl + DW * i) * 1024, goff[i]);
     }
   };
 
@@ -515,55 +542,148 @@ __global__ __launch_bounds__(NW * 64, D > 128 ? 1 : 2) void fwd16_kernel(Fwd16Pa
   // follows phase A(j), the last reader of K(j) and V(j-1), and are awaited one tile later. The
   // tile count is padded to even; a padded tile is fully masked (its probabilities are zero) and
   // its V rows are real data or zeros, so it leaves O and l unchanged.
-  const int n_eff = (n_t + 1) & ~1;
-  const int j_first = tile(0);
-  dma(Kh, j_first, sk0);
-  dma(Vh, j_first, sv0);
-  if (n_t > 1) dma(Kh, tile(1), sk1);
-  wait_vmem();
-  __syncthreads();
-  s_half(s0, sk0, 0);
-  debug_stage_sync();
-  phase_a(j_first, sk0, sv1, no{});
-  debug_stage_sync();
+  if constexpr (QSPLIT) {
+    // Each wave pair runs the tile loop below on its own buffers. (The plain launches keep the loop
+    // written out on their four buffers: bound through this lambda, the compiler allocates their
+    // registers worse, one wave per SIMD fewer at d = 64.)
+    auto main_loop = [&](char* K0, char* V0, char* K1, char* V1) __attribute__((always_inline)) {
+      const int n_eff = (n_loop + 1) & ~1;
+      const int j_first = tile(0);
+      dma(Kh, j_first, K0);
+      dma(Vh, j_first, V0);
+      if (n_t > 1) dma(Kh, tile(1), K1);
+      wait_vmem();
+      __syncthreads();
+      s_half(s0, K0, 0);
+      debug_stage_sync();
+      phase_a(j_first, K0, V1, no{});
+      debug_stage_sync();
 #pragma unroll 1
-  for (int t = 0; t < n_eff - 2; t += 2) {
-    const int j0 = tile(t), j1 = tile(t + 1), j2 = tile(t + 2);
+      for (int t = 0; t < n_eff - 2; t += 2) {
+        const int j0 = tile(t), j1 = tile(t + 1), j2 = tile(t + 2);
+        wait_vmem();
+        __syncthreads();
+        if (t + 2 < n_t) dma(Kh, j2, K0);
+        dma(Vh, j1, V1);
+        debug_stage_sync();
+        phase_b(j0, K1, V0, yes{});
+        debug_stage_sync();
+        phase_a(j1, K1, V0, yes{});
+        debug_stage_sync();
+        wait_vmem();
+        __syncthreads();
+        if (t + 3 < n_t) dma(Kh, tile(t + 3), K1);
+        dma(Vh, j2, V0);
+        debug_stage_sync();
+        phase_b(j1, K0, V1, yes{});
+        debug_stage_sync();
+        phase_a(j2, K0, V1, yes{});
+        debug_stage_sync();
+      }
+      {  // the last two tiles: the same steps without scoring a tile past the end
+        const int t = n_eff - 2;
+        const int j0 = tile(t), j1 = tile(t + 1);
+        wait_vmem();
+        __syncthreads();
+        dma(Vh, j1, V1);
+        debug_stage_sync();
+        phase_b(j0, K1, V0, yes{});
+        debug_stage_sync();
+        phase_a(j1, K1, V0, yes{});
+        debug_stage_sync();
+        wait_vmem();
+        __syncthreads();
+        phase_b(j1, K0, V1, no{});
+        debug_stage_sync();
+        pv_only(V1, 1, p1);
+      }
+    };
+    if (stream == 1) main_loop(skb0, svb0, skb1, svb1);
+    else main_loop(sk0, sv0, sk1, sv1);
+  } else {
+    const int n_eff = (n_loop + 1) & ~1;
+    const int j_first = tile(0);
+    dma(Kh, j_first, sk0);
+    dma(Vh, j_first, sv0);
+    if (n_t > 1) dma(Kh, tile(1), sk1);
     wait_vmem();
     __syncthreads();
-    if (t + 2 < n_t) dma(Kh, j2, sk0);
-    dma(Vh, j1, sv1);
+    s_half(s0, sk0, 0);
     debug_stage_sync();
-    phase_b(j0, sk1, sv0, yes{});
+    phase_a(j_first, sk0, sv1, no{});
     debug_stage_sync();
-    phase_a(j1, sk1, sv0, yes{});
-    debug_stage_sync();
-    wait_vmem();
-    __syncthreads();
-    if (t + 3 < n_t) dma(Kh, tile(t + 3), sk1);
-    dma(Vh, j2, sv0);
-    debug_stage_sync();
-    phase_b(j1, sk0, sv1, yes{});
-    debug_stage_sync();
-    phase_a(j2, sk0, sv1, yes{});
-    debug_stage_sync();
+#pragma unroll 1
+    for (int t = 0; t < n_eff - 2; t += 2) {
+      const int j0 = tile(t), j1 = tile(t + 1), j2 = tile(t + 2);
+      wait_vmem();
+      __syncthreads();
+      if (t + 2 < n_t) dma(Kh, j2, sk0);
+      dma(Vh, j1, sv1);
+      debug_stage_sync();
+      phase_b(j0, sk1, sv0, yes{});
+      debug_stage_sync();
+      phase_a(j1, sk1, sv0, yes{});
+      debug_stage_sync();
+      wait_vmem();
+      __syncthreads();
+      if (t + 3 < n_t) dma(Kh, tile(t + 3), sk1);
+      dma(Vh, j2, sv0);
+      debug_stage_sync();
+      phase_b(j1, sk0, sv1, yes{});
+      debug_stage_sync();
+      phase_a(j2, sk0, sv1, yes{});
+      debug_stage_sync();
+    }
+    {  // the last two tiles: the same steps without scoring a tile past the end
+      const int t = n_eff - 2;
+      const int j0 = tile(t), j1 = tile(t + 1);
+      wait_vmem();
+      __syncthreads();
+      dma(Vh, j1, sv1);
+      debug_stage_sync();
+      phase_b(j0, sk1, sv0, yes{});
+      debug_stage_sync();
+      phase_a(j1, sk1, sv0, yes{});
+      debug_stage_sync();
+      wait_vmem();
+      __syncthreads();
+      phase_b(j1, sk0, sv1, no{});
+      debug_stage_sync();
+      pv_only(sv1, 1, p1);
+    }
   }
-  {  // the last two tiles: the same steps without scoring a tile past the end
-    const int t = n_eff - 2;
-    const int j0 = tile(t), j1 = tile(t + 1);
-    wait_vmem();
+  if constexpr (QSPLIT) {
+    // The odd-tile pair hands (m, l, l~, O) to the even-tile pair, which merges them:
+    // m = max(m_a, m_b), each part scaled by exp2(m_x - m) (the online-softmax block merge).
+    static_assert(NDB * 4 * 64 * 16 <= TILE_BYTES && 3 * 64 * 4 <= TILE_BYTES, "exchange fits a tile buffer");
+    __syncthreads();  // every wave is done reading its last K/V tiles
+    f32x4* xo = reinterpret_cast<f32x4*>(wl ? skb1 : skb0);
+    float* xs = reinterpret_cast<float*>(wl ? svb1 : svb0);
+    if (stream == 1) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          xo[(4 * db + q4) * 64 + l] = f32x4{acc_o[db][4 * q4], acc_o[db][4 * q4 + 1], acc_o[db][4 * q4 + 2], acc_o[db][4 * q4 + 3]};
+      xs[l] = m_run;
+      xs[64 + l] = l_run;
+      xs[128 + l] = lr_run;
+    }
     __syncthreads();
-    dma(Vh, j1, sv1);
-    debug_stage_sync();
-    phase_b(j0, sk1, sv0, yes{});
-    debug_stage_sync();
-    phase_a(j1, sk1, sv0, yes{});
-    debug_stage_sync();
-    wait_vmem();
-    __syncthreads();
-    phase_b(j1, sk0, sv1, no{});
-    debug_stage_sync();
-    pv_only(sv1, 1, p1);
+    if (stream == 1) return;  // (no workgroup barrier follows)
+    const float mb = xs[l], m_new = vmax(m_run, mb);
+    const float aa = fast_exp2(m_run - m_new), ab = fast_exp2(mb - m_new);
+    m_run = m_new;
+    l_run = l_run * aa + xs[64 + l] * ab;
+    lr_run = lr_run * aa + xs[128 + l] * ab;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const f32x4 t = xo[(4 * db + q4) * 64 + l];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc_o[db][4 * q4 + e] = acc_o[db][4 * q4 + e] * aa + t[e] * ab;
+      }
   }
 
   // Epilogue: O = O_acc / l~, LSE = ln2 * (m + log2 l). The accumulator holds one query row per
@@ -609,7 +729,7 @@ __global__ __launch_bounds__(NW * 64, D > 128 ? 1 : 2) void fwd16_kernel(Fwd16Pa
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc_o[db][r] = empty ? 0.f : acc_o[db][r];
   }
-  __syncthreads();  // every wave is done reading the last K/V tiles
+  if (!QSPLIT) __syncthreads();  // every wave is done reading the last K/V tiles (split: merged above)
   char* ostage = w == 0 ? sk0 : (w == 1 ? sv0 : (w == 2 ? sk1 : sv1));
   store_rows_via_lds<E, D, TILE_BYTES>(ostage, acc_o, inv, make_rsrc(p.o + base, head_bytes), q_w0, l);
   if (p.lse && hf == 0) {
@@ -619,10 +739,10 @@ __global__ __launch_bounds__(NW * 64, D > 128 ? 1 : 2) void fwd16_kernel(Fwd16Pa
   write_carried_rows();
 }
 
-template <typename E, int D, int BC, int NW, bool CAUSAL, int MODE>
+template <typename E, int D, int BC, int NW, bool CAUSAL, int MODE, bool QSPLIT = false>
 static hipError_t launch_cfg(const Fwd16Params<E>& prm, int n_splits, hipStream_t stream) {
-  hipLaunchKernelGGL((fwd16_kernel<E, D, BC, NW, CAUSAL, MODE>), dim3(prm.n_qt * prm.nh, n_splits), dim3(NW * 64), 0,
-                     stream, prm);
+  hipLaunchKernelGGL((fwd16_kernel<E, D, BC, NW, CAUSAL, MODE, QSPLIT>), dim3(prm.n_qt * prm.nh, n_splits), dim3(NW * 64),
+                     0, stream, prm);
   return hipGetLastError();
 }
 
@@ -674,6 +794,17 @@ static hipError_t launch_typed(const void* q, const void* k, const void* v, void
   prm.drop_scale = x.drop.threshold > 0 ? 256.0f / (float)x.drop.threshold : 0.f;
   return with_head_dim(d, [&](auto dd) {
     constexpr int D = decltype(dd)::value;
+    if constexpr (MODE == kDense && D <= 64) {
+      // Small launch (no more 128-row tiles than CUs, at least 4 K/V tiles per row): 64-row
+      // workgroups whose wave pairs take the even and the odd K/V tiles (fwd16_kernel, QSPLIT),
+      // twice the workgroups, each with half the key loop.
+      if (N >= 256 && (long)prm.n_qt * BH <= device_cu_count()) {
+        Fwd16Params<E> sp = prm;
+        sp.n_qt = (N + 63) / 64;
+        return causal ? launch_cfg<E, D, 64, NW, true, MODE, true>(sp, 1, stream)
+                      : launch_cfg<E, D, 64, NW, false, MODE, true>(sp, 1, stream);
+      }
+    }
     return causal ? launch_cfg<E, D, 64, NW, true, MODE>(prm, x.n_splits, stream)
                   : launch_cfg<E, D, 64, NW, false, MODE>(prm, x.n_splits, stream);
   });

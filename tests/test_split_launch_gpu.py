@@ -8,18 +8,22 @@ tiles across two half-size workgroups:
   * dQ (d <= 64, launches that fill at most half of the chip's slots): the longest query tiles
     (rows 0-63 and 64-127 of the tile); each wave takes one of the two 32-key blocks of every key
     tile, and the two waves that share rows add their partial sums at the end.
-The shapes below cover head dims 32 to 128, bf16 and fp16, ragged lengths, and a launch where the
-fit bounds the dK/dV split count (12 heads of 16 key tiles at d = 128, one workgroup per CU).
-Every element of dQ, dK and dV is compared with the float64 oracle; outputs are poisoned with NaN
-beforehand."""
+  * forward (dense, d <= 64, no more 128-row tiles than CUs, N >= 256): 64-row workgroups whose
+    wave pairs take the even and the odd 64-key tiles of the rows; the odd pair hands its running
+    max, row sums and O accumulator to the even pair, which merges them by the online-softmax rule.
+The shapes below cover head dims 32 to 128, bf16 and fp16, ragged lengths, causal and not, a
+launch where the fit bounds the dK/dV split count (12 heads of 16 key tiles at d = 128, one
+workgroup per CU), and forward rows whose odd tiles score far above their even ones (the merge
+must rescale the even part). Every output element is compared with the float64 oracle; outputs
+are poisoned with NaN beforehand."""
 import numpy as np
 import pytest
 import torch
 
 from io_aware_flashattention_flash_amd import (flash_attn_bwd, flash_attn_bwd_dkdv, flash_attn_bwd_dq, flash_attn_fwd,
                                                inputs)
-from oracle import attn_bwd
-from tests.test_parity_gpu import GRAD, dev, grad_errors, host
+from oracle import attn_bwd, attn_fwd
+from tests.test_parity_gpu import BF16_LSE, BF16_O, GRAD, beyond_rounding, dev, grad_errors, host
 
 pytestmark = pytest.mark.gpu
 
@@ -71,3 +75,47 @@ def test_bwd_small_causal_launch_deterministic_and_staged():
     assert torch.equal(ref[0], dq2) and torch.equal(ref[1], dk2) and torch.equal(ref[2], dv2)
     want = np.sum(host(o) * x["do"].astype(np.float64), axis=-1)
     assert np.abs(host(delta) - want).max() <= 1e-4 * max(1.0, np.abs(want).max())
+
+
+@pytest.mark.parametrize("dtype,d,B,H,N,causal", [
+    ("bf16", 64, 1, 2, 1024, True),
+    ("bf16", 64, 1, 2, 2100, True),
+    ("bf16", 64, 1, 3, 1000, False),
+    ("bf16", 32, 2, 2, 1500, True),
+    ("bf16", 32, 1, 2, 333, False),
+    ("fp16", 64, 1, 2, 1100, True),
+    ("bf16", 64, 1, 2, 256, True),
+])
+def test_fwd_small_launch(dtype, d, B, H, N, causal):
+    print(f"split forward launch {dtype} B{B} H{H} N{N} d{d} causal {causal}", flush=True)
+    w = inputs.Workload("t", dtype, B, H, N, d, causal, False)
+    x = inputs.make_inputs(w, seed=3 * N + d + H)
+    q, k, v = (dev(x[n], DT[dtype]) for n in ("q", "k", "v"))
+    o = torch.full_like(q, float("nan"))
+    lse = torch.full(q.shape[:3], float("nan"), device=q.device)
+    flash_attn_fwd(q, k, v, w.scale, causal, out=o, lse=lse)
+    torch.cuda.synchronize()
+    O, L = attn_fwd(x["q"], x["k"], x["v"], w.scale, causal)
+    err, lerr = float(np.abs(host(o) - O).max()), float(np.abs(host(lse) - L).max())
+    print(f"  O err {err:.3e} (beyond output rounding {beyond_rounding(host(o), O):.3e}), LSE err {lerr:.3e}")
+    assert err <= BF16_O and lerr <= BF16_LSE
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fwd_small_launch_odd_tiles_score_higher(causal):
+    """Keys of the odd 64-key tiles scaled up so that their scores exceed the even tiles' by far
+    more than the 2^16 guard: the odd pair's running max ends far above the even pair's, and the
+    merge must scale the even part down by exp2(m_even - m) (underflowing to zero where the gap is
+    that large) without losing the odd part."""
+    B, H, N, d = 1, 2, 1024, 64
+    w = inputs.Workload("t", "bf16", B, H, N, d, causal, False)
+    x = inputs.make_inputs(w, seed=77)
+    factor = np.where((np.arange(N) // 64) % 2 == 1, 6.0, 1.0).astype(np.float32)
+    x["k"] = inputs.round_to_bf16(x["k"] * factor[None, None, :, None])
+    q, k, v = (dev(x[n], torch.bfloat16) for n in ("q", "k", "v"))
+    o, lse = flash_attn_fwd(q, k, v, w.scale, causal)
+    torch.cuda.synchronize()
+    O, L = attn_fwd(x["q"], x["k"], x["v"], w.scale, causal)
+    beyond, lerr = beyond_rounding(host(o), O), float(np.abs(host(lse) - L).max())
+    print(f"causal {causal}: O beyond output rounding {beyond:.3e}, LSE err {lerr:.3e}")
+    assert beyond <= BF16_O and lerr <= BF16_LSE

@@ -38,7 +38,7 @@ KERNEL_SOURCES = {"fwd": "fa_fwd_16bit.hip", "fwd_fp32": "fa_fwd_fp32.hip", "bwd
 KERNEL_PREFIX = {"fwd": ("fa::fwd16_kernel",), "fwd_fp32": ("fa::fwd_fp32_kernel", "fa::fwd_fp32_split_kernel"),
                  "bwd_dq": ("fa::bwd_dq_kernel",), "bwd_dkdv": ("fa::bwd_dkdv_kernel",),
                  "kvsplit_merge": ("fa::kvsplit_merge_kernel",)}
-KSPLIT_MODE = 1  # the forward kernel's last template argument in key-split launches
+KSPLIT_MODE = 1  # the forward kernel's sixth template argument (its launch mode) in key-split launches
 
 
 class Decode:
@@ -94,8 +94,10 @@ def readable_name(name: str) -> str:
 
 def kernel_key(name: str):
     short = readable_name(name)
-    if short.startswith("fa::fwd16_kernel<") and short.endswith(f", {KSPLIT_MODE}>"):
-        return "fwd_kvsplit"
+    if short.startswith("fa::fwd16_kernel<"):
+        args = short[len("fa::fwd16_kernel<"):-1].split(", ")
+        if len(args) > 5 and args[5] == str(KSPLIT_MODE):
+            return "fwd_kvsplit"
     for key, prefixes in KERNEL_PREFIX.items():
         if any(short.startswith(prefix + "<") for prefix in prefixes):
             return key

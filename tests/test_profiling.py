@@ -22,6 +22,15 @@ def test_mangled_and_demangled_names_classify_alike():
             ("fa::fwd16_kernel<bf16, 128, 64, 4, false, 1>", "fwd_kvsplit"),
         "_ZN2fa12fwd16_kernelIDF16_Li64ELi64ELi4ELb1ELi2EEEvNS_11Fwd16ParamsIT_EE":
             ("fa::fwd16_kernel<f16, 64, 64, 4, true, 2>", "fwd"),
+        # current instances carry one more argument (the split launches of small problems)
+        "_ZN2fa12fwd16_kernelIDF16bLi128ELi64ELi4ELb0ELi1ELb0EEEvNS_11Fwd16ParamsIT_EE":
+            ("fa::fwd16_kernel<bf16, 128, 64, 4, false, 1, false>", "fwd_kvsplit"),
+        "_ZN2fa12fwd16_kernelIDF16bLi64ELi64ELi4ELb1ELi0ELb1EEEvNS_11Fwd16ParamsIT_EE":
+            ("fa::fwd16_kernel<bf16, 64, 64, 4, true, 0, true>", "fwd"),
+        "_ZN2fa13bwd_dq_kernelIDF16bLi64ELi64ELi4ELb1ELb0ELb0ELb1EEEvNS_9BwdParamsIT_EE":
+            ("fa::bwd_dq_kernel<bf16, 64, 64, 4, true, false, false, true>", "bwd_dq"),
+        "_ZN2fa15bwd_dkdv_kernelIDF16bLi64ELi4ELi64ELb1ELb0ELb0ELi0ELb0EEEvNS_9BwdParamsIT_EE":
+            ("fa::bwd_dkdv_kernel<bf16, 64, 4, 64, true, false, false, 0, false>", "bwd_dkdv"),
         "__amd_rocclr_copyBuffer": ("__amd_rocclr_copyBuffer", None),
     }
     for raw, (pretty, key) in cases.items():

@@ -145,7 +145,8 @@ enum FwdMode : int { kDense = 0, kSplit = 1, kMasked = 2, kMaskedDropout = 3 };
 // d = 256 needs more than half the register file per lane (O accumulator 128, Q operand 64): one
 // workgroup per CU, one wave per SIMD. Smaller head dims run two workgroups per CU.
 //
-// QSPLIT (dense launches at d <= 64 whose 128-row tiles are no more than the CUs): a workgroup
+// QSPLIT (dense launches at d <= 128 whose 128-row tiles are no more than the CUs, or half of
+// them at d > 64, where the doubled tile buffers leave room for one workgroup per CU): a workgroup
 // takes 64 query rows, and its two wave pairs take the even and the odd K/V tiles: wave w runs the
 // 32 rows of group w & 1 over tiles w >> 1, (w >> 1) + 2, ..., each pair with its own double
 // buffer, and the pair of odd tiles hands its (m, l, l~, O) to the other at the end, which merges
@@ -169,7 +170,7 @@ __global__ __launch_bounds__(NW * 64, D > 128 ? 1 : 2) void fwd16_kernel(Fwd16Pa
   constexpr int NKK = D / 16;
   using T = SwizzledTile<D>;
   static_assert(!MASKED || BR == kMaskBlock, "a query tile is one row of the block map");
-  static_assert(!QSPLIT || (MODE == kDense && D <= 64 && NW == 4), "split launches: dense forward, d <= 64");
+  static_assert(!QSPLIT || (MODE == kDense && D <= 128 && NW == 4), "split launches: dense forward, d <= 128");
   constexpr int RW = QSPLIT ? 64 : BR;    // query rows per workgroup
   constexpr int DW = QSPLIT ? 2 : NW;     // waves that load one tile
   constexpr int NLDW = BC * NCH / (64 * DW);  // their DMA instructions per tile
@@ -794,11 +795,12 @@ static hipError_t launch_typed(const void* q, const void* k, const void* v, void
   prm.drop_scale = x.drop.threshold > 0 ? 256.0f / (float)x.drop.threshold : 0.f;
   return with_head_dim(d, [&](auto dd) {
     constexpr int D = decltype(dd)::value;
-    if constexpr (MODE == kDense && D <= 64) {
-      // Small launch (no more 128-row tiles than CUs, at least 4 K/V tiles per row): 64-row
-      // workgroups whose wave pairs take the even and the odd K/V tiles (fwd16_kernel, QSPLIT),
-      // twice the workgroups, each with half the key loop.
-      if (N >= 256 && (long)prm.n_qt * BH <= device_cu_count()) {
+    if constexpr (MODE == kDense && D <= 128) {
+      // Small launch (no more 128-row tiles than CUs, half as many at d > 64, whose split
+      // workgroups need 96-128 KB of LDS: one per CU; N >= 256): 64-row workgroups whose wave pairs
+      // take the even and the odd K/V tiles (fwd16_kernel, QSPLIT), twice the workgroups, each
+      // with half the key loop.
+      if (N >= 256 && (long)prm.n_qt * BH * (D > 64 ? 2 : 1) <= device_cu_count()) {
         Fwd16Params<E> sp = prm;
         sp.n_qt = (N + 63) / 64;
         return causal ? launch_cfg<E, D, 64, NW, true, MODE, true>(sp, 1, stream)

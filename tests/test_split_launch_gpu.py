@@ -1,5 +1,5 @@
-"""GPU parity of small causal backward launches, where the backward kernels split their longest
-tiles across two half-size workgroups:
+"""GPU parity of small launches (their workgroups fit on the chip at once), where the kernels split
+their longest work in two:
   * dK/dV: the longest key tiles of each head (keys 0-63 and 64-127 of the tile); each wave takes
     one of the two 32-row blocks of every query tile, and the two waves that share keys add their
     partial sums at the end. The host splits about 3/8 of a head's key tiles when the launch has
@@ -8,9 +8,10 @@ tiles across two half-size workgroups:
   * dQ (d <= 64, launches that fill at most half of the chip's slots): the longest query tiles
     (rows 0-63 and 64-127 of the tile); each wave takes one of the two 32-key blocks of every key
     tile, and the two waves that share rows add their partial sums at the end.
-  * forward (dense, d <= 64, no more 128-row tiles than CUs, N >= 256): 64-row workgroups whose
-    wave pairs take the even and the odd 64-key tiles of the rows; the odd pair hands its running
-    max, row sums and O accumulator to the even pair, which merges them by the online-softmax rule.
+  * forward (dense, d <= 128, no more 128-row tiles than CUs (half as many at d > 64), N >= 256):
+    64-row workgroups whose wave pairs take the even and the odd 64-key tiles of the rows; the
+    odd pair hands its running max, row sums and O accumulator to the even pair, which merges
+    them by the online-softmax rule.
 The shapes below cover head dims 32 to 128, bf16 and fp16, ragged lengths, causal and not, a
 launch where the fit bounds the dK/dV split count (12 heads of 16 key tiles at d = 128, one
 workgroup per CU), and forward rows whose odd tiles score far above their even ones (the merge
@@ -85,6 +86,10 @@ def test_bwd_small_causal_launch_deterministic_and_staged():
     ("bf16", 32, 1, 2, 333, False),
     ("fp16", 64, 1, 2, 1100, True),
     ("bf16", 64, 1, 2, 256, True),
+    ("bf16", 128, 1, 2, 1024, True),
+    ("bf16", 128, 1, 3, 700, False),
+    ("bf16", 96, 1, 2, 1000, True),
+    ("fp16", 128, 1, 2, 600, True),
 ])
 def test_fwd_small_launch(dtype, d, B, H, N, causal):
     print(f"split forward launch {dtype} B{B} H{H} N{N} d{d} causal {causal}", flush=True)

@@ -319,8 +319,9 @@ __global__ __launch_bounds__(NW * 64, D > 128 ? 1 : 2) void fwd16_kernel(Fwd16Pa
   };
 
   // Byte offsets (within a tile) of the 16-byte chunks this lane deposits: DMA instruction i of
-  // wave w fills LDS chunk positions (w + NW*i)*64 + lane, i.e. swizzled (row, chunk) slots.
-  // Tiles past the end of the head load zeros.
+  // loading wave wl (one of the NW waves, or of a split launch's pair) fills LDS chunk positions
+  // (wl + DW*i)*64 + lane, i.e. swizzled (row, chunk) slots. Tiles past the end of the head load
+  // zeros.
   int goff[NLDW];
 #pragma unroll
   for (int i = 0; i < NLDW; ++i) {

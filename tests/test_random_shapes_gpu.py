@@ -1,6 +1,7 @@
 """GPU parity on a seeded sweep of small shapes (the dense 16-bit forward and backward against the
 float64 oracle): batch, heads, ragged lengths, every head dim, causal or not, bf16 or fp16, and
-scales other than 1/sqrt(d) (larger, smaller, negative). Complements the fixed-shape tests with
+scales other than 1/sqrt(d) (larger, smaller, negative); a second sweep of longer causal rows
+reaches the split launches of small problems. Complements the fixed-shape tests with
 combinations none of them picks. Gates: O beyond the rounding of the stored output <= 1e-2 (the
 sharper rows of a large scale reach |O| where half a 16-bit ulp alone nears the gate), LSE <= 1e-3,
 gradients <= 5e-2 relative."""
@@ -52,6 +53,27 @@ def test_random_shape_fwd_bwd(i, B, H, N, d, causal, dtype, scale):
         assert np.isfinite(g).all(), name
         e_inf, e_fro = grad_errors(g, r)
         assert e_inf <= GRAD and e_fro <= GRAD, (name, e_inf, e_fro)
+
+
+def _long_configs(n=12, seed=4242):
+    """Causal rows long enough (at least 8 tiles of 128) for small launches to split the backward's
+    longest key and query tiles, and the forward's key loops, across two halves."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        d = int(rng.choice([32, 64, 96, 128]))
+        B = int(rng.integers(1, 3))
+        H = int(rng.choice([1, 2, 3]))
+        N = int(rng.choice([900, 1000, 1100, 1500, 2048]))
+        dtype = str(rng.choice(["bf16", "fp16"]))
+        scale = float(rng.choice([1.0, 0.5, 2.0, -1.0])) * d ** -0.5
+        out.append((100 + i, B, H, N, d, True, dtype, scale))
+    return out
+
+
+@pytest.mark.parametrize("i,B,H,N,d,causal,dtype,scale", _long_configs())
+def test_random_long_causal_fwd_bwd(i, B, H, N, d, causal, dtype, scale):
+    test_random_shape_fwd_bwd(i, B, H, N, d, causal, dtype, scale)
 
 
 def _masked_configs(n=64, seed=77):

@@ -23,8 +23,8 @@
 //  3. dQ kernel (query-outer): the forward's layout (S^T = K Q^T, a lane holds
 //     one query); computes its rows' delta from O and dO (and publishes it for
 //     kernel 2), recomputes P and dP, forms dS^T and accumulates
-//     dQ^T += K^T dS^T with K^T from the LDS transpose read. In small causal launches (d <= 64)
-//     the longest query tiles run as two workgroups of 64 rows each.
+//     dQ^T += K^T dS^T with K^T from the LDS transpose read. In small causal launches a
+//     workgroup takes 64 rows and its two wave pairs take the even and the odd key tiles.
 #include <algorithm>
 #include <type_traits>
 
@@ -538,8 +538,9 @@ __global__ __launch_bounds__(NW * 64, (dkdv_waves_per_simd<D, PART, CAUSAL, MASK
 // tile's map row; every tile takes the masked path.
 // DROPOUT (with MASKED): dS = P * (dP * keep * 256 / T - delta), the keep mask regenerated in
 // the forward's layout.
+// (Split launches at d = 96 hold 96 KB of tile buffers: one workgroup, one wave per SIMD.)
 template <typename E, int D, int BC, int NW, bool CAUSAL, bool MASKED, bool DROPOUT, bool QSPLIT = false>
-__global__ __launch_bounds__(NW * 64, D > 128 ? 1 : 2) void bwd_dq_kernel(BwdParams<E> p) {
+__global__ __launch_bounds__(NW * 64, (D > 128 || (QSPLIT && D == 96)) ? 1 : 2) void bwd_dq_kernel(BwdParams<E> p) {
   using H = Half16<E>;
   using e16x8 = typename H::x8;
   using e16x4 = typename H::x4;
@@ -555,17 +556,26 @@ __global__ __launch_bounds__(NW * 64, D > 128 ? 1 : 2) void bwd_dq_kernel(BwdPar
   // extra registers spill (measured slower).
   constexpr bool FOLD_DELTA = !DROPOUT && D != 96;
   static_assert(!MASKED || BR == kMaskBlock, "a query tile is one row of the block map");
-  // Split launches (small dense causal ones, see the host side): the last n_split query tiles of
-  // each head, the longest, run as two workgroups of 64 rows each (hs = 0, 1); wave w takes the
-  // 32 rows of group w & 1 against key block w >> 1 of every 64-key tile, and the two waves of a
-  // row group add their dQ partial sums through LDS at the end.
-  static_assert(!QSPLIT || (CAUSAL && !MASKED && !DROPOUT && NW == 4 && NKB == 2),
-                "split launches: dense causal, 2 row groups x 2 key blocks of 32");
+  // Split launches (small dense causal ones, see the host side): a workgroup takes 64 query rows,
+  // and its two wave pairs take the even and the odd K/V tiles: wave w runs the 32 rows of group
+  // w & 1 over tiles w >> 1, (w >> 1) + 2, ..., each pair with its own double buffer, and the pair
+  // of odd tiles hands its dQ partial sums to the other at the end. A wave's per-tile work is the
+  // same as in the plain launch; each row's key loop is half as long.
+  static_assert(!QSPLIT || (CAUSAL && !MASKED && !DROPOUT && NW == 4 && D <= 128), "split launches: dense causal");
+  constexpr int RW = QSPLIT ? 64 : BR;        // query rows per workgroup
+  constexpr int DW = QSPLIT ? 2 : NW;         // waves that load one tile
+  constexpr int NLDW = BC * NCH / (64 * DW);  // their DMA instructions per tile
+  static_assert(NLDW * 64 * DW == BC * NCH, "a tile splits evenly over its loading waves");
 
   __shared__ __attribute__((aligned(16))) char sk0[TILE_BYTES];
   __shared__ __attribute__((aligned(16))) char sv0[TILE_BYTES];
   __shared__ __attribute__((aligned(16))) char sk1[TILE_BYTES];
   __shared__ __attribute__((aligned(16))) char sv1[TILE_BYTES];
+  // the odd-tile pair's buffers (split launches)
+  __shared__ __attribute__((aligned(16))) char skb0[QSPLIT ? TILE_BYTES : 16];
+  __shared__ __attribute__((aligned(16))) char svb0[QSPLIT ? TILE_BYTES : 16];
+  __shared__ __attribute__((aligned(16))) char skb1[QSPLIT ? TILE_BYTES : 16];
+  __shared__ __attribute__((aligned(16))) char svb1[QSPLIT ? TILE_BYTES : 16];
   __shared__ short blist[MASKED ? kMaxMaskBlocks : 1];  // enabled key blocks of this query tile
 
   const int tid = threadIdx.x;
@@ -576,14 +586,10 @@ __global__ __launch_bounds__(NW * 64, D > 128 ? 1 : 2) void bwd_dq_kernel(BwdPar
   // after the other, so every workgroup does the same work and the launch has no tail of short
   // workgroups. (With few workgroups per CU the pairing would only serialise work, so it is off;
   // then tiles are dispatched longest-first.)
-  const bool paired = CAUSAL && p.n_units != p.n_tiles;
-  int head, unit, hs = -1;
+  const bool paired = !QSPLIT && CAUSAL && p.n_units != p.n_tiles;
+  int head, unit;
   if constexpr (QSPLIT) {
-    // split_rank counts tiles from the longest one (the head's last query tile)
-    int r, t;
-    map_workgroup(blockIdx.x, p.n_tiles + p.n_split, p.nh, Order::kLongestFirst, false, head, r);
-    split_rank(r, p.n_split, p.n_long, t, hs);
-    unit = p.n_tiles - 1 - t;
+    map_workgroup(blockIdx.x, p.n_units, p.nh, Order::kLongestFirst, true, head, unit);  // 64-row tiles
   } else if (!(MASKED && p.seqlens && !paired &&
                map_workgroup_varlen(blockIdx.x, p.n_units, p.nh, p.heads, p.seqlens, p.N, BR, CAUSAL, true, head,
                                     unit))) {
@@ -591,7 +597,8 @@ __global__ __launch_bounds__(NW * 64, D > 128 ? 1 : 2) void bwd_dq_kernel(BwdPar
     map_workgroup(blockIdx.x, p.n_units, p.nh, paired ? Order::kHeadMajor : (CAUSAL ? Order::kLongestFirst : Order::kHeadMajor),
                   !paired, head, unit);
   }
-  const bool split = QSPLIT && hs >= 0;  // a 64-row half (wave-uniform)
+  const int stream = QSPLIT ? (w >> 1) : 0;  // split launches: even (0) or odd (1) K/V tiles
+  const int wl = QSPLIT ? (w & 1) : w;       // the wave's index among the waves loading its tiles
   const int n_items = (paired && p.n_tiles - 1 - unit != unit) ? 2 : 1;
   const int Lb = valid_rows<MASKED>(p, head);  // rows >= Lb of every input read as zero
 #pragma unroll 1
@@ -601,8 +608,8 @@ __global__ __launch_bounds__(NW * 64, D > 128 ? 1 : 2) void bwd_dq_kernel(BwdPar
   const size_t base = (size_t)head * N * D;
   const size_t rbase = (size_t)head * N;
   const int head_bytes = N * D * 2;
-  const int row0 = qt * BR + (split ? 64 * hs : 0);  // the workgroup's first row
-  const int q_w0 = row0 + 32 * (split ? (w & 1) : w);
+  const int row0 = qt * RW;  // the workgroup's first row
+  const int q_w0 = row0 + 32 * wl;
   const int q = q_w0 + lq;
 
   // Q^T and dO^T operands: lane (q, hf) holds columns 16*kk + 8*hf .. +7 of its row. The same
@@ -627,11 +634,11 @@ __global__ __launch_bounds__(NW * 64, D > 128 ? 1 : 2) void bwd_dq_kernel(BwdPar
     }
     dlt = half_swap_sum(part);
     lse2 = buf_load4f(make_rsrc(p.lse + rbase, Lb * 4), q * 4) * kLog2e;
-    if (hf == 0 && !(split && w >= 2)) buf_store4(make_rsrc(p.delta + rbase, N * 4), q * 4, dlt);
+    if (hf == 0 && stream == 0) buf_store4(make_rsrc(p.delta + rbase, N * 4), q * 4, dlt);
   }
 
   int n_kv = (Lb + BC - 1) / BC;
-  if (CAUSAL) n_kv = min(n_kv, (min(Lb, split ? row0 + 64 : (qt + 1) * BR) - 1) / BC + 1);
+  if (CAUSAL) n_kv = min(n_kv, (min(Lb, row0 + RW) - 1) / BC + 1);
   if (MASKED && qt * BR >= Lb) n_kv = 0;  // padding rows only: dQ = 0
   // Loop positions u = 0 .. n_t - 1 map to key tiles tile(u): u, or with a block map the tiles of
   // the enabled 128-key blocks.
@@ -645,6 +652,7 @@ __global__ __launch_bounds__(NW * 64, D > 128 ? 1 : 2) void bwd_dq_kernel(BwdPar
     n_t = TPB * cnt;
   }
   auto tile = [&](int u) __attribute__((always_inline)) -> int {
+    if (QSPLIT) return 2 * u + stream;
     if (!sparse) return u;
     return TPB * __builtin_amdgcn_readfirstlane(blist[u / TPB]) + u % TPB;
   };
@@ -653,10 +661,10 @@ __global__ __launch_bounds__(NW * 64, D > 128 ? 1 : 2) void bwd_dq_kernel(BwdPar
 #pragma unroll
   for (int db = 0; db < NDB; ++db) dq[db] = f32x16{};
 
-  int goff[NLD];
+  int goff[NLDW];
 #pragma unroll
-  for (int i = 0; i < NLD; ++i) {
-    const int pos = (w + NW * i) * 64 + l;
+  for (int i = 0; i < NLDW; ++i) {
+    const int pos = (wl + DW * i) * 64 + l;
     const int row = pos / NCH, pc = pos % NCH;
     goff[i] = row * (D * 2) + ((pc ^ T::swz(row)) * 16);
   }
@@ -668,9 +676,9 @@ __global__ __launch_bounds__(NW * 64, D > 128 ? 1 : 2) void bwd_dq_kernel(BwdPar
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(p.k + base + (size_t)first * D, bytes);
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(p.v + base + (size_t)first * D, bytes);
 #pragma unroll
-    for (int i = 0; i < NLD; ++i) {
-      buf_load16_to_lds(rk, kb + (w + NW * i) * 1024, goff[i]);
-      buf_load16_to_lds(rv, vb + (w + NW * i) * 1024, goff[i]);
+    for (int i = 0; i < NLDW; ++i) {
+      buf_load16_to_lds(rk, kb + (wl + DW * i) * 1024, goff[i]);
+      buf_load16_to_lds(rv, vb + (wl + DW * i) * 1024, goff[i]);
     }
   };
 
@@ -705,52 +713,6 @@ __global__ __launch_bounds__(NW * 64, D > 128 ? 1 : 2) void bwd_dq_kernel(BwdPar
       const e16x4 a1 = lds_read_tr16<E>(kbuf, T::elem_off(16 * ks + 8 + tr_row_lane, col));
       return cat4<E>(a0, a1);
     };
-    if constexpr (QSPLIT) {
-      if (split) {
-        // one 32-key block of the tile: S and dP with the next k-step's fragments read one step
-        // ahead, then per k-step the elementwise work and the dQ products
-        const int kb = w >> 1;
-        f32x16 s = f32x16{}, dp = FOLD_DELTA ? ndlt : f32x16{};
-        e16x8 kn = lds_read16<E>(kbuf, T::chunk_off(32 * kb + lq, hf));
-        e16x8 vn = lds_read16<E>(vbuf, T::chunk_off(32 * kb + lq, hf));
-#pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) {
-          const e16x8 kc = kn, vc = vn;
-          if (kk + 1 < NKK) {
-            const int off = T::chunk_off(32 * kb + lq, 2 * (kk + 1) + hf);
-            kn = lds_read16<E>(kbuf, off);
-            vn = lds_read16<E>(vbuf, off);
-          }
-          __builtin_amdgcn_sched_barrier(0);
-          s = H::mfma(kc, qreg[kk], s);
-          dp = H::mfma(vc, oreg[kk], dp);
-        }
-#pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {
-          const int ks = 2 * kb + k2;
-          e16x8 dsb;
-          e16x8 fn = frag_dq(ks, 0);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int r = k2 * 8 + e;
-            float pr = fast_exp2(fmaf(s[r], c, -lse2));
-            if constexpr (MASK) {
-              const int krel = 32 * kb + (r >> 2) * 8 + (r & 3);
-              pr = krel <= lim ? pr : 0.f;
-            }
-            dsb[e] = (E)(FOLD_DELTA ? pr * dp[r] : pr * (dp[r] - dlt));
-          }
-#pragma unroll
-          for (int db = 0; db < NDB; ++db) {
-            const e16x8 fc = fn;
-            if (db + 1 < NDB) fn = frag_dq(ks, db + 1);
-            __builtin_amdgcn_sched_barrier(0);
-            dq[db] = H::mfma(fc, dsb, dq[db]);
-          }
-        }
-        return;
-      }
-    }
     if constexpr (NKB == 2) {
       // fragment i of block kb's S / dP products: even i = K (S), odd i = V (dP), k-step i / 2
       auto frag_sdp = [&](int kb, int i) __attribute__((always_inline)) -> e16x8 {
@@ -895,6 +857,12 @@ __global__ __launch_bounds__(NW * 64, D > 128 ? 1 : 2) void bwd_dq_kernel(BwdPar
   if (N % BC != 0) j_mask = min(j_mask, n_kv - 1);
   j_mask = min(j_mask, n_kv);
   if (MASKED) j_mask = 0;
+  if (QSPLIT) {
+    // loop positions of this wave pair: its clean tiles, then as many positions as the even
+    // tiles need for both pairs (the odd pair's last one may lie past its rows: masked, skipped)
+    j_mask = max(0, (j_mask - stream + 1) / 2);
+    n_t = (n_kv + 1) / 2;
+  }
   // Causal: a masked-path tile whose first key follows every row of this wave contributes nothing
   // to the wave's rows (all its scores are masked); the wave skips it but still issues its share of
   // the tile loads and meets the barriers.
@@ -917,7 +885,39 @@ __global__ __launch_bounds__(NW * 64, D > 128 ? 1 : 2) void bwd_dq_kernel(BwdPar
       __syncthreads();
     }
   };
-  if (!MASKED || n_t > 0) {
+  if constexpr (QSPLIT) {
+    // Each wave pair runs the tile loop on its own buffers; every loop position ends with one
+    // workgroup barrier in either loop, and both pairs run n_t positions, so the barriers match.
+    // (The plain launches keep the loop below written out on their four buffers.)
+    auto tiles = [&](char* K0, char* V0, char* K1, char* V1) __attribute__((always_inline)) {
+      auto pair_b = [&](auto mask_tag, int u, int u_end) __attribute__((always_inline)) {
+        if (u + 1 < n_t) dma(tile(u + 1), K1, V1);
+        debug_stage_sync();
+        run(mask_tag, tile(u), K0, V0);
+        debug_stage_sync();
+        wait_vmem();
+        __syncthreads();
+        if (u + 1 < u_end) {
+          if (u + 2 < n_t) dma(tile(u + 2), K0, V0);
+          debug_stage_sync();
+          run(mask_tag, tile(u + 1), K1, V1);
+          debug_stage_sync();
+          wait_vmem();
+          __syncthreads();
+        }
+      };
+      dma(tile(0), K0, V0);
+      wait_vmem();
+      __syncthreads();
+      int u = 0;
+#pragma unroll 1
+      for (; u + 1 < j_mask; u += 2) pair_b(std::false_type{}, u, j_mask);
+#pragma unroll 1
+      for (; u < n_t; u += 2) pair_b(std::true_type{}, u, n_t);
+    };
+    if (stream == 1) tiles(skb0, svb0, skb1, svb1);
+    else tiles(sk0, sv0, sk1, sv1);
+  } else if (!MASKED || n_t > 0) {
     dma(tile(0), sk0, sv0);
     wait_vmem();
     __syncthreads();
@@ -934,32 +934,29 @@ __global__ __launch_bounds__(NW * 64, D > 128 ? 1 : 2) void bwd_dq_kernel(BwdPar
   char* stage = w == 0 ? sk0 : (w == 1 ? sv0 : (w == 2 ? sk1 : sv1));
   bool stored = false;
   if constexpr (QSPLIT) {
-    if (split) {
-      // wave g + 2 hands its partial sum (fp32, 128 * D bytes: one tile buffer) to wave g, which
-      // adds it and writes the rows; the exchange buffers are not waves 0 and 1's staging areas
-      static_assert(NDB * 4 * 64 * 16 == TILE_BYTES, "a partial fills one tile buffer");
-      f32x4* xbuf = reinterpret_cast<f32x4*>((w & 1) ? sv1 : sk1);
-      if (w >= 2) {
+    // the odd-tile pair hands its dQ partial sums (fp32, 128 * D bytes per wave: one or two of its
+    // idle tile buffers) to the even-tile wave of the same rows, which adds them and writes the rows
+    constexpr int XCH = TILE_BYTES / 1024;  // 1 KB chunks (64 lanes x 16 bytes) per tile buffer
+    static_assert(NDB * 4 <= 2 * XCH, "a partial fits two tile buffers");
+    f32x4* xa = reinterpret_cast<f32x4*>(wl ? skb1 : skb0);
+    f32x4* xb = reinterpret_cast<f32x4*>(wl ? svb1 : svb0);
+    if (stream == 1) {
 #pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4)
-            xbuf[(4 * db + q4) * 64 + l] = f32x4{dq[db][4 * q4], dq[db][4 * q4 + 1], dq[db][4 * q4 + 2], dq[db][4 * q4 + 3]};
-      }
-      __syncthreads();
-      if (w < 2) {
-#pragma unroll
-        for (int db = 0; db < NDB; ++db)
-#pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4) {
-            const f32x4 t = xbuf[(4 * db + q4) * 64 + l];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) dq[db][4 * q4 + e] += t[e];
-          }
-        store_rows_via_lds<E, D, TILE_BYTES>(stage, dq, p.scale, make_rsrc(p.dq + base, head_bytes), q_w0, l);
-      }
-      stored = true;
+      for (int c = 0; c < 4 * NDB; ++c)
+        (c < XCH ? xa + c * 64 : xb + (c - XCH) * 64)[l] =
+            f32x4{dq[c >> 2][4 * (c & 3)], dq[c >> 2][4 * (c & 3) + 1], dq[c >> 2][4 * (c & 3) + 2], dq[c >> 2][4 * (c & 3) + 3]};
     }
+    __syncthreads();
+    if (stream == 0) {
+#pragma unroll
+      for (int c = 0; c < 4 * NDB; ++c) {
+        const f32x4 t = (c < XCH ? xa + c * 64 : xb + (c - XCH) * 64)[l];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dq[c >> 2][4 * (c & 3) + e] += t[e];
+      }
+      store_rows_via_lds<E, D, TILE_BYTES>(stage, dq, p.scale, make_rsrc(p.dq + base, head_bytes), q_w0, l);
+    }
+    stored = true;
   }
   if (!stored) store_rows_via_lds<E, D, TILE_BYTES>(stage, dq, p.scale, make_rsrc(p.dq + base, head_bytes), q_w0, l);
   }  // item
@@ -1060,20 +1057,14 @@ hipError_t dq_d(BwdParams<E> prm, hipStream_t stream) {
   const bool by_length = MASKED && prm.seqlens && prm.heads % 8 == 0 && prm.nh / prm.heads <= 64;
   prm.n_units = (CAUSAL && !by_length && (long)prm.n_tiles * prm.nh >= 4L * device_cu_count()) ? (prm.n_tiles + 1) / 2
                                                                                               : prm.n_tiles;
-  if constexpr (CAUSAL && !MASKED && D <= 64) {
-    // Small launch (its workgroups fill at most half of the chip's slots, two per CU): split the
-    // longest ~3/8 of the query tiles (the same balance as the dK/dV split: each half takes half a
-    // tile's work per key tile, at ~25% more time per unit of work); the extra workgroups always
-    // fit. Not at d = 96, whose split kernel spills (measured 26% slower), nor on fuller chips
-    // (B1 H24 N2048 d64, 384 workgroups: 2% slower).
-    const long slots = 2L * device_cu_count();
-    const long wgs = (long)prm.n_tiles * prm.nh;
-    if (prm.n_tiles >= 8 && 2 * wgs <= slots) {
-      prm.n_units = prm.n_tiles;
-      prm.n_split = (3 * prm.n_tiles + 4) / 8;
-      prm.n_long = prm.n_split;  // no unsplit tile is longer than the longest half
+  if constexpr (CAUSAL && !MASKED && D <= 128) {
+    // Small launch: when its 64-row workgroups all fit on the chip at once (two per CU; one at
+    // d = 96, whose doubled tile buffers take 96 KB), the split kernel halves each row's key loop.
+    const long slots = (D == 96 ? 1L : 2L) * device_cu_count();
+    if (prm.N >= 512 && 2L * prm.n_tiles * prm.nh <= slots) {
+      prm.n_units = (prm.N + 63) / 64;
       hipLaunchKernelGGL((bwd_dq_kernel<E, D, dq_bc<D>(), kDqNW, CAUSAL, MASKED, DROPOUT, true>),
-                         dim3((prm.n_tiles + prm.n_split) * prm.nh), dim3(kDqNW * 64), 0, stream, prm);
+                         dim3(prm.n_units * prm.nh), dim3(kDqNW * 64), 0, stream, prm);
       return hipGetLastError();
     }
   }

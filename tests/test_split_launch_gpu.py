@@ -5,9 +5,9 @@ their longest work in two:
     partial sums at the end. The host splits about 3/8 of a head's key tiles when the launch has
     at least 8 key tiles per head and its workgroups all fit on the chip at once (so the launch
     would otherwise last as long as key tile 0), and only as many as still fit.
-  * dQ (d <= 64, launches that fill at most half of the chip's slots): the longest query tiles
-    (rows 0-63 and 64-127 of the tile); each wave takes one of the two 32-key blocks of every key
-    tile, and the two waves that share rows add their partial sums at the end.
+  * dQ (causal, d <= 128, when the 64-row workgroups all fit at once; N >= 512): 64-row
+    workgroups whose wave pairs take the even and the odd key tiles of the rows; the odd pair hands
+    its dQ partial sums to the even pair, which adds them.
   * forward (dense, d <= 128, no more 128-row tiles than CUs (half as many at d > 64), N >= 256):
     64-row workgroups whose wave pairs take the even and the odd 64-key tiles of the rows; the
     odd pair hands its running max, row sums and O accumulator to the even pair, which merges

@@ -174,8 +174,15 @@ constexpr int dkdv_waves_per_simd() {
   return (D > 128 || (D == 128 && PART == 0)) ? 1 : ((D == 64 && CAUSAL && !MASKED) ? 3 : 2);
 }
 
-template <typename E, int D, int NW, int BQ, bool CAUSAL, bool MASKED, bool DROPOUT, int PART, bool QSPLIT = false>
-__global__ __launch_bounds__(NW * 64, (dkdv_waves_per_simd<D, PART, CAUSAL, MASKED>())) void bwd_dkdv_kernel(BwdParams<E> p) {
+//
+// QSTREAM (small causal launches whose 64-key workgroups all fit at once): a workgroup takes 64
+// keys, and its two wave pairs take the even and the odd query tiles: wave w runs the 32 keys of
+// group w & 1 over query tiles w >> 1, (w >> 1) + 2, ..., each pair with its own double buffer,
+// and the two waves of a key group exchange their dK and dV partial sums at the end. (Its tile
+// buffers take 64 KB at d = 64, 96-128 KB at d = 96, 128: two or one workgroups per CU.)
+template <typename E, int D, int NW, int BQ, bool CAUSAL, bool MASKED, bool DROPOUT, int PART, bool QSPLIT = false,
+          bool QSTREAM = false>
+__global__ __launch_bounds__(NW * 64, (QSTREAM ? (D <= 64 ? 2 : 1) : dkdv_waves_per_simd<D, PART, CAUSAL, MASKED>())) void bwd_dkdv_kernel(BwdParams<E> p) {
   constexpr bool WANT_DV = PART != 2, WANT_DK = PART != 1;
   using H = Half16<E>;
   using e16x8 = typename H::x8;
@@ -195,6 +202,12 @@ __global__ __launch_bounds__(NW * 64, (dkdv_waves_per_simd<D, PART, CAUSAL, MASK
   constexpr bool FOLD_DELTA = !DROPOUT && !(D == 128 && PART == 0);
   static_assert(!QSPLIT || (CAUSAL && !MASKED && PART == 0 && NW == 4 && BQ == 64),
                 "split launches: dense causal dK and dV, 2 key groups x 2 query blocks of 32");
+  static_assert(!QSTREAM || (!QSPLIT && CAUSAL && !MASKED && PART == 0 && NW == 4 && BQ == 64),
+                "stream launches: dense causal dK and dV");
+  constexpr int KW = QSTREAM ? 64 : BKV;      // keys per workgroup
+  constexpr int DW = QSTREAM ? 2 : NW;        // waves that load one tile
+  constexpr int NLDW = BQ * NCH / (64 * DW);  // their DMA instructions per tensor and tile
+  static_assert(NLDW * 64 * DW == BQ * NCH, "a tile splits evenly over its loading waves");
 
   __shared__ __attribute__((aligned(16))) char sq0[TILE_BYTES];
   __shared__ __attribute__((aligned(16))) char so0[TILE_BYTES];
@@ -202,6 +215,13 @@ __global__ __launch_bounds__(NW * 64, (dkdv_waves_per_simd<D, PART, CAUSAL, MASK
   __shared__ __attribute__((aligned(16))) char so1[TILE_BYTES];
   __shared__ __attribute__((aligned(16))) float sr0[2 * BQ];  // [lse * log2(e) | delta] of the tile's rows
   __shared__ __attribute__((aligned(16))) float sr1[2 * BQ];
+  // the odd-tile pair's buffers (stream launches)
+  __shared__ __attribute__((aligned(16))) char sqb0[QSTREAM ? TILE_BYTES : 16];
+  __shared__ __attribute__((aligned(16))) char sob0[QSTREAM ? TILE_BYTES : 16];
+  __shared__ __attribute__((aligned(16))) char sqb1[QSTREAM ? TILE_BYTES : 16];
+  __shared__ __attribute__((aligned(16))) char sob1[QSTREAM ? TILE_BYTES : 16];
+  __shared__ __attribute__((aligned(16))) float srb0[QSTREAM ? 2 * BQ : 4];
+  __shared__ __attribute__((aligned(16))) float srb1[QSTREAM ? 2 * BQ : 4];
   __shared__ short blist[MASKED ? kMaxMaskBlocks : 1];  // enabled query blocks of this key tile
   __shared__ __attribute__((aligned(16))) uint8_t sdrop[DROPOUT ? NW * 1024 : 4];  // per wave: bytes [key][query]
 
@@ -211,7 +231,9 @@ __global__ __launch_bounds__(NW * 64, (dkdv_waves_per_simd<D, PART, CAUSAL, MASK
   const int N = p.N;
   int head, kt, hs = -1;
   // causal: key tile 0 has the most work; with sequence lengths, padding key tiles run last
-  if constexpr (QSPLIT) {
+  if constexpr (QSTREAM) {
+    map_workgroup(blockIdx.x, p.n_units, p.nh, Order::kLongestFirst, false, head, kt);  // 64-key tiles
+  } else if constexpr (QSPLIT) {
     int r;
     map_workgroup(blockIdx.x, p.n_tiles + p.n_split, p.nh, Order::kLongestFirst, false, head, r);
     split_rank(r, p.n_split, p.n_long, kt, hs);
@@ -220,11 +242,13 @@ __global__ __launch_bounds__(NW * 64, (dkdv_waves_per_simd<D, PART, CAUSAL, MASK
     map_workgroup(blockIdx.x, p.n_tiles, p.nh, CAUSAL ? Order::kLongestFirst : Order::kHeadMajor, false, head, kt);
   }
   const bool split = QSPLIT && hs >= 0;                  // a 64-key half (wave-uniform)
-  const int kspan0 = kt * BKV + (split ? 64 * hs : 0);  // the workgroup's first key
+  const int kspan0 = kt * KW + (split ? 64 * hs : 0);   // the workgroup's first key
+  const int stream = QSTREAM ? (w >> 1) : 0;  // stream launches: even (0) or odd (1) query tiles
+  const int wl = QSTREAM ? (w & 1) : w;       // the wave's index among the waves loading its tiles
   const size_t base = (size_t)head * N * D;
   const size_t rbase = (size_t)head * N;
   const int head_bytes = N * D * 2;
-  const int key_w0 = kspan0 + 32 * (split ? (w & 1) : w);
+  const int key_w0 = kspan0 + 32 * (split ? (w & 1) : wl);
   const int key = key_w0 + lq;
   const int Lb = valid_rows<MASKED>(p, head);  // rows >= Lb of every input read as zero
 
@@ -265,15 +289,23 @@ __global__ __launch_bounds__(NW * 64, (dkdv_waves_per_simd<D, PART, CAUSAL, MASK
     // list entries are relative to the first block scanned (the diagonal one when causal)
     if (CAUSAL && (cnt == 0 || __builtin_amdgcn_readfirstlane(blist[0]) != 0)) n_diag = 0;
   }
+  if (QSTREAM) {
+    // this wave pair's query tiles qt0 + stream, qt0 + stream + 2, ...; both pairs run as many
+    // positions as the even tiles need (the odd pair's last may be past the head: zero rows).
+    // Only the first query tile meets the 64-key diagonal, the even pair's first position.
+    n_t = (n_t + 1) / 2;
+    n_diag = stream == 0 ? 2 : 0;
+  }
   auto tile = [&](int u) __attribute__((always_inline)) -> int {
+    if (QSTREAM) return qt0 + 2 * u + stream;
     if (!sparse) return qt0 + u;
     return qt0 + TPB * __builtin_amdgcn_readfirstlane(blist[u / TPB]) + u % TPB;
   };
 
-  int goff[NLD];
+  int goff[NLDW];
 #pragma unroll
-  for (int i = 0; i < NLD; ++i) {
-    const int pos = (w + NW * i) * 64 + l;
+  for (int i = 0; i < NLDW; ++i) {
+    const int pos = (wl + DW * i) * 64 + l;
     const int row = pos / NCH, pc = pos % NCH;
     goff[i] = row * (D * 2) + ((pc ^ T::swz(row)) * 16);
   }
@@ -288,17 +320,17 @@ __global__ __launch_bounds__(NW * 64, (dkdv_waves_per_simd<D, PART, CAUSAL, MASK
     const __amdgpu_buffer_rsrc_t rq = make_rsrc(p.q + base + (size_t)first * D, bytes);
     const __amdgpu_buffer_rsrc_t ro = make_rsrc(p.dout + base + (size_t)first * D, bytes);
 #pragma unroll
-    for (int t = 0; t < NLD; ++t) {
-      buf_load16_to_lds(rq, qb + (w + NW * t) * 1024, goff[t]);
-      buf_load16_to_lds(ro, ob + (w + NW * t) * 1024, goff[t]);
+    for (int t = 0; t < NLDW; ++t) {
+      buf_load16_to_lds(rq, qb + (wl + DW * t) * 1024, goff[t]);
+      buf_load16_to_lds(ro, ob + (wl + DW * t) * 1024, goff[t]);
     }
-    if (w == 0) {
+    if (wl == 0) {
       st_l = buf_load4f(rlse, (row0 + l) * 4) * kLog2e;
       st_d = buf_load4f(rdel, (row0 + l) * 4);
     }
   };
   auto stage_rows = [&](float* sr) __attribute__((always_inline)) {
-    if (w == 0) {
+    if (wl == 0) {
       sr[l] = st_l;
       sr[BQ + l] = FOLD_DELTA ? -st_d : st_d;
     }
@@ -466,7 +498,42 @@ __global__ __launch_bounds__(NW * 64, (dkdv_waves_per_simd<D, PART, CAUSAL, MASK
       __syncthreads();
     }
   };
-  if (n_t > 0) {
+  if constexpr (QSTREAM) {
+    // Each wave pair runs the tile loop on its own buffers; every loop position ends with one
+    // workgroup barrier and both pairs run n_t positions, so the barriers match. (The plain
+    // launches keep the loop below written out on their buffers.)
+    auto tiles = [&](char* Q0, char* O0, char* Q1, char* O1, float* R0, float* R1) __attribute__((always_inline)) {
+      auto pair_b = [&](auto diag_tag, int u) __attribute__((always_inline)) {
+        if (u + 1 < n_t) dma(tile(u + 1), Q1, O1);
+        debug_stage_sync();
+        compute(diag_tag, tile(u), Q0, O0, R0);
+        debug_stage_sync();
+        wait_vmem();
+        stage_rows(R1);
+        __syncthreads();
+        if (u + 1 < n_t) {
+          if (u + 2 < n_t) dma(tile(u + 2), Q0, O0);
+          debug_stage_sync();
+          compute(diag_tag, tile(u + 1), Q1, O1, R1);
+          debug_stage_sync();
+          wait_vmem();
+          stage_rows(R0);
+          __syncthreads();
+        }
+      };
+      dma(tile(0), Q0, O0);
+      stage_rows(R0);
+      wait_vmem();
+      __syncthreads();
+      int u = 0;
+#pragma unroll 1
+      for (; u < n_diag && u < n_t; u += 2) pair_b(std::true_type{}, u);
+#pragma unroll 1
+      for (; u < n_t; u += 2) pair_b(std::false_type{}, u);
+    };
+    if (stream == 1) tiles(sqb0, sob0, sqb1, sob1, srb0, srb1);
+    else tiles(sq0, so0, sq1, so1, sr0, sr1);
+  } else if (n_t > 0) {
     dma(tile(0), sq0, so0);
     stage_rows(sr0);
     wait_vmem();
@@ -488,6 +555,43 @@ __global__ __launch_bounds__(NW * 64, (dkdv_waves_per_simd<D, PART, CAUSAL, MASK
   // dK = scale * dK^T^T and dV, written as whole rows through this wave's idle tile buffer.
   __syncthreads();  // every wave is done reading the last Q / dO tile
   char* stage = w == 0 ? sq0 : (w == 1 ? so0 : (w == 2 ? sq1 : so1));
+  if constexpr (QSTREAM) {
+    // Waves g and g + 2 hold key group g's partial sums over the even and the odd query tiles.
+    // Wave g + 2 hands its dK partial to wave g, wave g hands its dV partial to wave g + 2 (fp32,
+    // one of the odd pair's idle tile buffers each: 128 * D bytes); then wave g writes dK and wave
+    // g + 2 writes dV, staging in buffers the exchange does not use.
+    static_assert(NDB * 4 * 64 * 16 == TILE_BYTES, "a partial fills one tile buffer");
+    f32x4* xk = reinterpret_cast<f32x4*>(wl ? sqb1 : sqb0);
+    f32x4* xv = reinterpret_cast<f32x4*>(wl ? sob1 : sob0);
+    auto give = [&](const f32x16(&acc)[NDB], f32x4* out4) __attribute__((always_inline)) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          out4[(4 * db + q4) * 64 + l] = f32x4{acc[db][4 * q4], acc[db][4 * q4 + 1], acc[db][4 * q4 + 2], acc[db][4 * q4 + 3]};
+    };
+    auto take = [&](f32x16(&acc)[NDB], const f32x4* in4) __attribute__((always_inline)) {
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const f32x4 t = in4[(4 * db + q4) * 64 + l];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[db][4 * q4 + e] += t[e];
+        }
+    };
+    if (stream == 1) give(dk, xk);
+    else give(dv, xv);
+    __syncthreads();
+    if (stream == 0) {
+      take(dk, xk);
+      store_rows_via_lds<E, D, TILE_BYTES>(stage, dk, p.scale, make_rsrc(p.dk + base, head_bytes), key_w0, l);
+    } else {
+      take(dv, xv);
+      store_rows_via_lds<E, D, TILE_BYTES>(stage, dv, 1.0f, make_rsrc(p.dv + base, head_bytes), key_w0, l);
+    }
+    return;
+  }
   if (split) {
     // Waves g and g + 2 hold key group g's partial sums over query blocks 0 and 1. Wave g + 2 hands
     // its dK partial to wave g, wave g hands its dV partial to wave g + 2 (fp32, through the tile
@@ -1025,7 +1129,17 @@ hipError_t dkdv_d(BwdParams<E> prm, hipStream_t stream) {
     hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, kKvNW, kKvBQ, CAUSAL, MASKED, DROPOUT, 2>), grid, block, 0, stream, prm);
   } else {
     if constexpr (CAUSAL && !MASKED) {
-      // Small launch (its workgroups fit on the chip at once): split about 3/8 of the key tiles, as
+      // Small launch whose 64-key workgroups all fit on the chip at once (two per CU at d <= 64;
+      // one at d = 96, 128, whose doubled tile buffers take 96-128 KB): the stream kernel halves
+      // each key's query loop.
+      const long per_cu = D <= 64 ? 2 : 1;
+      if (prm.N >= 512 && 2L * prm.n_tiles * prm.nh <= per_cu * device_cu_count()) {
+        prm.n_units = (prm.N + 63) / 64;
+        hipLaunchKernelGGL((bwd_dkdv_kernel<E, D, kKvNW, kKvBQ, CAUSAL, MASKED, DROPOUT, 0, false, true>),
+                           dim3(prm.n_units * prm.nh), block, 0, stream, prm);
+        return hipGetLastError();
+      }
+      // Otherwise, when its 128-key workgroups fit at once: split about 3/8 of the key tiles, as
       // long as the extra workgroups still fit. Halving a tile costs ~25% more time per query tile
       // (half the work per barrier and tile load), so key tile 0's halves then last about as long
       // as the first unsplit tile.

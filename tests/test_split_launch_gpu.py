@@ -4,7 +4,9 @@ their longest work in two:
     one of the two 32-row blocks of every query tile, and the two waves that share keys add their
     partial sums at the end. The host splits about 3/8 of a head's key tiles when the launch has
     at least 8 key tiles per head and its workgroups all fit on the chip at once (so the launch
-    would otherwise last as long as key tile 0), and only as many as still fit.
+    would otherwise last as long as key tile 0), and only as many as still fit. Smaller launches,
+    whose 64-key workgroups all fit at once (N >= 512), instead give every workgroup 64 keys and
+    its wave pairs the even and the odd query tiles, exchanging dK and dV partials at the end.
   * dQ (causal, d <= 128, when the 64-row workgroups all fit at once; N >= 512): 64-row
     workgroups whose wave pairs take the even and the odd key tiles of the rows; the odd pair hands
     its dQ partial sums to the even pair, which adds them.

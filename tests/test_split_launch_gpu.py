@@ -41,6 +41,7 @@ DT = {"bf16": torch.bfloat16, "fp16": torch.float16}
     ("bf16", 128, 1, 2, 1024),
     ("bf16", 128, 1, 12, 2048),
     ("fp16", 64, 2, 2, 1100),
+    ("bf16", 64, 1, 24, 1500),  # too many 64-key workgroups for the stream split: the key-tile split
 ])
 def test_bwd_small_causal_launch(dtype, d, B, H, N):
     print(f"split dK/dV launch {dtype} B{B} H{H} N{N} d{d} causal", flush=True)

@@ -19,8 +19,10 @@ Prints ONE JSON line. Besides the headline it carries:
                 headline's shape, so the headline's warm-up and timed steps run on a GPU whose clock
                 has settled for this kind of load; it takes ~100 steps from a change of load)
   shader clock  the gfx clock sampled from the host (amdsmi) during each timed region, or null
-  extras        the same kernels on fp16 storage (the long causal forward and the fwd+bwd step) and
-                the key-split decoding step (one query against 8192 keys, HBM-bound: GB/s)
+  extras        the same kernels on fp16 storage (the long causal forward and the fwd+bwd step), the
+                key-split decoding step (one query against 8192 keys, HBM-bound: GB/s), block-sparse
+                and variable-length forwards, the step with dropout, head dims 32 / 96 / 256, and two
+                small launches (B1 H16 d64, B1 H8 d128, N 2048 causal: the split kernels)
 """
 from __future__ import annotations
 
@@ -642,6 +644,13 @@ def main():
                                "tflops": round((bw.fwd_flops() + bw.bwd_flops()) / (ms * 1e-3) / 1e12, 1),
                                "kernels_us": {n: round(t * 1e3, 2) for n, t in km.items()}}
             torch.cuda.empty_cache()
+        # small launches (their workgroups fit on the chip at once: the split kernels)
+        for B, H, d in ((1, 16, 64), (1, 8, 128)):
+            bw = inputs.Workload(f"fwdbwd_bf16_b{B}h{H}n2048d{d}_causal", "bf16", B, H, 2048, d, True, True)
+            ms, km = time_fwdbwd(bw, inputs.make_inputs(bw), 30, 5, dev, to_dev)
+            extras[bw.name] = {"workload": bw.name, "pass": "fwd+bwd", "us": round(ms * 1e3, 2),
+                               "tflops": round((bw.fwd_flops() + bw.bwd_flops()) / (ms * 1e-3) / 1e12, 1),
+                               "kernels_us": {n: round(t * 1e3, 2) for n, t in km.items()}}
         torch.cuda.empty_cache()
 
     # ------------------------------------------------------------------ CPU oracle baseline

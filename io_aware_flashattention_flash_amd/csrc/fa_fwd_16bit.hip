@@ -146,7 +146,8 @@ enum FwdMode : int { kDense = 0, kSplit = 1, kMasked = 2, kMaskedDropout = 3 };
 // workgroup per CU, one wave per SIMD. Smaller head dims run two workgroups per CU.
 //
 // QSPLIT (dense launches at d <= 128 whose 128-row tiles are no more than the CUs, or half of
-// them at d > 64, where the doubled tile buffers leave room for one workgroup per CU): a workgroup
+// them at d > 64, where the doubled tile buffers leave room for one workgroup per CU; causal ones
+// with long rows up to twice that): a workgroup
 // takes 64 query rows, and its two wave pairs take the even and the odd K/V tiles: wave w runs the
 // 32 rows of group w & 1 over tiles w >> 1, (w >> 1) + 2, ..., each pair with its own double
 // buffer, and the pair of odd tiles hands its (m, l, l~, O) to the other at the end, which merges
@@ -800,8 +801,12 @@ static hipError_t launch_typed(const void* q, const void* k, const void* v, void
       // Small launch (no more 128-row tiles than CUs, half as many at d > 64, whose split
       // workgroups need 96-128 KB of LDS: one per CU; N >= 256): 64-row workgroups whose wave pairs
       // take the even and the odd K/V tiles (fwd16_kernel, QSPLIT), twice the workgroups, each
-      // with half the key loop.
-      if (N >= 256 && (long)prm.n_qt * BH * (D > 64 ? 2 : 1) <= device_cu_count()) {
+      // with half the key loop. Causal launches with up to twice as many tiles also take it when
+      // their rows are long (N >= 4096 at d <= 64, N >= 2048 above): their longest rows then set
+      // the launch's length (measured +7 to +26%; shorter rows lose up to 8%).
+      const long tiles = (long)prm.n_qt * BH * (D > 64 ? 2 : 1), cus = device_cu_count();
+      const bool long_causal = causal && tiles <= 2 * cus && N >= (D > 64 ? 2048 : 4096);
+      if (N >= 256 && (tiles <= cus || long_causal)) {
         Fwd16Params<E> sp = prm;
         sp.n_qt = (N + 63) / 64;
         return causal ? launch_cfg<E, D, 64, NW, true, MODE, true>(sp, 1, stream)

@@ -10,7 +10,8 @@ their longest work in two:
   * dQ (causal, d <= 128, when the 64-row workgroups all fit at once; N >= 512): 64-row
     workgroups whose wave pairs take the even and the odd key tiles of the rows; the odd pair hands
     its dQ partial sums to the even pair, which adds them.
-  * forward (dense, d <= 128, no more 128-row tiles than CUs (half as many at d > 64), N >= 256):
+  * forward (dense, d <= 128, no more 128-row tiles than CUs (half as many at d > 64; causal
+    launches with long rows up to twice that), N >= 256):
     64-row workgroups whose wave pairs take the even and the odd 64-key tiles of the rows; the
     odd pair hands its running max, row sums and O accumulator to the even pair, which merges
     them by the online-softmax rule.
@@ -93,6 +94,8 @@ def test_bwd_small_causal_launch_deterministic_and_staged():
     ("bf16", 128, 1, 3, 700, False),
     ("bf16", 96, 1, 2, 1000, True),
     ("fp16", 128, 1, 2, 600, True),
+    ("bf16", 128, 1, 12, 2048, True),  # causal with long rows: up to twice the tiles
+    ("bf16", 64, 1, 16, 4096, True),
 ])
 def test_fwd_small_launch(dtype, d, B, H, N, causal):
     print(f"split forward launch {dtype} B{B} H{H} N{N} d{d} causal {causal}", flush=True)

@@ -48,8 +48,10 @@ def _replay_and_compare(graph, static_in, static_out, eager, seed):
         _other_work()
 
 
-def test_graph_dense_forward_backward():
-    B, H, N, d, causal = 2, 4, 333, 64, True
+@pytest.mark.parametrize("N", [333, 1100])
+def test_graph_dense_forward_backward(N):
+    """N = 1100 (small launch) runs the split forward, dQ and dK/dV kernels."""
+    B, H, d, causal = 2, 4, 64, True
     scale = d ** -0.5
     q, k, v, do = (torch.empty(B, H, N, d, dtype=torch.bfloat16, device=DEV) for _ in range(4))
     o = torch.empty_like(q)
